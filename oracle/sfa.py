@@ -1,0 +1,205 @@
+"""Stream-factorized attention, written as its plain definition (float64).
+
+TEST INFRASTRUCTURE ONLY: see the package docstring for who may import this.
+
+Notation (0-indexed): n streams, L tokens, S = n*L expanded positions.
+Token i, stream k sits at expanded position p = i*n + k. The page writes the
+same map 1-indexed as (i-1)n + k ([HD-tahou] 隐式序列缩放的技术细节, step 1);
+subtracting 1 from a 1-indexed position gives this 0-indexed form. Hence
+stream(p) = p mod n and token(p) = p div n.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MODES = ("intra", "cross_full", "cross_window")
+
+
+# ---------------------------------------------------------------------------
+# Stream expansion
+# ---------------------------------------------------------------------------
+
+def interleave(src: np.ndarray) -> np.ndarray:
+    """Place stream k of token i at expanded position i*n + k.
+
+    [HD-tahou] 隐式序列缩放的技术细节, step 1: given the n per-stream embeddings,
+    the k-th stream representation of the i-th token goes to position
+    (i-1)n+k (1-indexed), giving a sequence of length nL.
+
+    src: [n][B][L][...] (one slab per stream). Returns [B][n*L][...].
+    """
+    src = np.asarray(src)
+    n, B, L = src.shape[:3]
+    out = np.empty((B, n * L) + src.shape[3:], dtype=src.dtype)
+    for k in range(n):
+        # positions k, n+k, 2n+k, ... are token 0, 1, 2, ... of stream k
+        out[:, k::n] = src[k]
+    return out
+
+
+def deinterleave(x: np.ndarray, n: int) -> np.ndarray:
+    """Inverse of :func:`interleave`: [B][n*L][...] -> [n][B][L][...].
+
+    Used to split an expanded sequence back into per-stream slabs, e.g. to
+    fill the per-stream KV cache ([HD-aiflow] "Latent computation scaling and
+    Hidden Decoding": the KV cache of the internal streams is kept as context).
+    """
+    x = np.asarray(x)
+    S = x.shape[1]
+    if S % n:
+        raise ValueError("expanded length must be a multiple of n")
+    return np.stack([x[:, k::n] for k in range(n)])
+
+
+# ---------------------------------------------------------------------------
+# Masks
+# ---------------------------------------------------------------------------
+
+def mask(mode: str, n: int, L: int, window: int | None = None, rows=None) -> np.ndarray:
+    """Which keys each query may attend to, as an explicit boolean matrix.
+
+    Returns M[len(rows)][S] with M[r, q] True iff query position p = rows[r]
+    may attend to key position q. ``rows`` defaults to all S positions.
+
+    * cross_full: standard causal attention over the expanded sequence,
+      q <= p ([HD-tahou] 隐式序列缩放的技术细节, step 2, and the cross-stream
+      layer of 规模化落地的工程优化 in its full-attention form).
+    * cross_window: the same, kept within a sliding window of ``window``
+      expanded positions counting the query itself: 0 <= p - q < window
+      (规模化落地的工程优化: cross-stream layers keep the base layer's form,
+      sliding window or full).
+    * intra: only earlier positions of the same stream, the query itself
+      included: q <= p and q mod n == p mod n (规模化落地的工程优化, the
+      intra-stream layer).
+    """
+    if mode not in MODES:
+        raise ValueError(f"unknown mode {mode!r}")
+    S = n * L
+    p = np.arange(S, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    q = np.arange(S, dtype=np.int64)
+    P = p[:, None]
+    Q = q[None, :]
+    allowed = Q <= P
+    if mode == "intra":
+        allowed &= (Q % n) == (P % n)
+    elif mode == "cross_window":
+        if window is None or window < 1:
+            raise ValueError("cross_window needs window >= 1")
+        allowed &= (P - Q) < window
+    return allowed
+
+
+def pair_count(mode: str, n: int, L: int, window: int | None = None, block: int = 2048) -> int:
+    """Number of allowed (query, key) pairs of one head: the popcount of
+    :func:`mask`, counted in row blocks. Useful attention work is proportional
+    to it ([HD-tahou] 规模化落地的工程优化: dense attention grows with the
+    square of the sequence length, 16x at n=4; the factorised form adds about
+    n times)."""
+    S = n * L
+    total = 0
+    for r0 in range(0, S, block):
+        total += int(mask(mode, n, L, window, np.arange(r0, min(S, r0 + block))).sum())
+    return total
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed: np.ndarray, scale: float):
+    """Masked softmax attention for one head, the textbook definition.
+
+    q: [R][D] queries, k and v: [S][D] keys and values, allowed: [R][S].
+    Returns (o [R][D], lse [R]) with
+        o[r]   = sum_j w[r,j] v[j] / sum_j w[r,j],   w[r,j] = exp(s[r,j] - max_j s[r,j])
+        lse[r] = ln sum_{j allowed} exp(s[r,j]),     s = scale * q k^T,
+    where disallowed scores are -inf. Every row must admit at least one key.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s = float(scale) * (q @ k.T)
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("a query row admits no key")
+    w = np.exp(s - m)
+    den = w.sum(axis=1, keepdims=True)
+    o = (w @ v) / den
+    lse = m[:, 0] + np.log(den[:, 0])
+    return o, lse
+
+
+def attn_fwd(q, k, v, mode: str, n: int, window: int | None = None, scale: float | None = None,
+             rows=None, block: int = 512, with_lse: bool = False):
+    """Stream-factorized attention over the expanded sequence.
+
+    q: [B][S][Hq][D], k and v: [B][S][Hkv][D] (any real dtype; computed in
+    float64). Grouped-query attention ([HD-aiflow] "Tencent's ecosystem first
+    scaling strategy"): query head h reads key/value head h // (Hq/Hkv).
+    ``rows`` restricts the output to those query positions (all by default).
+
+    Returns o [B][len(rows)][Hq][D] (and lse [B][Hq][len(rows)] if asked).
+    The mask rows are built explicitly, ``block`` query rows at a time, and the
+    full dense score rows are computed, masked pairs included: nothing is
+    skipped.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if S % n or Hq % Hkv:
+        raise ValueError("S must be a multiple of n and Hq of Hkv")
+    G = Hq // Hkv
+    L = S // n
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((B, len(rows), Hq, D))
+    lse = np.empty((B, Hq, len(rows)))
+    for r0 in range(0, len(rows), block):
+        rr = rows[r0:r0 + block]
+        allowed = mask(mode, n, L, window, rr)
+        for b in range(B):
+            for h in range(Hq):
+                kh = h // G
+                ob, lb = attend(q[b, rr, h], k[b, :, kh], v[b, :, kh], allowed, scale)
+                o[b, r0:r0 + len(rr), h] = ob
+                lse[b, h, r0:r0 + len(rr)] = lb
+    return (o, lse) if with_lse else o
+
+
+def decode(q_new, k_cache, v_cache, T: int, mode: str, window: int | None = None,
+           scale: float | None = None):
+    """One decode step: the n stream queries of token T-1 in one pass.
+
+    [HD-tahou] 实验效果与成本分析: the n streams of a new token are processed
+    in parallel in one forward pass. The per-stream KV cache ([HD-aiflow]
+    "Latent computation scaling and Hidden Decoding"; independent per-stream
+    state, [HD-tahou] 中间流的作用验证) holds tokens 0..T-1, token T-1's own
+    n rows included.
+
+    q_new: [B][n][Hq][D]; k_cache, v_cache: [B][n][T_max][Hkv][D].
+    Returns o [B][n][Hq][D]: row k is the output at expanded position
+    (T-1)*n + k, i.e. the last n rows of :func:`attn_fwd` over the T tokens.
+    """
+    q_new = np.asarray(q_new, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)[:, :, :T]
+    vc = np.asarray(v_cache, dtype=np.float64)[:, :, :T]
+    B, n, Hq, D = q_new.shape
+    Hkv = kc.shape[3]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    # Rebuild the expanded key/value sequence: position t*n + k holds stream k of token t.
+    K = interleave(np.moveaxis(kc, 1, 0))  # [B][nT][Hkv][D]
+    V = interleave(np.moveaxis(vc, 1, 0))
+    rows = (T - 1) * n + np.arange(n)
+    allowed = mask(mode, n, T, window, rows)
+    o = np.empty((B, n, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // G
+            o[b, :, h], _ = attend(q_new[b, :, h], K[b, :, kh], V[b, :, kh], allowed, scale)
+    return o
