@@ -1,0 +1,71 @@
+"""Build libsfattn.so in-tree with hipcc for gfx950.
+
+    python -m hidden_decoding_stream_amd.build
+
+Compiles every HIP source under csrc/ to an object in _build/ (at the repository
+root) and links them into hidden_decoding_stream_amd/libsfattn.so. Always
+recompiles: it is the "does it build" check as well as the build.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import pathlib
+import shutil
+import subprocess
+import sys
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+BUILD = ROOT / "_build"
+LIB = PKG / "libsfattn.so"
+SOURCES = ["api.hip", "interleave.hip", "attn_fwd.hip", "attn_decode.hip"]
+
+ARCH = "gfx950"
+# Packed fp32 VALU ops are disabled: the compiler would otherwise form them
+# from ordinary float code on its own.
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libsfattn)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(verbose: bool = False, extra_flags=()) -> pathlib.Path:
+    cc = hipcc()
+    BUILD.mkdir(exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = BUILD / (pathlib.Path(src).stem + ".o")
+        objs.append(obj)
+        cmds.append([cc, *FLAGS, *extra_flags, "-c", str(CSRC / src), "-o", str(obj)])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        for cmd, r in zip(cmds, ex.map(_run, cmds)):
+            if verbose:
+                print(" ".join(cmd))
+                sys.stdout.write(r.stderr)
+    tmp = LIB.with_name(LIB.name + ".tmp")
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

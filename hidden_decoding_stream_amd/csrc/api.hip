@@ -1,0 +1,194 @@
+// C ABI of libsfattn: host-side validation, then dispatch to the launchers.
+//
+// Every check runs before any HIP call, so a rejected call has no device
+// side effects (and the checks can be exercised on a machine without a GPU).
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/sfattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+sf_status fail(sf_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+sf_status ok() {
+  g_error.clear();
+  return SF_OK;
+}
+
+sf_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SF_ERR_DEVICE, "%s: HIP error %d (%s)", what, int(e), hipGetErrorString(e));
+}
+
+// a*b*... without overflow; false if the product exceeds INT64_MAX.
+bool mul_ok(int64_t& acc, int64_t x) {
+  int64_t r;
+  if (__builtin_mul_overflow(acc, x, &r)) return false;
+  acc = r;
+  return true;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + uint64_t(bbytes) && b0 < a0 + uint64_t(abytes);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+const char* mode_name(int32_t m) {
+  switch (m) {
+    case SF_INTRA: return "intra";
+    case SF_CROSS_FULL: return "cross_full";
+    case SF_CROSS_WINDOW: return "cross_window";
+    default: return "?";
+  }
+}
+
+// Checks shared by prefill and decode.
+sf_status check_heads(int32_t n, int32_t hq, int32_t hkv, int32_t d, int32_t mode, int64_t window,
+                      float scale) {
+  if (n < 1) return fail(SF_ERR_INVALID, "n must be >= 1 (got %d)", n);
+  if (hq < 1 || hkv < 1) return fail(SF_ERR_INVALID, "head counts must be >= 1 (hq=%d hkv=%d)", hq, hkv);
+  if (hq % hkv) return fail(SF_ERR_INVALID, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
+  if (mode != SF_INTRA && mode != SF_CROSS_FULL && mode != SF_CROSS_WINDOW)
+    return fail(SF_ERR_INVALID, "unknown mode %d", mode);
+  if (mode == SF_CROSS_WINDOW && window < 1)
+    return fail(SF_ERR_INVALID, "cross_window needs window >= 1 (got %lld)", (long long)window);
+  if (!std::isfinite(scale)) return fail(SF_ERR_INVALID, "scale must be finite");
+  if (!(scale > 0.0f)) return fail(SF_ERR_UNSUPPORTED, "scale must be > 0 (got %g)", double(scale));
+  if (d != 64 && d != 128) return fail(SF_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  return SF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sf_abi_version(void) { return SF_ABI_VERSION; }
+
+const char* sf_last_error(void) { return g_error.c_str(); }
+
+sf_status sf_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_t batch,
+                        int64_t row_bytes, int32_t inverse, hipStream_t stream) {
+  if (n < 1) return fail(SF_ERR_INVALID, "n must be >= 1 (got %d)", n);
+  if (L < 0 || batch < 0) return fail(SF_ERR_INVALID, "L and batch must be >= 0");
+  if (row_bytes < 1) return fail(SF_ERR_INVALID, "row_bytes must be >= 1");
+  if (inverse != 0 && inverse != 1) return fail(SF_ERR_INVALID, "inverse must be 0 or 1");
+  if (L == 0 || batch == 0) return ok();
+  if (!src || !dst) return fail(SF_ERR_INVALID, "null src or dst");
+  int64_t bytes = row_bytes;
+  if (!mul_ok(bytes, n) || !mul_ok(bytes, L) || !mul_ok(bytes, batch))
+    return fail(SF_ERR_INVALID, "tensor size overflows int64");
+  if (overlaps(src, bytes, dst, bytes)) return fail(SF_ERR_INVALID, "src and dst overlap");
+  const uint64_t align = uint64_t(reinterpret_cast<uintptr_t>(src)) |
+                         uint64_t(reinterpret_cast<uintptr_t>(dst)) | uint64_t(row_bytes);
+  const int vb = (align & 15) == 0 ? 16 : (align & 7) == 0 ? 8 : (align & 3) == 0 ? 4 : (align & 1) == 0 ? 2 : 1;
+  if (uint64_t(bytes) / uint64_t(vb) >= (uint64_t(1) << 32))
+    return fail(SF_ERR_UNSUPPORTED, "interleave of %lld bytes exceeds 2^32 vectors of %d bytes",
+                (long long)bytes, vb);
+  return device_status(sfa::launch_interleave(src, dst, n, L, batch, row_bytes, inverse, stream),
+                       "sf_interleave launch");
+}
+
+sf_status sf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
+                      int32_t mode, int64_t window, float scale, hipStream_t stream) {
+  if (batch < 0 || L < 0) return fail(SF_ERR_INVALID, "batch and L must be >= 0");
+  sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
+  if (st != SF_OK) return st;
+  if (batch == 0 || L == 0) return ok();
+  if (!q || !k || !v || !o) return fail(SF_ERR_INVALID, "null q, k, v or o");
+  int64_t qe = batch, kve = batch;
+  if (!mul_ok(qe, n) || !mul_ok(qe, L) || !mul_ok(qe, hq) || !mul_ok(qe, d) ||
+      !mul_ok(kve, n) || !mul_ok(kve, L) || !mul_ok(kve, hkv) || !mul_ok(kve, d))
+    return fail(SF_ERR_INVALID, "tensor size overflows int64");
+  if (qe > (int64_t(1) << 30))
+    return fail(SF_ERR_UNSUPPORTED, "q has %lld elements; at most 2^30 supported", (long long)qe);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(SF_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(SF_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
+  if (overlaps(o, qe * 2, q, qe * 2) || overlaps(o, qe * 2, k, kve * 2) || overlaps(o, qe * 2, v, kve * 2))
+    return fail(SF_ERR_INVALID, "o overlaps an input");
+  if (lse) {
+    int64_t le = batch;
+    mul_ok(le, hq);
+    mul_ok(le, n);
+    mul_ok(le, L);
+    if (overlaps(lse, le * 4, o, qe * 2) || overlaps(lse, le * 4, q, qe * 2) ||
+        overlaps(lse, le * 4, k, kve * 2) || overlaps(lse, le * 4, v, kve * 2))
+      return fail(SF_ERR_INVALID, "lse overlaps another tensor");
+  }
+  sfa::FwdArgs a{q, k, v, o, lse, batch, n, L, hq, hkv, d, mode, window, scale};
+  return device_status(sfa::launch_attn_fwd(a, stream), "sf_attn_fwd launch");
+}
+
+size_t sf_attn_decode_workspace_bytes(int64_t batch, int32_t n, int64_t T, int32_t hq,
+                                      int32_t hkv, int32_t d, int32_t mode, int64_t window,
+                                      int32_t num_splits) {
+  if (batch <= 0 || T < 1 || num_splits < 0) return 0;
+  if (check_heads(n, hq, hkv, d, mode, window, 1.0f) != SF_OK) return 0;
+  return sfa::plan_decode(batch, n, T, hq, hkv, d, mode, window, num_splits).ws_bytes;
+}
+
+sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_cache, void* o_new,
+                         int64_t batch, int32_t n, int64_t T, int64_t T_max, int32_t hq,
+                         int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,
+                         int32_t num_splits, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (batch < 0) return fail(SF_ERR_INVALID, "batch must be >= 0");
+  if (T < 1) return fail(SF_ERR_INVALID, "T must be >= 1 (got %lld)", (long long)T);
+  if (T_max < T) return fail(SF_ERR_INVALID, "T (%lld) exceeds T_max (%lld)", (long long)T, (long long)T_max);
+  if (num_splits < 0) return fail(SF_ERR_INVALID, "num_splits must be >= 0");
+  sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
+  if (st != SF_OK) return st;
+  const int32_t G = hq / hkv;
+  if (mode == SF_INTRA ? G > 16 : int64_t(n) * G > 16)
+    return fail(SF_ERR_UNSUPPORTED, "%s decode supports at most 16 query rows per kv head (n=%d, G=%d)",
+                mode_name(mode), n, G);
+  if (batch == 0) return ok();
+  if (!q_new || !k_cache || !v_cache || !o_new) return fail(SF_ERR_INVALID, "null q_new, cache or o_new");
+  int64_t ce = batch, qe = batch;
+  if (!mul_ok(ce, n) || !mul_ok(ce, T_max) || !mul_ok(ce, hkv) || !mul_ok(ce, d) || !mul_ok(qe, n) ||
+      !mul_ok(qe, hq) || !mul_ok(qe, d))
+    return fail(SF_ERR_INVALID, "tensor size overflows int64");
+  if (!aligned(q_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o_new, 16))
+    return fail(SF_ERR_UNSUPPORTED, "q_new, caches and o_new must be 16-byte aligned");
+  if (overlaps(o_new, qe * 2, q_new, qe * 2) || overlaps(o_new, qe * 2, k_cache, ce * 2) ||
+      overlaps(o_new, qe * 2, v_cache, ce * 2))
+    return fail(SF_ERR_INVALID, "o_new overlaps an input");
+  if (T_max > INT32_MAX / 2 || ce > (int64_t(1) << 40))
+    return fail(SF_ERR_UNSUPPORTED, "cache too large (T_max=%lld)", (long long)T_max);
+  const sfa::DecodePlan plan = sfa::plan_decode(batch, n, T, hq, hkv, d, mode, window, num_splits);
+  if (plan.units > 65535)
+    return fail(SF_ERR_UNSUPPORTED, "decode supports at most 65535 key ranges (batch*hkv%s = %lld)",
+                mode == SF_INTRA ? "*n" : "", (long long)plan.units);
+  if (!workspace || workspace_bytes < plan.ws_bytes)
+    return fail(SF_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                plan.ws_bytes);
+  if (!aligned(workspace, 16)) return fail(SF_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (overlaps(workspace, int64_t(plan.ws_bytes), o_new, qe * 2) ||
+      overlaps(workspace, int64_t(plan.ws_bytes), q_new, qe * 2) ||
+      overlaps(workspace, int64_t(plan.ws_bytes), k_cache, ce * 2) ||
+      overlaps(workspace, int64_t(plan.ws_bytes), v_cache, ce * 2))
+    return fail(SF_ERR_INVALID, "workspace overlaps a tensor");
+  sfa::DecodeArgs a{q_new, k_cache, v_cache, o_new, batch, n, T, T_max, hq, hkv, d, mode,
+                    window, scale, num_splits, workspace};
+  return device_status(sfa::launch_attn_decode(a, plan, stream), "sf_attn_decode launch");
+}
+
+}  // extern "C"

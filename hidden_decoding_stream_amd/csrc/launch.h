@@ -1,0 +1,61 @@
+// Internal kernel launchers of libsfattn. Arguments arrive here already
+// validated by the C ABI layer (api.hip); these functions only pick a
+// configuration and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sfa {
+
+hipError_t launch_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_t batch,
+                             int64_t row_bytes, int inverse, hipStream_t stream);
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t batch;
+  int32_t n;
+  int64_t L;
+  int32_t hq, hkv, d;
+  int32_t mode;
+  int64_t window;
+  float scale;
+};
+hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  void* o;
+  int64_t batch;
+  int32_t n;
+  int64_t T, T_max;
+  int32_t hq, hkv, d;
+  int32_t mode;
+  int64_t window;
+  float scale;
+  int32_t num_splits;
+  void* ws;
+};
+// Split plan shared by the workspace query and the launcher.
+struct DecodePlan {
+  int32_t rows_per_unit;   // query rows that share one key range (n*G cross, G intra)
+  int64_t units;           // independent key ranges
+  int64_t t_lo;            // first cache token any query may see
+  int64_t keys_per_stream; // padded tokens per stream in the key index space
+  int64_t keys;            // keys per unit in the key index space (padded)
+  int32_t splits;          // pieces per unit
+  int64_t chunk;           // keys per piece (multiple of the step)
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t hkv, int32_t d,
+                       int32_t mode, int64_t window, int32_t num_splits);
+hipError_t launch_attn_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
+
+}  // namespace sfa

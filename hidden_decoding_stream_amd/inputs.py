@@ -5,8 +5,11 @@ of the method's arithmetic (no index maps, masks or softmax), so the GPU path
 and the CPU oracle can both take their inputs from it without sharing any
 computation.
 
-Recipe (the same on every machine, no GPU needed):
-  * a CPU ``torch.Generator`` seeded with ``seed``;
+Recipe:
+  * a ``torch.Generator`` seeded with ``seed``, on the CPU by default (the
+    same values on every machine) or on the GPU for the large workloads
+    (``device="cuda"``: much faster to draw; the oracle then consumes exact
+    copies of the GPU tensors, so parity does not depend on the stream);
   * tensors are drawn in a fixed order (Q, K, V for prefill; q_new, K cache,
     V cache for decode), each as float32 N(0, 1);
   * attention inputs are then rounded to bfloat16 (round-to-nearest-even).
@@ -97,15 +100,15 @@ def decode_workload(batch: int, mode: str, T: int = 8192, T_max: int | None = No
                           batch, 32, 8, 128, mode, window=window, seed=1004)
 
 
-def _gen(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def _gen(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return g
 
 
 def normal(shape, gen: torch.Generator) -> torch.Tensor:
-    """float32 N(0,1) on the CPU."""
-    return torch.randn(*shape, generator=gen, dtype=torch.float32)
+    """float32 N(0,1) on the generator's device."""
+    return torch.randn(*shape, generator=gen, dtype=torch.float32, device=gen.device)
 
 
 def to_bf16(x: torch.Tensor) -> torch.Tensor:
@@ -114,10 +117,10 @@ def to_bf16(x: torch.Tensor) -> torch.Tensor:
 
 
 def stream_qkv(n: int, L: int, batch: int, hq: int, hkv: int, d: int, seed: int,
-               dtype: str = "bf16"):
+               dtype: str = "bf16", device="cpu"):
     """Per-stream Q, K, V as produced by the n stream embeddings: layout
     [n][batch][L][heads][d], drawn Q then K then V."""
-    g = _gen(seed)
+    g = _gen(seed, device)
     q = normal((n, batch, L, hq, d), g)
     k = normal((n, batch, L, hkv, d), g)
     v = normal((n, batch, L, hkv, d), g)
@@ -126,26 +129,26 @@ def stream_qkv(n: int, L: int, batch: int, hq: int, hkv: int, d: int, seed: int,
     return q, k, v
 
 
-def expanded_qkv(S: int, batch: int, hq: int, hkv: int, d: int, seed: int):
+def expanded_qkv(S: int, batch: int, hq: int, hkv: int, d: int, seed: int, device="cpu"):
     """Q, K, V already in the expanded layout [batch][S][heads][d] (bf16),
     drawn Q then K then V. Used where the interleave is not under test."""
-    g = _gen(seed)
+    g = _gen(seed, device)
     q = to_bf16(normal((batch, S, hq, d), g))
     k = to_bf16(normal((batch, S, hkv, d), g))
     v = to_bf16(normal((batch, S, hkv, d), g))
     return q, k, v
 
 
-def workload_qkv(w: Workload):
+def workload_qkv(w: Workload, device="cpu"):
     """Expanded-layout bf16 Q, K, V for a prefill workload."""
-    return expanded_qkv(w.S, w.batch, w.hq, w.hkv, w.d, w.seed)
+    return expanded_qkv(w.S, w.batch, w.hq, w.hkv, w.d, w.seed, device)
 
 
-def decode_inputs(w: DecodeWorkload):
+def decode_inputs(w: DecodeWorkload, device="cpu"):
     """q_new [batch][n][hq][d] and the per-stream caches [batch][n][T_max][hkv][d]
     (bf16), drawn q_new, then K cache, then V cache. Slots t >= T hold random
     values too; a correct decode never reads them."""
-    g = _gen(w.seed)
+    g = _gen(w.seed, device)
     q = to_bf16(normal((w.batch, w.n, w.hq, w.d), g))
     kc = to_bf16(normal((w.batch, w.n, w.T_max, w.hkv, w.d), g))
     vc = to_bf16(normal((w.batch, w.n, w.T_max, w.hkv, w.d), g))

@@ -1,0 +1,187 @@
+"""Python binding of libsfattn (ctypes): argument marshalling only.
+
+Every function here has the name of the C entry point it calls (declared in
+include/sfattn.h). They take torch tensors that already live on the GPU, pass
+their device pointers and torch's current HIP stream, and raise SFError when
+the library returns a non-OK status. All computation happens in the library's
+HIP kernels; there is no fallback path. If libsfattn.so has not been built,
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import pathlib
+
+import torch
+
+_PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = pathlib.Path(os.environ.get("SFATTN_LIB", str(_PKG / "libsfattn.so")))
+
+SF_OK, SF_ERR_INVALID, SF_ERR_UNSUPPORTED, SF_ERR_DEVICE = 0, 1, 2, 3
+MODES = {"intra": 0, "cross_full": 1, "cross_window": 2}
+
+_lib_handle = None
+
+
+class SFError(RuntimeError):
+    """A non-OK status from libsfattn, with the library's message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libsfattn status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsfattn.so (once) and declare the C signatures."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m hidden_decoding_stream_amd.build`")
+    L = ctypes.CDLL(str(LIB_PATH))
+    c = ctypes
+    L.sf_abi_version.restype = c.c_int32
+    L.sf_abi_version.argtypes = []
+    L.sf_last_error.restype = c.c_char_p
+    L.sf_last_error.argtypes = []
+    L.sf_interleave.restype = c.c_int
+    L.sf_interleave.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int64, c.c_int64, c.c_int64,
+                                c.c_int32, c.c_void_p]
+    L.sf_attn_fwd.restype = c.c_int
+    L.sf_attn_fwd.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                              c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32, c.c_int32,
+                              c.c_int32, c.c_int64, c.c_float, c.c_void_p]
+    L.sf_attn_decode_workspace_bytes.restype = c.c_size_t
+    L.sf_attn_decode_workspace_bytes.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32,
+                                                 c.c_int32, c.c_int32, c.c_int64, c.c_int32]
+    L.sf_attn_decode.restype = c.c_int
+    L.sf_attn_decode.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                 c.c_int64, c.c_int32, c.c_int64, c.c_int64, c.c_int32, c.c_int32,
+                                 c.c_int32, c.c_int32, c.c_int64, c.c_float, c.c_int32,
+                                 c.c_void_p, c.c_size_t, c.c_void_p]
+    _lib_handle = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != SF_OK:
+        raise SFError(status, lib().sf_last_error().decode(errors="replace"))
+
+
+def _mode(mode) -> int:
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"unknown mode {mode!r}")
+        return MODES[mode]
+    return int(mode)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def sf_abi_version() -> int:
+    return int(lib().sf_abi_version())
+
+
+def sf_last_error() -> str:
+    return lib().sf_last_error().decode(errors="replace")
+
+
+def sf_interleave(src: torch.Tensor, n: int, inverse: bool = False, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Forward: src [n][B][L][...] -> [B][n*L][...]; inverse: [B][n*L][...] -> [n][B][L][...].
+    Any dtype; a bit-exact copy."""
+    if not inverse:
+        if src.dim() < 3 or src.shape[0] != n:
+            raise ValueError("forward interleave expects src of shape [n][B][L][...]")
+        _, B, L = src.shape[:3]
+        out_shape = (B, n * L) + tuple(src.shape[3:])
+    else:
+        if src.dim() < 2 or src.shape[1] % n:
+            raise ValueError("inverse interleave expects src of shape [B][n*L][...]")
+        B, S = src.shape[:2]
+        L = S // n
+        out_shape = (n, B, L) + tuple(src.shape[2:])
+    if out is None:
+        out = torch.empty(out_shape, dtype=src.dtype, device=src.device)
+    elif tuple(out.shape) != out_shape or out.dtype != src.dtype:
+        raise ValueError(f"out must be {out_shape} {src.dtype}")
+    row_bytes = src.element_size() * int(math.prod(out_shape[3:] if inverse else src.shape[3:]))
+    _check(lib().sf_interleave(_dev(src, "src"), _dev(out, "out"), n, L, B, row_bytes, int(inverse),
+                               _stream(stream)))
+    return out
+
+
+def sf_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode, n: int, window: int = 0,
+                scale: float | None = None, out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = None,
+                stream=None):
+    """Prefill attention. q [B][n*L][hq][d], k/v [B][n*L][hkv][d], bf16.
+    Returns out, or (out, lse) when lse is True or a float32 [B][hq][n*L] tensor."""
+    B, S, hq, d = q.shape
+    hkv = k.shape[2]
+    if S % n:
+        raise ValueError("sequence length must be a multiple of n")
+    if k.shape != (B, S, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B][S][hkv][d] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+    lse_ptr = _dev(lse, "lse", torch.float32) if want_lse else None
+    bf = torch.bfloat16
+    _check(lib().sf_attn_fwd(_dev(q, "q", bf), _dev(k, "k", bf), _dev(v, "v", bf), _dev(out, "out", bf),
+                             lse_ptr, B, n, S // n, hq, hkv, d, _mode(mode), int(window), float(scale),
+                             _stream(stream)))
+    return (out, lse) if want_lse else out
+
+
+def sf_attn_decode_workspace_bytes(batch: int, n: int, T: int, hq: int, hkv: int, d: int, mode,
+                                   window: int = 0, num_splits: int = 0) -> int:
+    return int(lib().sf_attn_decode_workspace_bytes(batch, n, T, hq, hkv, d, _mode(mode), int(window),
+                                                    int(num_splits)))
+
+
+def sf_attn_decode(q_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, T: int, mode,
+                   window: int = 0, scale: float | None = None, num_splits: int = 0,
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Decode the n stream queries of token T-1. q_new [B][n][hq][d];
+    caches [B][n][T_max][hkv][d]; bf16. The workspace is allocated with torch
+    when not given."""
+    B, n, hq, d = q_new.shape
+    T_max, hkv = k_cache.shape[2], k_cache.shape[3]
+    if k_cache.shape != (B, n, T_max, hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B][n][T_max][hkv][d] matching q_new")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q_new)
+    need = sf_attn_decode_workspace_bytes(B, n, T, hq, hkv, d, mode, window, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_new.device)
+    bf = torch.bfloat16
+    _check(lib().sf_attn_decode(_dev(q_new, "q_new", bf), _dev(k_cache, "k_cache", bf),
+                                _dev(v_cache, "v_cache", bf), _dev(out, "out", bf), B, n, int(T), T_max,
+                                hq, hkv, d, _mode(mode), int(window), float(scale), int(num_splits),
+                                _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                _stream(stream)))
+    return out

@@ -1,0 +1,144 @@
+/*
+ * sfattn.h -- C ABI of libsfattn: stream-factorized attention (SFA) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (Hidden Decoding) expands each of L tokens into n stream
+ * representations and runs the unchanged transformer over the expanded
+ * sequence of length S = n*L. Stream-factorized attention makes most layers
+ * attend within a stream and a few across streams. Sources, cited below by
+ * page and section:
+ *   [HD-tahou]  "微信WeLM提出Hidden Decoding：大模型推理新范式" (www.tahou.com),
+ *               sections 隐式序列缩放的技术细节, 规模化落地的工程优化,
+ *               实验效果与成本分析, 中间流的作用验证.
+ *   [HD-aiflow] aiflownews.com/?p=965, sections "Latent computation scaling and
+ *               Hidden Decoding" and "Tencent's ecosystem first scaling strategy".
+ *
+ * Conventions shared by every call:
+ *   - Indices are 0-based: token i, stream k sits at expanded position
+ *     p = i*n + k (the page's 1-based (i-1)n+k, [HD-tahou] 隐式序列缩放的技术细节,
+ *     step 1).
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates or frees device memory; decode scratch space is passed in
+ *     by the caller (see sf_attn_decode_workspace_bytes).
+ *   - Calls enqueue work on `stream` (0 = the null stream) and return without
+ *     synchronising. Results are valid once the stream has been synchronised.
+ *   - Arguments are validated on the host before any HIP call. A rejected call
+ *     launches nothing, touches no device state and returns SF_ERR_INVALID
+ *     (malformed arguments) or SF_ERR_UNSUPPORTED (well-formed but outside the
+ *     supported set). A failed launch returns SF_ERR_DEVICE. In every non-OK
+ *     case sf_last_error() describes the problem.
+ *   - Calls are re-entrant: the only mutable state is the thread-local error
+ *     string. Calls that write the same output buffer concurrently race.
+ *   - Empty problems (batch == 0 or L == 0) are valid no-ops.
+ */
+#ifndef SFATTN_H
+#define SFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SF_ABI_VERSION 1
+
+typedef enum {
+  SF_OK = 0,
+  SF_ERR_INVALID = 1,     /* malformed arguments: null pointer, negative size, T > T_max, ... */
+  SF_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported set (head dim, alignment, size limits) */
+  SF_ERR_DEVICE = 3       /* the HIP runtime reported an error while launching */
+} sf_status;
+
+/* Attention masks of stream-factorized attention ([HD-tahou] 规模化落地的工程优化).
+ * For query position p and key position q (both expanded positions):
+ *   SF_INTRA        q <= p and q mod n == p mod n: only earlier positions of the
+ *                   same stream, itself included (the intra-stream layer).
+ *   SF_CROSS_FULL   q <= p: standard causal attention over the expanded sequence
+ *                   (the cross-stream layer in its full-attention form; also
+ *                   [HD-tahou] 隐式序列缩放的技术细节, step 2).
+ *   SF_CROSS_WINDOW q <= p and p - q < window: the cross-stream layer in its
+ *                   sliding-window form; `window` counts expanded positions,
+ *                   the query itself included. */
+typedef enum { SF_INTRA = 0, SF_CROSS_FULL = 1, SF_CROSS_WINDOW = 2 } sf_mode;
+
+/* Returns SF_ABI_VERSION of the loaded library. */
+int32_t sf_abi_version(void);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next libsfattn call on the same thread. */
+const char* sf_last_error(void);
+
+/* Stream interleave ([HD-tahou] 隐式序列缩放的技术细节, step 1: stream k of token
+ * i goes to position (i-1)n+k, 1-based) and its exact inverse (used to fill the
+ * per-stream KV cache, [HD-aiflow] "Latent computation scaling and Hidden
+ * Decoding").
+ *   inverse == 0:  dst[b][i*n + k][0:row_bytes] = src[k][b][i][0:row_bytes]
+ *                  src layout [n][batch][L][row], dst layout [batch][n*L][row]
+ *   inverse == 1:  dst[k][b][i][:] = src[b][i*n + k][:]   (layouts swapped)
+ * A row is `row_bytes` opaque bytes (e.g. heads*d*sizeof(element)), so any
+ * element type works and the copy is bit-exact. src and dst must not overlap.
+ * Any alignment and row size is accepted; 16-byte aligned pointers with
+ * row_bytes a multiple of 16 take the widest (fastest) copy.
+ * Limits: total bytes / vector width < 2^32 (SF_ERR_UNSUPPORTED otherwise). */
+sf_status sf_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_t batch,
+                        int64_t row_bytes, int32_t inverse, hipStream_t stream);
+
+/* Prefill attention over the expanded sequence, one of the three masks above,
+ * with grouped-query attention ([HD-aiflow] "Tencent's ecosystem first scaling
+ * strategy"): query head h reads key/value head h / (hq/hkv).
+ *   q, o : bf16 [batch][n*L][hq][d]      (o may not alias q, k or v)
+ *   k, v : bf16 [batch][n*L][hkv][d]
+ *   lse  : fp32 [batch][hq][n*L] or NULL; lse[b][h][p] = ln sum_{q allowed}
+ *          exp(scale * <q_p, k_q>), the natural-log normaliser of row p.
+ *   window: used only by SF_CROSS_WINDOW (must be >= 1 there); ignored otherwise.
+ *   scale : softmax scale applied to q.k (e.g. 1/sqrt(d)); finite and > 0.
+ * Output rows are O[p] = sum_q softmax_q(scale*q_p.k_q over allowed q) v_q,
+ * computed with fp32 accumulation and rounded to bf16 once.
+ * Supported: d in {64, 128}; hq % hkv == 0; q, k, v, o 16-byte aligned, lse
+ * 4-byte aligned; batch*n*L*hq*d <= 2^30 elements. */
+sf_status sf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
+                      int32_t mode, int64_t window, float scale, hipStream_t stream);
+
+/* Bytes of device workspace sf_attn_decode needs for these arguments (0 if the
+ * arguments are invalid or the problem is empty). num_splits as for
+ * sf_attn_decode; the result depends on nothing else. */
+size_t sf_attn_decode_workspace_bytes(int64_t batch, int32_t n, int64_t T, int32_t hq,
+                                      int32_t hkv, int32_t d, int32_t mode, int64_t window,
+                                      int32_t num_splits);
+
+/* One decode step: the n stream queries of the newest token t = T-1 in one
+ * pass ([HD-tahou] 实验效果与成本分析: the n streams of a token go through one
+ * forward pass in parallel) against a per-stream KV cache ([HD-aiflow] "Latent
+ * computation scaling and Hidden Decoding"; independent per-stream state,
+ * [HD-tahou] 中间流的作用验证).
+ *   q_new, o_new : bf16 [batch][n][hq][d]; row k is stream k of token T-1,
+ *                  i.e. expanded position (T-1)*n + k.
+ *   k_cache, v_cache : bf16 [batch][n][T_max][hkv][d]; tokens 0..T-1 are valid
+ *                  and the caller has already written token T-1's n rows.
+ *   The result equals rows (T-1)*n .. (T-1)*n + n-1 of sf_attn_fwd over the T
+ *   tokens with the same mode and window: under the cross masks stream k of
+ *   the new token also sees streams 0..k of that token; under SF_INTRA it sees
+ *   tokens 0..T-1 of its own stream only.
+ *   workspace : device scratch of at least sf_attn_decode_workspace_bytes(...)
+ *               bytes, 16-byte aligned. Its contents on entry do not matter.
+ *   num_splits: how many pieces each key range is cut into (0 = chosen by the
+ *               library from the problem size). The result does not depend on
+ *               it beyond float rounding.
+ * Supported: d in {64, 128}; hq % hkv == 0; n*G <= 16 query rows per key/value
+ * head under the cross masks (G = hq/hkv), G <= 16 under SF_INTRA; 16-byte
+ * aligned q_new, caches and o_new. */
+sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_cache, void* o_new,
+                         int64_t batch, int32_t n, int64_t T, int64_t T_max, int32_t hq,
+                         int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,
+                         int32_t num_splits, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFATTN_H */

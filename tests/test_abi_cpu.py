@@ -1,0 +1,140 @@
+"""libsfattn loads, exports what include/sfattn.h declares, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+import hidden_decoding_stream_amd as sfa
+from hidden_decoding_stream_amd import sfattn as B
+
+HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "sfattn.h"
+
+if not B.LIB_PATH.exists():
+    pytest.skip("libsfattn.so not built", allow_module_level=True)
+
+L = sfa.lib()
+# fake, 16-byte aligned, never dereferenced device addresses
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x40000000)
+P3 = ctypes.c_void_p(0x80000000)
+P4 = ctypes.c_void_p(0xC0000000)
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sf_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"sf_interleave", "sf_attn_fwd", "sf_attn_decode", "sf_attn_decode_workspace_bytes",
+            "sf_abi_version", "sf_last_error"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_abi_version():
+    assert sfa.sf_abi_version() == 1
+
+
+def fwd(q=P, k=P2, v=P3, o=P4, lse=None, batch=1, n=4, Lt=64, hq=4, hkv=4, d=64, mode=1, window=0,
+        scale=0.125):
+    return L.sf_attn_fwd(q, k, v, o, lse, batch, n, Lt, hq, hkv, d, mode, window, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), B.SF_ERR_INVALID),
+    (dict(batch=-1), B.SF_ERR_INVALID),
+    (dict(Lt=-3), B.SF_ERR_INVALID),
+    (dict(hq=0), B.SF_ERR_INVALID),
+    (dict(hq=6, hkv=4), B.SF_ERR_INVALID),
+    (dict(mode=7), B.SF_ERR_INVALID),
+    (dict(mode=2, window=0), B.SF_ERR_INVALID),
+    (dict(scale=float("nan")), B.SF_ERR_INVALID),
+    (dict(scale=float("inf")), B.SF_ERR_INVALID),
+    (dict(scale=-1.0), B.SF_ERR_UNSUPPORTED),
+    (dict(d=96), B.SF_ERR_UNSUPPORTED),
+    (dict(d=256), B.SF_ERR_UNSUPPORTED),
+    (dict(q=None), B.SF_ERR_INVALID),
+    (dict(o=None), B.SF_ERR_INVALID),
+    (dict(q=ctypes.c_void_p(0x10008)), B.SF_ERR_UNSUPPORTED),
+    (dict(lse=ctypes.c_void_p(0x20002)), B.SF_ERR_UNSUPPORTED),
+    (dict(o=P), B.SF_ERR_INVALID),                       # o aliases q
+    (dict(batch=1 << 20, Lt=1 << 20), B.SF_ERR_UNSUPPORTED),  # beyond 2^30 elements
+    (dict(batch=1 << 40, Lt=1 << 40), B.SF_ERR_INVALID),      # int64 overflow
+])
+def test_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+    assert sfa.sf_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(Lt=0), dict(batch=0, q=None, k=None, v=None, o=None)])
+def test_fwd_empty_is_noop(kw):
+    assert fwd(**kw) == B.SF_OK
+    assert sfa.sf_last_error() == ""
+
+
+def ilv(src=P, dst=P2, n=4, Lt=16, batch=2, row=64, inverse=0):
+    return L.sf_interleave(src, dst, n, Lt, batch, row, inverse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), B.SF_ERR_INVALID),
+    (dict(Lt=-1), B.SF_ERR_INVALID),
+    (dict(row=0), B.SF_ERR_INVALID),
+    (dict(inverse=2), B.SF_ERR_INVALID),
+    (dict(src=None), B.SF_ERR_INVALID),
+    (dict(dst=ctypes.c_void_p(0x10000 + 64)), B.SF_ERR_INVALID),   # overlap
+    (dict(row=1 << 40, Lt=1 << 30), B.SF_ERR_INVALID),            # overflow
+    (dict(row=1 << 30, Lt=1 << 4, n=64, batch=64, dst=ctypes.c_void_p(1 << 50)), B.SF_ERR_UNSUPPORTED),
+])
+def test_interleave_rejects(kw, status):
+    assert ilv(**kw) == status
+
+
+def test_interleave_empty_is_noop():
+    assert ilv(Lt=0, src=None, dst=None) == B.SF_OK
+    assert ilv(batch=0) == B.SF_OK
+
+
+def dec(q=P, kc=P2, vc=P3, o=P4, batch=1, n=4, T=16, Tmax=16, hq=32, hkv=8, d=128, mode=1, window=0,
+        scale=0.088, splits=0, ws=ctypes.c_void_p(0x100000000), wsb=1 << 30):
+    return L.sf_attn_decode(q, kc, vc, o, batch, n, T, Tmax, hq, hkv, d, mode, window, scale, splits,
+                            ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), B.SF_ERR_INVALID),
+    (dict(T=17), B.SF_ERR_INVALID),                  # T > T_max
+    (dict(batch=-1), B.SF_ERR_INVALID),
+    (dict(splits=-1), B.SF_ERR_INVALID),
+    (dict(n=8), B.SF_ERR_UNSUPPORTED),                # n*G = 32 > 16 rows under cross
+    (dict(hq=32, hkv=1, mode=0), B.SF_ERR_UNSUPPORTED),  # G = 32 > 16 under intra
+    (dict(d=80), B.SF_ERR_UNSUPPORTED),
+    (dict(mode=2, window=0), B.SF_ERR_INVALID),
+    (dict(ws=None), B.SF_ERR_INVALID),
+    (dict(wsb=16), B.SF_ERR_INVALID),                 # workspace too small
+    (dict(q=None), B.SF_ERR_INVALID),
+    (dict(kc=ctypes.c_void_p(0x40000004)), B.SF_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_empty_batch_is_noop():
+    assert dec(batch=0) == B.SF_OK
+
+
+def test_workspace_query():
+    ws = sfa.sf_attn_decode_workspace_bytes(1, 4, 8192, 32, 8, 128, "cross_full")
+    assert ws > 0 and ws % 256 == 0
+    # one split: rows * (d + 2) floats, each part rounded to 256 bytes
+    one = sfa.sf_attn_decode_workspace_bytes(1, 4, 8192, 32, 8, 128, "cross_full", num_splits=1)
+    rows = 1 * 4 * 32
+    assert one == -(-rows * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
+    assert sfa.sf_attn_decode_workspace_bytes(0, 4, 8192, 32, 8, 128, "intra") == 0
+    assert sfa.sf_attn_decode_workspace_bytes(1, 4, 0, 32, 8, 128, "intra") == 0
+    assert sfa.sf_attn_decode_workspace_bytes(1, 4, 16, 32, 8, 96, "intra") == 0

@@ -1,0 +1,161 @@
+"""sf_attn_fwd on the GPU against the fp64 oracle.
+
+Small problems are compared on every output element (several key tiles, ragged
+tails, all three masks, GQA and MHA, d = 64 and 128). The full-size workloads
+run in the exact launch configuration the benchmark times and are compared on
+sampled query rows (all heads, all batch elements), which the oracle computes
+one by one. Masks are checked bit-exactly with probes: constant keys make the
+softmax uniform over the allowed set, one-hot values then read out, per query
+row, which probe keys were admitted (exactly) and the lse gives the count.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hidden_decoding_stream_amd as sfa
+import hidden_decoding_stream_amd.inputs as I
+import oracle.sfa as orc
+from gpu_util import assert_close, np64, oracle_mask_cols, probe_values, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _scale(d):
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def _run(q, k, v, mode, n, window=0, lse=False):
+    out = sfa.sf_attn_fwd(q.cuda(), k.cuda(), v.cuda(), mode, n, window=window, scale=_scale(q.shape[-1]),
+                          lse=lse)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("w", [I.TINY_INTRA, I.TINY_CROSS], ids=lambda w: w.name)
+def test_tiny_workloads_all_rows(w):
+    say("prefill", w.name)
+    q, k, v = I.workload_qkv(w)
+    o, lse = _run(q, k, v, w.mode, w.n, lse=True)
+    ref, ref_lse = orc.attn_fwd(np64(q), np64(k), np64(v), w.mode, w.n, scale=w.scale, with_lse=True)
+    assert_close(np64(o), ref, w.name)
+    assert np.abs(np64(lse) - ref_lse).max() < 1e-3
+
+
+CASES = [
+    # n, L, B, hq, hkv, d, mode, window
+    (4, 300, 1, 8, 2, 128, "cross_full", 0),
+    (4, 300, 1, 8, 2, 128, "intra", 0),
+    (4, 300, 1, 8, 2, 128, "cross_window", 257),
+    (4, 300, 2, 4, 4, 64, "cross_window", 64),
+    (3, 101, 2, 6, 3, 64, "intra", 0),
+    (3, 101, 1, 2, 1, 128, "cross_full", 0),
+    (1, 500, 1, 4, 4, 128, "intra", 0),
+    (2, 45, 1, 8, 8, 128, "cross_window", 1000),     # window >= S: full causal
+    (4, 17, 1, 16, 2, 128, "cross_full", 0),          # G = 8: two head groups
+    (4, 1, 1, 4, 2, 64, "cross_full", 0),              # one token
+    (2, 700, 1, 4, 1, 64, "cross_window", 1),          # self only
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_small_all_rows(case):
+    n, L, B, hq, hkv, d, mode, W = case
+    say("prefill small", case)
+    q, k, v = I.expanded_qkv(n * L, B, hq, hkv, d, seed=11 + L)
+    o, lse = _run(q, k, v, mode, n, window=W, lse=True)
+    ref, ref_lse = orc.attn_fwd(np64(q), np64(k), np64(v), mode, n, window=W or None, scale=_scale(d),
+                                with_lse=True)
+    assert_close(np64(o), ref, str(case))
+    assert np.abs(np64(lse) - ref_lse).max() < 1e-3
+    if mode == "cross_window" and W == 1:
+        G = hq // hkv
+        assert torch.equal(o.cpu(), v.repeat_interleave(G, dim=2)), "window 1 must return V exactly"
+
+
+def test_window_at_least_sequence_is_full_causal():
+    say("prefill window >= S")
+    q, k, v = I.expanded_qkv(4 * 200, 1, 8, 2, 128, seed=5)
+    a = _run(q, k, v, "cross_window", 4, window=800)
+    b = _run(q, k, v, "cross_full", 4)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode,W", [("intra", 0), ("cross_full", 0), ("cross_window", 37), ("cross_window", 64)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_mask_probe_tiny_all_keys(mode, W, d):
+    """Every (query, key) pair of a 4 x 64 problem, bit-exactly."""
+    n, L, hq, hkv = 4, 64, 4, 2
+    S = n * L
+    say("mask probe tiny", mode, W, d)
+    g = torch.Generator().manual_seed(3)
+    q = I.to_bf16(torch.randn(1, S, hq, d, generator=g))
+    k = torch.zeros(1, S, hkv, d, dtype=torch.bfloat16)
+    rows = np.arange(S)
+    for c0 in range(0, S, d):
+        cols = list(range(c0, min(S, c0 + d)))
+        v = probe_values(S, hkv, d, cols)
+        o, lse = _run(q, k, v, mode, n, window=W, lse=True)
+        sub, cnt = oracle_mask_cols(mode, n, L, W or None, rows, cols)
+        got = np64(o)[0][:, :, :len(cols)] != 0                    # [S][hq][cols]
+        for h in range(hq):
+            assert np.array_equal(got[:, h], sub), (mode, W, h)
+            assert np.array_equal(np.rint(np.exp(np64(lse)[0, h])).astype(np.int64), cnt)
+
+
+@pytest.mark.parametrize("w", [I.CROSS_32K, I.INTRA_32K, I.WINDOW_16K], ids=lambda w: w.name)
+def test_mask_probe_full_size(w):
+    """Probe keys at tile edges, window edges and the stream boundaries, all rows."""
+    say("mask probe full", w.name)
+    S, d = w.S, w.d
+    cand = {0, 1, 2, 3, 4, 5, 63, 64, 65, 127, 128, 129, 255, 256, 1023, 1024, 4095, 4096, 4097,
+            8191, 8192, 16383, 16384, 16385, S // 2 - 1, S // 2, S - 65, S - 64, S - 63, S - 5, S - 4,
+            S - 3, S - 2, S - 1}
+    cols = sorted(c for c in cand if c < S)[:d]
+    gq = torch.Generator(device="cuda").manual_seed(w.seed)
+    q = torch.randn((1, S, w.hq, d), generator=gq, device="cuda").to(torch.bfloat16)
+    k = torch.zeros((1, S, w.hkv, d), dtype=torch.bfloat16, device="cuda")
+    v = probe_values(S, w.hkv, d, cols)
+    o, lse = _run(q, k, v, w.mode, w.n, window=w.window, lse=True)
+    rows = np.arange(S)
+    sub, cnt = oracle_mask_cols(w.mode, w.n, w.L, w.window or None, rows, cols)
+    got = (o[0, :, :, :len(cols)] != 0).cpu().numpy()
+    lse_cnt = torch.round(torch.exp(lse[0].double())).long().cpu().numpy()
+    for h in range(0, w.hq, 5):
+        assert np.array_equal(got[:, h], sub), (w.name, h)
+        assert np.array_equal(lse_cnt[h], cnt), (w.name, h)
+
+
+@pytest.mark.parametrize("w", [I.INTRA_16K, I.WINDOW_16K, I.CROSS_32K, I.INTRA_32K], ids=lambda w: w.name)
+def test_full_size_sampled_rows(w):
+    say("prefill full size", w.name)
+    q, k, v = I.workload_qkv(w, device="cuda")
+    o, lse = _run(q, k, v, w.mode, w.n, window=w.window, lse=True)
+    rows = sample_rows(w.S, seed=w.seed, window=w.window)
+    ref, ref_lse = orc.attn_fwd(np64(q), np64(k), np64(v), w.mode, w.n,
+                                window=w.window or None, scale=w.scale, rows=rows, with_lse=True)
+    assert_close(np64(o[:, rows]), ref, w.name)
+    assert np.abs(np64(lse[:, :, rows]) - ref_lse).max() < 1e-3
+    # determinism: a second run is bitwise identical
+    o2 = _run(q, k, v, w.mode, w.n, window=w.window)
+    assert torch.equal(o, o2)
+
+
+def test_intra_equals_per_stream_cross_full():
+    """Intra attention == causal attention on each de-interleaved stream (GPU vs GPU)."""
+    n, L, hq, hkv, d = 4, 257, 8, 2, 128
+    say("intra vs per-stream causal")
+    q, k, v = I.expanded_qkv(n * L, 1, hq, hkv, d, seed=21)
+    o = _run(q, k, v, "intra", n)
+    for s in range(n):
+        idx = torch.arange(s, n * L, n)
+        os_ = _run(q[:, idx].contiguous(), k[:, idx].contiguous(), v[:, idx].contiguous(), "cross_full", 1)
+        assert_close(np64(o[:, idx]), np64(os_), f"stream {s}", max_abs=1e-2, mean_abs=1e-3)
+
+
+def test_empty_problems():
+    say("prefill empty")
+    q = torch.empty((0, 0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    out = sfa.sf_attn_fwd(q, q[:, :, :2], q[:, :, :2], "cross_full", 4)
+    assert out.shape == q.shape
