@@ -281,23 +281,51 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 }
 
-// One block per output row, one thread per d: merge the splits in order.
+// One wave per output row. Lanes own splits (lane, lane+64, ...) for the
+// max and the normaliser, and d values (lane, lane+64) for the output; the
+// split weights exp2(m_s - M) are broadcast from LDS. Every reduction runs in
+// a fixed order, so the result is deterministic.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecParams p) {
-  const size_t orow = blockIdx.x;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int64_t rows) {
+  constexpr int kMaxSplits = 1024;
+  __shared__ float wsh[4][kMaxSplits];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t orow = int64_t(blockIdx.x) * 4 + wave;
+  if (orow >= rows) return;
   const float* ml = p.ws_ml + orow * p.splits * 2;
   float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ml[2 * s]);
-  float acc = 0.f, lt = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
+  for (int s = lane; s < p.splits; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float lt = 0.f;
+  for (int s = lane; s < p.splits; s += 64) {
     const float ms = ml[2 * s];
-    if (ms == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(ms - M);
-    acc += f * p.ws_o[(orow * p.splits + s) * D + d];
+    const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    wsh[wave][s] = f;
     lt += f * ml[2 * s + 1];
   }
-  p.o[orow * D + d] = __builtin_bit_cast(u16, (__bf16)(acc / lt));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float inv = 1.f / lt;
+  const float* po = p.ws_o + orow * p.splits * D;
+#pragma unroll
+  for (int d0 = 0; d0 < D; d0 += 64) {
+    float acc = 0.f;
+    int s = 0;
+    for (; s + 4 <= p.splits; s += 4) {
+      const float a0 = po[(s + 0) * D + d0 + lane], a1 = po[(s + 1) * D + d0 + lane];
+      const float a2 = po[(s + 2) * D + d0 + lane], a3 = po[(s + 3) * D + d0 + lane];
+      acc += wsh[wave][s + 0] * a0;
+      acc += wsh[wave][s + 1] * a1;
+      acc += wsh[wave][s + 2] * a2;
+      acc += wsh[wave][s + 3] * a3;
+    }
+    for (; s < p.splits; ++s) acc += wsh[wave][s] * po[s * D + d0 + lane];
+    p.o[orow * D + d0 + lane] = __builtin_bit_cast(u16, (__bf16)(acc * inv));
+  }
 }
 
 int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
@@ -326,7 +354,7 @@ DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t 
     want = (target_groups + pl.units - 1) / pl.units;
     want = std::min<int64_t>(want, std::max<int64_t>(1, pl.keys / 256));
   }
-  want = std::max<int64_t>(1, std::min<int64_t>(want, pl.keys / kStep));
+  want = std::max<int64_t>(1, std::min<int64_t>({want, pl.keys / kStep, int64_t(1024)}));
   pl.chunk = round_up((pl.keys + want - 1) / want, kChunkQuantum);
   pl.splits = int32_t((pl.keys + pl.chunk - 1) / pl.chunk);
   const int64_t rows = batch * n * hq;
@@ -364,10 +392,10 @@ hipError_t launch_attn_decode(const DecodeArgs& a, const DecodePlan& pl, hipStre
   const dim3 grid(uint32_t(pl.splits), uint32_t(pl.units));
   if (a.d == 128) {
     hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(uint32_t(rows)), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(uint32_t((rows + 3) / 4)), dim3(256), 0, stream, p, rows);
   } else {
     hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(uint32_t(rows)), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(uint32_t((rows + 3) / 4)), dim3(256), 0, stream, p, rows);
   }
   return hipGetLastError();
 }

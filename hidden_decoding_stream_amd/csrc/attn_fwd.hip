@@ -27,14 +27,17 @@
 //   Row max / row sum are then lane-local plus one exchange with lane l^32.
 //   The probabilities feed O^T = V^T P^T straight from the accumulator
 //   registers: K rows are read in a permuted order (sigma below) such that
-//   lane half h holds keys 16h .. 16h+15 of each 32-key block, and V is stored
-//   transposed in LDS with its columns permuted in 4-key groups to the order
-//   those registers hold them, so every A-operand read is one contiguous
-//   16-byte load.
-// * Memory. Global loads are buffer loads: rows past the end of a sequence
-//   use an out-of-range offset and read as zeros, with no branch. LDS rows are
-//   padded so that all operand reads are free of bank conflicts and use one
-//   base register plus immediate offsets.
+//   lane half h holds keys 16h .. 16h+15 of each 32-key block. V stays
+//   row-major in LDS; its A operand (V^T) is gathered with the gfx950
+//   transposed LDS read ds_read_b64_tr_b16, addressed so that each lane
+//   receives exactly the keys its P^T registers hold.
+// * Memory. K and V tiles go from HBM to LDS by buffer->LDS DMA loads (no
+//   staging registers, no LDS write instructions), double-buffered with one
+//   barrier per tile. Rows past the end of a sequence use an out-of-range
+//   offset and read as zeros, with no branch. LDS rows are padded so that all
+//   operand reads are free of bank conflicts.
+// * Occupancy. Each wave owns 32 queries; two 4-wave work groups share a CU,
+//   so one wave's softmax overlaps the other's matrix-core work.
 // * Online softmax in base 2 with lazy rescaling: the running reference max m
 //   is raised only when a tile's max exceeds it by more than 2^8; until then
 //   exp2(s - m) <= 256 and no O rescale is needed. The result is the same
@@ -56,10 +59,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
+// Query blocks of 32 per wave and work groups per CU (occupancy hint).
+#ifndef SFA_FWD_QB
+#define SFA_FWD_QB 1
+#endif
+#ifndef SFA_FWD_OCC
+#define SFA_FWD_OCC 2
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BN = 64;                    // keys per tile
-constexpr int VSTR = BN + 8;              // padded row (elements) of the transposed V tile
 constexpr float kRescaleLog2 = 8.0f;      // lazy-rescale threshold (log2 units)
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -85,8 +95,6 @@ struct FwdParams {
   uint32_t kv_bytes;
 };
 
-constexpr int KSTR_PAD = 8;               // K row padding (elements)
-
 // Key group (4 keys) that MFMA row group m>>2 reads from the K tile. After
 // S^T = K Q^T, accumulator register 4g+r of lane half h holds C row
 // 8g + 4h + r, i.e. key 4*kSigmaG[2g+h] + r: keys 16h .. 16h+15 of the block.
@@ -99,17 +107,11 @@ __device__ __forceinline__ int sigma(int m) {
 // Offset (within a 32-key block) of the 4 keys held in registers 4g..4g+3 by
 // lane half h: 16h + 4*(((g&1)*2 + (g>>1)) ^ h).
 __device__ __forceinline__ int reg_key_offset(int g, int h) { return 16 * h + 4 * ((((g & 1) * 2 + (g >> 1))) ^ h); }
-// Column group (within a 32-key block) of the transposed V tile that stores
-// key group kg, so that lane half h reading columns 16h + 8j2 .. +8 gets the
-// keys of registers 8j2 .. 8j2+7.
-__device__ __forceinline__ int v_col_group(int kg) {
-  constexpr uint32_t kKg2Pc = 0x57463120u;  // kg 0..7 -> 0 2 1 3 6 4 7 5 (nibbles, lowest first)
-  return int((kKg2Pc >> (4 * kg)) & 7u);
-}
-
 __device__ __forceinline__ float wave_max_pair(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Offset that makes a buffer load return zeros (>= every num_records used).
 constexpr uint32_t kOobOffset = 0x80000000u;
@@ -121,20 +123,37 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes bytes [16 i, 16 i + 16) after `dst` (one contiguous KiB per wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, u16* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+
+// Tile layouts in LDS (elements, bf16):
+//  K: BN rows of D + 8 (one 16-byte pad slot per row): MFMA A-operand reads of
+//     16 rows hit 16 distinct bank groups.
+//  V: BN rows of D + 32 (four pad slots): a transposed read touches 4
+//     consecutive rows x 64 bytes per half wave, and a 320-byte (D=128) or
+//     192-byte (D=64) row stride puts them in 4 distinct 64-byte bank quarters.
+template <int D> struct Tile {
+  static constexpr int KROW = D + 8, VROW = D + 32;
+  static constexpr int KSLOTS = KROW / 8, VSLOTS = VROW / 8;   // 16-byte slots per row
+  static constexpr int KI = BN * KSLOTS / 64, VI = BN * VSLOTS / 64;  // 1 KiB DMA chunks per tile
+  static constexpr int KELEMS = BN * KROW, VELEMS = BN * VROW;
+  static_assert(BN * KSLOTS % 64 == 0 && BN * VSLOTS % 64 == 0, "tile must be whole KiB chunks");
+};
 
 template <int D, int QB>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, SFA_FWD_OCC) void attn_fwd_kernel(FwdParams p) {
+  using TL = Tile<D>;
   constexpr int KD = D / 16;              // 16-wide d steps of Q K^T
   constexpr int DB = D / 32;              // 32-row d blocks of O^T
   constexpr int PSW = 32 * QB;            // query positions per wave
-  constexpr int KCH = D / 8;              // 16-byte chunks per K/V row
-  constexpr int KSTR = D + KSTR_PAD;      // K tile row stride (elements)
-  constexpr int NLD = BN * KCH / kThreads;  // 16-byte loads per thread per tile (K, and V)
-  constexpr int KPT = NLD;                // keys per thread in the V transpose
-  static_assert(NLD == 2 || NLD == 4, "tile shape");
+  constexpr int NKW = (TL::KI + kWaves - 1) / kWaves;   // DMA chunks per wave (K)
+  constexpr int NVW = (TL::VI + kWaves - 1) / kWaves;   // DMA chunks per wave (V)
 
-  __shared__ __attribute__((aligned(16))) u16 ks[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) u16 vts[2][D * VSTR];
+  __shared__ __attribute__((aligned(16))) u16 ks[2][TL::KELEMS];
+  __shared__ __attribute__((aligned(16))) u16 vs[2][TL::VELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -180,50 +199,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- tile staging: global -> registers -> LDS ----
-  // K: thread loads chunk (c % KCH) of row c / KCH, c = tid + j*256.
-  // V: thread loads chunk dg of keys kg*KPT .. +KPT and writes them transposed.
-  const int dg = tid % KCH, kg = tid / KCH;
-  uint4 kreg[NLD], vreg[NLD];
-  auto load_tile = [&](int kt) {
+  // ---- tile staging: global -> LDS by DMA ----
+  // Slot s of a tile (16 bytes at element 8 s) is row s / SLOTS, chunk s % SLOTS;
+  // chunks past the row's data are padding and read zeros (out-of-range offset).
+  int krow[NKW], kch[NKW], vrow[NVW], vch[NVW];
+#pragma unroll
+  for (int j = 0; j < NKW; ++j) {
+    const int s = (wave + j * kWaves) * 64 + lane;
+    krow[j] = s / TL::KSLOTS;
+    kch[j] = s % TL::KSLOTS;
+  }
+#pragma unroll
+  for (int j = 0; j < NVW; ++j) {
+    const int s = (wave + j * kWaves) * 64 + lane;
+    vrow[j] = s / TL::VSLOTS;
+    vch[j] = s % TL::VSLOTS;
+  }
+  auto load_tile = [&](int kt, int buf) {
     const int k0 = kt * BN;
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int c = tid + j * kThreads;
-      const int vk = k0 + c / KCH;
-      const uint32_t off = vk < p.Lv ? uint32_t(base_row + vk * p.pstride) * kv_pos_bytes + kv_head_bytes + (c % KCH) * 16
-                                     : kOobOffset;
-      kreg[j] = bload16(krs, off);
+    for (int j = 0; j < NKW; ++j) {
+      const int ci = wave + j * kWaves;
+      if (ci < TL::KI) {
+        const int vk = k0 + krow[j];
+        const bool ok = vk < p.Lv && kch[j] < D / 8;
+        const uint32_t off = ok ? uint32_t(base_row + vk * p.pstride) * kv_pos_bytes + kv_head_bytes + kch[j] * 16
+                                : kOobOffset;
+        dma16(krs, &ks[buf][ci * 512], off);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int vk = k0 + kg * KPT + j;
-      const uint32_t off = vk < p.Lv ? uint32_t(base_row + vk * p.pstride) * kv_pos_bytes + kv_head_bytes + dg * 16
-                                     : kOobOffset;
-      vreg[j] = bload16(vrs, off);
-    }
-  };
-  // Column of the transposed V tile where this thread's first key goes.
-  const int vkey0 = kg * KPT;
-  const int vcol = (vkey0 & ~31) + 4 * v_col_group((vkey0 & 31) >> 2) + (vkey0 & 3);
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int c = tid + j * kThreads;
-      *reinterpret_cast<uint4*>(&ks[buf][(c / KCH) * KSTR + (c % KCH) * 8]) = kreg[j];
-    }
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(vreg);  // w[j*4 + e/2]: key j, d pair e/2
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u16* dst = &vts[buf][(dg * 8 + e) * VSTR + vcol];
-      const int sh = (e & 1) * 16;
-      if constexpr (KPT == 4) {
-        const uint32_t a0 = (w[0 * 4 + e / 2] >> sh) & 0xffffu, a1 = (w[1 * 4 + e / 2] >> sh) & 0xffffu;
-        const uint32_t a2 = (w[2 * 4 + e / 2] >> sh) & 0xffffu, a3 = (w[3 * 4 + e / 2] >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-      } else {
-        const uint32_t a0 = (w[0 * 4 + e / 2] >> sh) & 0xffffu, a1 = (w[1 * 4 + e / 2] >> sh) & 0xffffu;
-        *reinterpret_cast<uint32_t*>(dst) = a0 | (a1 << 16);
+    for (int j = 0; j < NVW; ++j) {
+      const int ci = wave + j * kWaves;
+      if (ci < TL::VI) {
+        const int vk = k0 + vrow[j];
+        const bool ok = vk < p.Lv && vch[j] < D / 8;
+        const uint32_t off = ok ? uint32_t(base_row + vk * p.pstride) * kv_pos_bytes + kv_head_bytes + vch[j] * 16
+                                : kOobOffset;
+        dma16(vrs, &vs[buf][ci * 512], off);
       }
     }
   };
@@ -238,16 +251,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db) oacc[qi][db] = f32x16{};
   }
 
-  const int krow0 = sigma(l32);           // K row (within a 32-key block) this lane reads
+  // K row (within a 32-key block) this lane reads for the S^T A operand.
+  const int krow0 = sigma(l32);
+  // Transposed V reads: lane i of 16-lane group G gathers d = 16*(G%2) + i and
+  // sources row base + i/4 at column 4*(i%4) for its group's 4 keys. The 4-key
+  // group of registers (2*j2 + t) of lane half h starts at key
+  // 16h + 4*((2t + j2) ^ h); its offset from the h = 0 case is 20 rows when
+  // 2t + j2 is even and 12 rows when odd.
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vh = grp >> 1;
+  const int vbase = (gi >> 2) * TL::VROW + 16 * (grp & 1) + 4 * (gi & 3);
+  const int vbase_even = vbase + vh * 20 * TL::VROW;
+  const int vbase_odd = vbase + vh * 12 * TL::VROW;
   const bool wave_live = q0 < p.Lv;
 
-  load_tile(kt_begin);
-  store_tile(0);
+  load_tile(kt_begin, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
-    if (kt + 1 < kt_end) load_tile(kt + 1);
+    if (kt + 1 < kt_end) load_tile(kt + 1, buf ^ 1);
 
     // Wave-uniform tile class: `live` if any of the wave's queries has an
     // allowed key in the tile, `full` if every (query, key) pair is allowed.
@@ -259,16 +283,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
       // ---- S^T = K Q^T for two 32-key blocks ----
       f32x16 sacc[QB][2];
 #pragma unroll
-      for (int qi = 0; qi < QB; ++qi) sacc[qi][0] = sacc[qi][1] = f32x16{};
-#pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const u16* kr = &ks[buf][(kb * 32 + krow0) * KSTR + 8 * hh];
+        const u16* kr = &ks[buf][(kb * 32 + krow0) * TL::KROW + 8 * hh];
+        bf16x8 a[KD];
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
+        for (int kk = 0; kk < KD; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
 #pragma unroll
-          for (int qi = 0; qi < QB; ++qi)
-            sacc[qi][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qi][kk], sacc[qi][kb], 0, 0, 0);
+        for (int qi = 0; qi < QB; ++qi) {
+          sacc[qi][kb] = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < KD; ++kk)
+            sacc[qi][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qf[qi][kk], sacc[qi][kb], 0, 0, 0);
         }
       }
       if (!full) {
@@ -325,22 +350,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
         lsum[qi] += ls;
       }
 
-      // ---- O^T += V^T P^T ----
-      const u16* vr = &vts[buf][l32 * VSTR + 16 * hh];
+      // ---- O^T += V^T P^T, V^T gathered by transposed LDS reads ----
+      const u16* vt = &vs[buf][0];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) {
+        bf16x8 a[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j2 = 0; j2 < 2; ++j2) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + db * 32 * VSTR + kb * 32 + 8 * j2);
+            s16x4 x[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const int c = 2 * tt + j2;
+              const int base = (c & 1) ? vbase_odd : vbase_even;
+              const int off = base + (kb * 32 + 4 * c) * TL::VROW + db * 32;
+              x[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vt + off));
+            }
+            __builtin_memcpy(&a[kb][j2], x, 16);
+          }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j2 = 0; j2 < 2; ++j2)
 #pragma unroll
             for (int qi = 0; qi < QB; ++qi)
-              oacc[qi][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qi][kb][j2], oacc[qi][db], 0, 0, 0);
-          }
+              oacc[qi][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb][j2], pf[qi][kb][j2], oacc[qi][db], 0, 0, 0);
+      }
     }
 
-    if (kt + 1 < kt_end) store_tile(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -392,7 +431,7 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   // A window at least as long as the sequence is full causal attention.
   p.window = (a.mode == 2 && a.window < S) ? int32_t(a.window) : 0;
   p.c = a.scale * kLog2e;
-  constexpr int QB = 2;
+  constexpr int QB = SFA_FWD_QB;
   const int PS = (kWaves / p.HG) * 32 * QB;
   p.nqb = (p.Lv + PS - 1) / PS;
   const int64_t total = int64_t(a.batch) * p.nseq * p.hkv * p.nqb * p.hgroups;

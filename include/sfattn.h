@@ -126,7 +126,7 @@ size_t sf_attn_decode_workspace_bytes(int64_t batch, int32_t n, int64_t T, int32
  *   workspace : device scratch of at least sf_attn_decode_workspace_bytes(...)
  *               bytes, 16-byte aligned. Its contents on entry do not matter.
  *   num_splits: how many pieces each key range is cut into (0 = chosen by the
- *               library from the problem size). The result does not depend on
+ *               library from the problem size; at most 1024 are used). The result does not depend on
  *               it beyond float rounding.
  * Supported: d in {64, 128}; hq % hkv == 0; n*G <= 16 query rows per key/value
  * head under the cross masks (G = hq/hkv), G <= 16 under SF_INTRA; 16-byte
