@@ -48,7 +48,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode-sweep", action="store_true", help="skip the decode bandwidth sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters), then exit")
     return ap.parse_args()
@@ -203,7 +203,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "attn_fwd_kernel<128,2> cross_full 32k",
+            "kernel": "attn_fwd_kernel<128, 1> (cross_full) 32k",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -59,15 +59,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-// Query blocks of 32 per wave and work groups per CU (occupancy hint).
-#ifndef SFA_FWD_QB
-#define SFA_FWD_QB 1
-#endif
-#ifndef SFA_FWD_OCC
-#define SFA_FWD_OCC 2
-#endif
-
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BN = 64;                    // keys per tile
 constexpr float kRescaleLog2 = 8.0f;      // lazy-rescale threshold (log2 units)
@@ -107,7 +99,17 @@ __device__ __forceinline__ int sigma(int m) {
 // Offset (within a 32-key block) of the 4 keys held in registers 4g..4g+3 by
 // lane half h: 16h + 4*(((g&1)*2 + (g>>1)) ^ h).
 __device__ __forceinline__ int reg_key_offset(int g, int h) { return 16 * h + 4 * ((((g & 1) * 2 + (g >> 1))) ^ h); }
-__device__ __forceinline__ float wave_max_pair(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// Combine a value with the one held by lane l^32 (the other half of the
+// wave): v_permlane32_swap exchanges the two halves without going through LDS,
+// and the max / sum of the two results is the same whichever half lands where.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -130,33 +132,60 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, u16* dst, uint32
 }
 
 // Tile layouts in LDS (elements, bf16):
-//  K: BN rows of D + 8 (one 16-byte pad slot per row): MFMA A-operand reads of
-//     16 rows hit 16 distinct bank groups.
-//  V: BN rows of D + 32 (four pad slots): a transposed read touches 4
-//     consecutive rows x 64 bytes per half wave, and a 320-byte (D=128) or
-//     192-byte (D=64) row stride puts them in 4 distinct 64-byte bank quarters.
+//  K: BN rows of D + 16 (two 16-byte pad slots per row). A 16-byte operand
+//     read is served 8 lanes from each half wave per cycle (lanes i and i+32
+//     together); with this stride those 16 reads hit 16 distinct bank groups.
+//  V: BN rows of D, unpadded; the 64-byte pieces of a row (32 d values) are
+//     stored XOR-swizzled by row (position db ^ (row & 3) for D=128,
+//     db ^ ((row >> 1) & 1) for D=64) so that a transposed read, which takes
+//     64 bytes from each of 4 consecutive rows per half wave, hits 4 distinct
+//     64-byte bank quarters.
 template <int D> struct Tile {
-  static constexpr int KROW = D + 8, VROW = D + 32;
-  static constexpr int KSLOTS = KROW / 8, VSLOTS = VROW / 8;   // 16-byte slots per row
+  static constexpr int KROW = D + 16;
+  static constexpr int KSLOTS = KROW / 8, VSLOTS = D / 8;      // 16-byte slots per row
   static constexpr int KI = BN * KSLOTS / 64, VI = BN * VSLOTS / 64;  // 1 KiB DMA chunks per tile
-  static constexpr int KELEMS = BN * KROW, VELEMS = BN * VROW;
+  static constexpr int KELEMS = BN * KROW, VELEMS = BN * D;
   static_assert(BN * KSLOTS % 64 == 0 && BN * VSLOTS % 64 == 0, "tile must be whole KiB chunks");
 };
+template <int D> __device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) return row & 3;
+  else return (row >> 1) & 1;
+}
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads, SFA_FWD_OCC) void attn_fwd_kernel(FwdParams p) {
+// Work group: 8 waves, two per SIMD, each owning 32 queries. K and V tiles
+// of 64 keys go through a 3-stage LDS ring: while tile t is computed, the DMA
+// of tile t+2 is in flight (its chunks are issued in small groups between the
+// phases of tile t, so the load queue never stalls a wave for long), and one
+// barrier per tile publishes tile t+1. Per tile a wave runs
+//   S^T = K Q^T (16 MFMAs) -> mask (edge tiles) -> row max -> lazy rescale
+//   -> P = exp2(S - m), row sums, bf16 -> O^T += V^T P^T (16 MFMAs),
+// with the V^T fragments gathered before the softmax so they arrive while it
+// runs. The two waves of a SIMD come from the same work group but drift
+// apart within a tile, so one's softmax overlaps the other's MFMAs.
+// MODE is the mask (0 intra, 1 causal over the expanded sequence, 2 causal
+// and windowed), fixed at compile time so that the masks and the position
+// arithmetic of the other modes fold away.
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   using TL = Tile<D>;
   constexpr int KD = D / 16;              // 16-wide d steps of Q K^T
   constexpr int DB = D / 32;              // 32-row d blocks of O^T
-  constexpr int PSW = 32 * QB;            // query positions per wave
-  constexpr int NKW = (TL::KI + kWaves - 1) / kWaves;   // DMA chunks per wave (K)
-  constexpr int NVW = (TL::VI + kWaves - 1) / kWaves;   // DMA chunks per wave (V)
+  constexpr int NCH = TL::KI + TL::VI;    // DMA chunks per tile (K then V)
+  constexpr int NCW = (NCH + kWaves - 1) / kWaves;   // chunks per wave (max)
+  constexpr int kMinChunks = NCH / kWaves;           // chunks per wave (min)
+  constexpr int ST = 3;                   // LDS stages
 
-  __shared__ __attribute__((aligned(16))) u16 ks[2][TL::KELEMS];
-  __shared__ __attribute__((aligned(16))) u16 vs[2][TL::VELEMS];
+  __shared__ __attribute__((aligned(16))) u16 ks[ST][TL::KELEMS];
+  __shared__ __attribute__((aligned(16))) u16 vs[ST][TL::VELEMS];
+
+  const int pstride = MODE == 0 ? p.pstride : 1;
+  const int window = MODE == 2 ? p.window : 0;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // wave index as a wave-uniform (scalar) value, so that per-wave decisions
+  // below are scalar branches rather than exec-mask branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
 
   // ---- work item ----
@@ -172,11 +201,11 @@ __global__ __launch_bounds__(kThreads, SFA_FWD_OCC) void attn_fwd_kernel(FwdPara
   const int sq = bs % p.nseq;
   const int b = bs / p.nseq;
   const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
-  const int PS = (kWaves / p.HG) * PSW;
+  const int PS = (kWaves / p.HG) * 32;
   const int wg_q0 = qb * PS;
-  const int q0 = wg_q0 + (wave / p.HG) * PSW;
+  const int q0 = wg_q0 + (wave / p.HG) * 32;
   const int wg_qlast = min(wg_q0 + PS, p.Lv) - 1;
-  const int kt_begin = p.window > 0 ? max(0, wg_q0 - p.window + 1) / BN : 0;
+  const int kt_begin = window > 0 ? max(0, wg_q0 - window + 1) / BN : 0;
   const int kt_end = wg_qlast / BN + 1;
 
   const int base_row = b * p.S + sq;       // position of virtual index 0
@@ -186,226 +215,238 @@ __global__ __launch_bounds__(kThreads, SFA_FWD_OCC) void attn_fwd_kernel(FwdPara
   const uint32_t kv_pos_bytes = uint32_t(p.hkv) * D * 2;      // bytes between positions in K/V
   const uint32_t kv_head_bytes = uint32_t(kvh) * D * 2;
 
-  // ---- Q^T fragments (B operand): lane holds Q[q0+qi*32+l32][kk*16 + 8*hh .. +8] ----
-  bf16x8 qf[QB][KD];
-#pragma unroll
-  for (int qi = 0; qi < QB; ++qi) {
-    const int vq = q0 + qi * 32 + l32;
-    const uint32_t off = vq < p.Lv ? ((uint32_t(base_row + vq * p.pstride) * p.hq + h) * D + 8 * hh) * 2 : kOobOffset;
+  // ---- Q^T fragments (B operand): lane holds Q[q0+l32][kk*16 + 8*hh .. +8] ----
+  bf16x8 qf[KD];
+  {
+    const int vq = q0 + l32;
+    const uint32_t off = ((uint32_t(base_row + vq * pstride) * p.hq + h) * D + 8 * hh) * 2 +
+                         (vq < p.Lv ? 0u : kOobOffset);
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
       const uint4 x = bload16(qrs, off + kk * 32);
-      __builtin_memcpy(&qf[qi][kk], &x, 16);
+      __builtin_memcpy(&qf[kk], &x, 16);
     }
   }
 
   // ---- tile staging: global -> LDS by DMA ----
-  // Slot s of a tile (16 bytes at element 8 s) is row s / SLOTS, chunk s % SLOTS;
-  // chunks past the row's data are padding and read zeros (out-of-range offset).
-  int krow[NKW], kch[NKW], vrow[NVW], vch[NVW];
+  // Chunk c < KI is K chunk c (slot sl = 64 c + lane of the padded K tile:
+  // row sl / KSLOTS, data chunk sl % KSLOTS, padding reads zeros); chunk
+  // c >= KI is V chunk c - KI (row sl / VSLOTS, stored 16-byte unit
+  // sl % VSLOTS, holding a data chunk of the swizzled 64-byte piece).
+  // Wave w moves chunks w, w + 8, ... The byte offset of a chunk is a
+  // tile-independent part (kept per chunk; padding slots carry the
+  // out-of-range offset for good) plus a scalar tile base.
+  uint32_t coff[NCW];
 #pragma unroll
-  for (int j = 0; j < NKW; ++j) {
-    const int s = (wave + j * kWaves) * 64 + lane;
-    krow[j] = s / TL::KSLOTS;
-    kch[j] = s % TL::KSLOTS;
-  }
-#pragma unroll
-  for (int j = 0; j < NVW; ++j) {
-    const int s = (wave + j * kWaves) * 64 + lane;
-    vrow[j] = s / TL::VSLOTS;
-    vch[j] = s % TL::VSLOTS;
-  }
-  auto load_tile = [&](int kt, int buf) {
-    const int k0 = kt * BN;
-#pragma unroll
-    for (int j = 0; j < NKW; ++j) {
-      const int ci = wave + j * kWaves;
-      if (ci < TL::KI) {
-        const int vk = k0 + krow[j];
-        const bool ok = vk < p.Lv && kch[j] < D / 8;
-        const uint32_t off = ok ? uint32_t(base_row + vk * p.pstride) * kv_pos_bytes + kv_head_bytes + kch[j] * 16
-                                : kOobOffset;
-        dma16(krs, &ks[buf][ci * 512], off);
-      }
+  for (int j = 0; j < NCW; ++j) {
+    const int c = wave + j * kWaves;
+    int row = 0, ch = 0;
+    bool pad = false;
+    if (c < TL::KI) {
+      const int sl = c * 64 + lane;
+      row = sl / TL::KSLOTS;
+      ch = sl % TL::KSLOTS;
+      pad = ch >= D / 8;
+    } else {
+      const int sl = (c - TL::KI) * 64 + lane;
+      row = sl / TL::VSLOTS;
+      const int u = sl % TL::VSLOTS;
+      ch = (((u >> 2) ^ vswz<D>(row)) << 2) | (u & 3);
     }
+    coff[j] = pad ? kOobOffset : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
+  }
+  auto issue_chunks = [&](int kt, int j0, int j1) {
+    const int st = kt % ST;
+    const uint32_t tbase = uint32_t(base_row + kt * BN * pstride) * kv_pos_bytes;
+    const bool ragged = (kt + 1) * BN > p.Lv;   // last tile of a sequence: rows past the end read zeros
 #pragma unroll
-    for (int j = 0; j < NVW; ++j) {
-      const int ci = wave + j * kWaves;
-      if (ci < TL::VI) {
-        const int vk = k0 + vrow[j];
-        const bool ok = vk < p.Lv && vch[j] < D / 8;
-        const uint32_t off = ok ? uint32_t(base_row + vk * p.pstride) * kv_pos_bytes + kv_head_bytes + vch[j] * 16
-                                : kOobOffset;
-        dma16(vrs, &vs[buf][ci * 512], off);
+    for (int j = j0; j < j1; ++j) {
+      const int c = wave + j * kWaves;
+      if (c < NCH) {
+        uint32_t off = tbase + coff[j];
+        if (ragged) {
+          const int row = c < TL::KI ? (c * 64 + lane) / TL::KSLOTS : ((c - TL::KI) * 64 + lane) / TL::VSLOTS;
+          off += kt * BN + row < p.Lv ? 0u : kOobOffset;
+        }
+        if (c < TL::KI) dma16(krs, &ks[st][c * 512], off);
+        else dma16(vrs, &vs[st][(c - TL::KI) * 512], off);
       }
     }
   };
 
-  float m[QB], lsum[QB];
-  f32x16 oacc[QB][DB];
-#pragma unroll
-  for (int qi = 0; qi < QB; ++qi) {
-    m[qi] = -INFINITY;
-    lsum[qi] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[qi][db] = f32x16{};
-  }
-
   // K row (within a 32-key block) this lane reads for the S^T A operand.
   const int krow0 = sigma(l32);
   // Transposed V reads: lane i of 16-lane group G gathers d = 16*(G%2) + i and
-  // sources row base + i/4 at column 4*(i%4) for its group's 4 keys. The 4-key
-  // group of registers (2*j2 + t) of lane half h starts at key
-  // 16h + 4*((2t + j2) ^ h); its offset from the h = 0 case is 20 rows when
-  // 2t + j2 is even and 12 rows when odd.
+  // sources row base + i/4 at column 4*(i%4) of its 64-byte piece, for its
+  // group's 4 keys. The 4-key group of registers (2*j2 + t) of lane half h
+  // starts at key 16h + 4*((2t + j2) ^ h); its offset from the h = 0 case is
+  // 20 rows when 2t + j2 is even and 12 rows when odd. The swizzle of the
+  // piece depends only on (row & 3) = i/4 (D=128) or on bit 1 of it (D=64).
   const int grp = lane >> 4, gi = lane & 15;
   const int vh = grp >> 1;
-  const int vbase = (gi >> 2) * TL::VROW + 16 * (grp & 1) + 4 * (gi & 3);
-  const int vbase_even = vbase + vh * 20 * TL::VROW;
-  const int vbase_odd = vbase + vh * 12 * TL::VROW;
+  const int vsw = D == 128 ? (gi >> 2) : ((gi >> 3) & 1);
+  const int vbase = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3);
+  const int vbase_even = vbase + vh * 20 * D;
+  const int vbase_odd = vbase + vh * 12 * D;
+  const int qhi = min(q0 + 32, p.Lv) - 1;
   const bool wave_live = q0 < p.Lv;
 
-  load_tile(kt_begin, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+
+  // ---- prologue: tiles kt_begin and kt_begin + 1 in flight, wait for the first ----
+  issue_chunks(kt_begin, 0, NCW);
+  if (kt_begin + 1 < kt_end) {
+    issue_chunks(kt_begin + 1, 0, NCW);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kMinChunks) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    if (kt + 1 < kt_end) load_tile(kt + 1, buf ^ 1);
-
-    // Wave-uniform tile class: `live` if any of the wave's queries has an
-    // allowed key in the tile, `full` if every (query, key) pair is allowed.
+    const int st = kt % ST;
+    const int pre = kt + 2;                    // tile whose DMA is issued during this one
+    const bool do_pre = pre < kt_end;
     const int k0 = kt * BN;
-    const int qlo = q0, qhi = min(q0 + PSW, p.Lv) - 1;
-    const bool live = wave_live && k0 <= qhi && !(p.window > 0 && qlo - (k0 + BN - 1) >= p.window);
-    const bool full = (k0 + BN - 1 <= qlo) && (p.window == 0 || qhi - k0 < p.window);
+    const bool live = wave_live && k0 <= qhi && !(window > 0 && q0 - (k0 + BN - 1) >= window);
+    if (do_pre) issue_chunks(pre, 0, NCW);
     if (live) {
       // ---- S^T = K Q^T for two 32-key blocks ----
-      f32x16 sacc[QB][2];
+      f32x16 sacc[2];
+      const u16* kr0 = &ks[st][krow0 * TL::KROW + 8 * hh];
+      bf16x8 ka[2][KD];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) ka[kb][kk] = *reinterpret_cast<const bf16x8*>(kr0 + kb * 32 * TL::KROW + kk * 16);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const u16* kr = &ks[buf][(kb * 32 + krow0) * TL::KROW + 8 * hh];
-        bf16x8 a[KD];
+        sacc[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi) {
-          sacc[qi][kb] = f32x16{};
-#pragma unroll
-          for (int kk = 0; kk < KD; ++kk)
-            sacc[qi][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qf[qi][kk], sacc[qi][kb], 0, 0, 0);
-        }
+        for (int kk = 0; kk < KD; ++kk)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][kk], qf[kk], sacc[kb], 0, 0, 0);
       }
+      const bool full = (k0 + BN - 1 <= q0) && (window == 0 || qhi - k0 < window);
       if (!full) {
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi) {
-          const int vq = q0 + qi * 32 + l32;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kb * 32 + reg_key_offset(g, hh) + r;
-                const bool ok = key <= vq && (p.window == 0 || vq - key < p.window);
-                sacc[qi][kb][4 * g + r] = ok ? sacc[qi][kb][4 * g + r] : -INFINITY;
-              }
-        }
-      }
-
-      // ---- online softmax (base 2, lazy rescale) ----
-      bf16x8 pf[QB][2][2];
-#pragma unroll
-      for (int qi = 0; qi < QB; ++qi) {
-        float mx = -INFINITY;
+        const int vq = q0 + l32;
+        const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[qi][kb][i]);
-        mx = wave_max_pair(mx);
-        const float cand = mx * p.c;
-        const bool need = cand > m[qi] + kRescaleLog2;
-        if (__any(need)) {
-          const float alpha = need ? __builtin_amdgcn_exp2f(m[qi] - cand) : 1.f;
-          m[qi] = need ? cand : m[qi];
-          lsum[qi] *= alpha;
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[qi][db] *= alpha;
-        }
-        const float mu = m[qi] == -INFINITY ? 0.f : m[qi];
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2) {
-            bf16x8 pv;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float e = __builtin_amdgcn_exp2f(fmaf(sacc[qi][kb][j2 * 8 + i], p.c, -mu));
-              ls += e;
-              pv[i] = (__bf16)e;
+            for (int r = 0; r < 4; ++r) {
+              const int key = k0 + kb * 32 + reg_key_offset(g, hh) + r;
+              // 0 <= vq - key < lim, one unsigned compare (lim 2^31: causal only)
+              const bool ok = uint32_t(vq - key) < lim;
+              sacc[kb][4 * g + r] = ok ? sacc[kb][4 * g + r] : -INFINITY;
             }
-            pf[qi][kb][j2] = pv;
-          }
-        lsum[qi] += ls;
       }
 
-      // ---- O^T += V^T P^T, V^T gathered by transposed LDS reads ----
-      const u16* vt = &vs[buf][0];
+      // ---- V^T fragments, gathered by transposed LDS reads; requested
+      // before the softmax so they arrive while it runs ----
+      const u16* vt = &vs[st][0];
+      bf16x8 va[DB][2][2];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        bf16x8 a[2][2];
+        const int col = ((db ^ vsw) - db) * 32;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j2 = 0; j2 < 2; ++j2) {
             s16x4 x[2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-              const int c = 2 * tt + j2;
+            for (int tr = 0; tr < 2; ++tr) {
+              const int c = 2 * tr + j2;
               const int base = (c & 1) ? vbase_odd : vbase_even;
-              const int off = base + (kb * 32 + 4 * c) * TL::VROW + db * 32;
-              x[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vt + off));
+              const int off = base + col + (kb * 32 + 4 * c) * D + db * 32;
+              x[tr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vt + off));
             }
-            __builtin_memcpy(&a[kb][j2], x, 16);
+            __builtin_memcpy(&va[db][kb][j2], x, 16);
           }
+      }
+
+      // ---- online softmax (base 2, lazy rescale) ----
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      const float cand = pair_max(mx) * p.c;
+      const bool need = cand > m + kRescaleLog2;
+      float o_alpha = 1.f;
+      const bool o_rescale = __any(need);
+      if (o_rescale) {
+        o_alpha = need ? __builtin_amdgcn_exp2f(m - cand) : 1.f;
+        m = need ? cand : m;
+        lsum *= o_alpha;
+      }
+      const float mu = m == -INFINITY ? 0.f : m;
+      bf16x8 pf[2][2];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          bf16x8 pv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j2 * 8 + i], p.c, -mu));
+            ls += e;
+            pv[i] = (__bf16)e;
+          }
+          pf[kb][j2] = pv;
+        }
+      lsum += ls;
+
+      // ---- O^T += V^T P^T (a raised reference max rescales O first) ----
+      if (o_rescale) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= o_alpha;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j2 = 0; j2 < 2; ++j2)
-#pragma unroll
-            for (int qi = 0; qi < QB; ++qi)
-              oacc[qi][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb][j2], pf[qi][kb][j2], oacc[qi][db], 0, 0, 0);
-      }
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb][j2], pf[kb][j2], oacc[db], 0, 0, 0);
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    if (kt + 1 < kt_end) {
+      // tile kt + 1 must have landed; the chunks of tile kt + 2 may still fly
+      if (do_pre)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kMinChunks) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = O^T / l, bf16; optional natural-log LSE ----
   if (!wave_live) return;
+  const float lt = pair_sum(lsum);
+  const int vq = q0 + l32;
+  if (vq >= p.Lv) return;
+  const float inv = 1.f / lt;
+  const size_t prow = (size_t)(base_row + vq * pstride);
+  u16* orow = p.o + (prow * p.hq + h) * D;
 #pragma unroll
-  for (int qi = 0; qi < QB; ++qi) {
-    const float lt = lsum[qi] + __shfl_xor(lsum[qi], 32);
-    const int vq = q0 + qi * 32 + l32;
-    if (vq >= p.Lv) continue;
-    const float inv = 1.f / lt;
-    const size_t prow = (size_t)(base_row + vq * p.pstride);
-    u16* orow = p.o + (prow * p.hq + h) * D;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int g = 0; g < 4; ++g) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 ov;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 ov;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(oacc[qi][db][4 * g + r] * inv);
-        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hh) = ov;
-      }
-    if (p.lse && hh == 0)
-      p.lse[((size_t)b * p.hq + h) * p.S + (prow - (size_t)b * p.S)] = (m[qi] + log2f(lt)) * kLn2;
-  }
+      for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(oacc[db][4 * g + r] * inv);
+      *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hh) = ov;
+    }
+  if (p.lse && hh == 0)
+    p.lse[((size_t)b * p.hq + h) * p.S + (prow - (size_t)b * p.S)] = (m + log2f(lt)) * kLn2;
 }
 
 }  // namespace
@@ -426,13 +467,13 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.G = a.hq / a.hkv;
-  p.HG = p.G % 4 == 0 ? 4 : (p.G % 2 == 0 ? 2 : 1);
+  p.HG = 1;
+  while (p.HG * 2 <= kWaves && p.G % (p.HG * 2) == 0) p.HG *= 2;
   p.hgroups = p.G / p.HG;
   // A window at least as long as the sequence is full causal attention.
   p.window = (a.mode == 2 && a.window < S) ? int32_t(a.window) : 0;
   p.c = a.scale * kLog2e;
-  constexpr int QB = SFA_FWD_QB;
-  const int PS = (kWaves / p.HG) * 32 * QB;
+  const int PS = (kWaves / p.HG) * 32;
   p.nqb = (p.Lv + PS - 1) / PS;
   const int64_t total = int64_t(a.batch) * p.nseq * p.hkv * p.nqb * p.hgroups;
   p.total = int32_t(total);
@@ -440,10 +481,12 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   p.q_bytes = uint32_t(a.batch * S * a.hq * a.d * 2);
   p.kv_bytes = uint32_t(a.batch * S * a.hkv * a.d * 2);
   const dim3 grid(uint32_t(p.per_xcd) * 8u);
-  if (a.d == 128)
-    hipLaunchKernelGGL((attn_fwd_kernel<128, QB>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<64, QB>), grid, dim3(kThreads), 0, stream, p);
+  using Kernel = void (*)(FwdParams);
+  static constexpr Kernel kKernels[2][3] = {
+      {attn_fwd_kernel<64, 0>, attn_fwd_kernel<64, 1>, attn_fwd_kernel<64, 2>},
+      {attn_fwd_kernel<128, 0>, attn_fwd_kernel<128, 1>, attn_fwd_kernel<128, 2>}};
+  const int kind = intra ? 0 : (p.window > 0 ? 2 : 1);
+  hipLaunchKernelGGL(kKernels[a.d == 128][kind], grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
