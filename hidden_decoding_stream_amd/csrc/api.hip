@@ -171,16 +171,18 @@ sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_c
   if (overlaps(o_new, qe * 2, q_new, qe * 2) || overlaps(o_new, qe * 2, k_cache, ce * 2) ||
       overlaps(o_new, qe * 2, v_cache, ce * 2))
     return fail(SF_ERR_INVALID, "o_new overlaps an input");
-  if (T_max > INT32_MAX / 2 || ce > (int64_t(1) << 40))
-    return fail(SF_ERR_UNSUPPORTED, "cache too large (T_max=%lld)", (long long)T_max);
+  if (ce > (int64_t(1) << 40) || T_max * hkv * d * 2 > INT32_MAX)
+    return fail(SF_ERR_UNSUPPORTED, "cache too large (T_max * hkv * d * 2 = %lld bytes per stream, at most 2^31 - 1)",
+                (long long)(T_max * hkv * d * 2));
   const sfa::DecodePlan plan = sfa::plan_decode(batch, n, T, hq, hkv, d, mode, window, num_splits);
   if (plan.units > 65535)
     return fail(SF_ERR_UNSUPPORTED, "decode supports at most 65535 key ranges (batch*hkv%s = %lld)",
                 mode == SF_INTRA ? "*n" : "", (long long)plan.units);
-  if (!workspace || workspace_bytes < plan.ws_bytes)
+  if ((plan.ws_bytes > 0 && !workspace) || workspace_bytes < plan.ws_bytes)
     return fail(SF_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
                 plan.ws_bytes);
-  if (!aligned(workspace, 16)) return fail(SF_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (plan.ws_bytes > 0 && !aligned(workspace, 16))
+    return fail(SF_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (overlaps(workspace, int64_t(plan.ws_bytes), o_new, qe * 2) ||
       overlaps(workspace, int64_t(plan.ws_bytes), q_new, qe * 2) ||
       overlaps(workspace, int64_t(plan.ws_bytes), k_cache, ce * 2) ||

@@ -18,19 +18,26 @@
 // * A unit is one key range shared by a set of query rows: (batch, kv head)
 //   with its n*G rows under the cross masks, or (batch, kv head, stream) with
 //   its G rows under intra. Each unit's keys are cut into `splits` chunks; a
-//   work group of 4 waves takes one chunk and each wave 32-key steps of it.
-// * Keys of one stream are contiguous 32-key steps (each stream's token range
-//   is padded to a multiple of 32), so a step never straddles two streams.
-// * Scores use v_mfma_f32_16x16x32_bf16 as S^T = K Q^T: the K rows go from HBM
-//   straight into A-operand registers (no LDS), Q^T is held in registers. The
-//   two 16-key blocks of a step read keys {8g+r} and {8g+4+r} (g = lane/16)
-//   so that each lane ends up holding 8 consecutive keys of one query row,
-//   the B-operand layout of O^T = V^T P^T.
-// * V is transposed through a per-wave LDS slab (16-byte global loads,
-//   register transpose, 16-byte LDS reads), prefetched one step ahead.
-// * The 4 waves of a group merge their (max, sum, O) in LDS; the group writes
-//   one fp32 partial per query row and split. A second kernel merges the
-//   splits in a fixed order (deterministic), rescaling by exp2(m_s - M).
+//   work group of 4 waves (one per SIMD) takes one chunk and each wave every
+//   4th 32-key step of it. Keys of one stream are contiguous 32-key steps
+//   (each stream's token range is padded to a multiple of 32), so a step
+//   never straddles two streams.
+// * Memory. A step's K and V rows (32 x 2 x d x 2 bytes) go from HBM to LDS
+//   by buffer->LDS DMA, each wave through its own ring of stages, so no wave
+//   waits for another and no barrier is needed until the end. Every group of
+//   4 lanes fetches one contiguous 64-byte piece of a row (coalesced); the
+//   16-byte chunks of a row are stored XOR-swizzled by key (swk / swv) so
+//   that the operand reads below hit distinct LDS banks. Rows past token T-1
+//   lie outside the buffer range and read as zeros.
+// * Scores use v_mfma_f32_16x16x32_bf16 as S^T = K Q^T with Q^T held in
+//   registers. The two 16-key blocks of a step read keys {8g+r} and
+//   {8g+4+r} (g = lane/16) so that each lane ends up holding 8 consecutive
+//   keys of one query row: the B-operand layout of O^T = V^T P^T. V^T comes
+//   from the row-major V stage by transposed LDS reads (ds_read_b64_tr_b16).
+// * The 4 waves of a group merge their (max, sum, O) in LDS. With one split
+//   the group writes the normalised bf16 output; otherwise it writes one fp32
+//   partial per query row and split, and a second kernel merges the splits in
+//   a fixed order (deterministic), rescaling by exp2(m_s - M).
 #include <math.h>
 
 #include <algorithm>
@@ -43,13 +50,13 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;                 // keys per wave step
 constexpr int kChunkQuantum = kStep * kWaves;
-constexpr int VTS = kStep + 8;            // padded row (elements) of a transposed V slab
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -69,27 +76,54 @@ struct DecParams {
   int32_t splits, chunk, keys;
 };
 
-template <int D>
-struct Smem {
-  union {
-    u16 vt[kWaves][D * VTS];
-    struct {
-      float o[kWaves][16][D];
-      float m[kWaves][16];
-      float l[kWaves][16];
-    } mrg;
-  };
+// One wave's step: 32 rows of K then 32 rows of V, d elements each.
+template <int D> struct Stage {
+  static constexpr int CH = D / 8;              // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;           // rows per 1 KiB DMA instruction
+  static constexpr int NI = kStep / RPI;        // DMA instructions per 32-row tile
+  static constexpr int TILE = kStep * D;        // elements per tile
+  static constexpr int NS = D == 128 ? 2 : 4;   // ring depth (32 KiB per wave either way)
 };
+
+// Chunk swizzles (16-byte chunk index XOR a function of the key's low 4 bits).
+// K is read 16 bytes per lane in the MFMA A layout; LDS serves lanes i and
+// i+32 together, 8 of each per cycle: keys {0-3, 8-11} (+4 or +16) at chunks
+// c and c^2. swk gives those 8 keys distinct values modulo XOR 2, so the 16
+// reads hit 16 distinct bank groups. V is read 8 bytes per lane by the
+// transposed read, 32-byte pieces of keys {0-3, 8-11} (+4, +16) at once; swv
+// puts them in 8 distinct 32-byte bank slots. Both permute the chunks of a
+// 64-byte quad among themselves or move whole quads, so 4 consecutive DMA
+// lanes still read one contiguous 64-byte piece of the row.
+template <int D> __device__ __forceinline__ int swk(int k) {
+  if constexpr (D == 128) return (k & 1) | ((k & 2) << 1) | (k & 8);
+  else return ((k >> 1) & 1) | ((k >> 1) & 4);
+}
+template <int D> __device__ __forceinline__ int swv(int k) {
+  if constexpr (D == 128) return ((k & 3) << 1) | (k & 8);
+  else return (k & 2) | ((k >> 1) & 4);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
+  using SG = Stage<D>;
   constexpr int KC = D / 32;              // 32-wide d steps of the 16x16x32 MFMA
   constexpr int DB = D / 16;              // 16-row d blocks of O^T
-  constexpr int KCH = D / 8;              // 16-byte chunks per row
-  constexpr int VPL = kStep * KCH / 64;   // V chunks (keys) per lane per step
-  __shared__ __attribute__((aligned(16))) Smem<D> sm;
+  constexpr int NS = SG::NS;
+  constexpr int NI = SG::NI;
+  // per wave: NS stages of (K tile, V tile); the merge area aliases the rings
+  struct Merge {
+    float o[kWaves][16][D];
+    float m[kWaves][16];
+    float l[kWaves][16];
+  };
+  constexpr int kRingElems = kWaves * NS * 2 * SG::TILE;
+  static_assert(sizeof(Merge) <= kRingElems * 2, "merge area must fit in the rings");
+  __shared__ __attribute__((aligned(16))) u16 ring[kRingElems];
+  Merge& mrg = *reinterpret_cast<Merge*>(ring);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
@@ -120,35 +154,50 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 
   const size_t stream_stride = (size_t)p.Tmax * p.hkv * D;      // elements between streams
+  const uint32_t trow_b = uint32_t(p.hkv) * D * 2;              // bytes between tokens
+  // Bytes from a stream's (token 0, kv head) to the end of token T-1's rows:
+  // every row t < T lies inside, every row t >= T outside (reads zeros).
+  const uint32_t range_b = uint32_t(p.T) * trow_b - uint32_t(kvh) * D * 2;
   const u16* kbase = p.kc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
   const u16* vbase = p.vc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
-  const int trow = p.hkv * D;                                   // elements between tokens
 
   const int j_begin = split * p.chunk;
   const int j_end = min(p.keys, j_begin + p.chunk);
   const int nsteps = j_end > j_begin ? (j_end - j_begin + kStep - 1) / kStep : 0;
+  const int nu = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;   // steps of this wave
 
-  uint4 kreg[2][KC], vreg[VPL];
-  auto load_step = [&](int st) {
-    const int j0 = j_begin + st * kStep;
-    const int sp = p.intra ? s_unit : j0 / p.kps;
-    const int t0 = p.t_lo + (j0 - (j0 / p.kps) * p.kps);
-    const u16* ks = kbase + (size_t)sp * stream_stride;
-    const u16* vs = vbase + (size_t)sp * stream_stride;
+  // Per-lane DMA offsets within a step (tile row r, stored chunk lane % CH,
+  // fetched chunk XOR the row's swizzle).
+  uint32_t koff[NI], voff[NI];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int t = t0 + 8 * (l16 >> 2) + 4 * kb + (l16 & 3);
+  for (int i = 0; i < NI; ++i) {
+    const int row = i * SG::RPI + lane / SG::CH;
+    const int c = lane % SG::CH;
+    koff[i] = uint32_t(row) * trow_b + uint32_t(c ^ swk<D>(row)) * 16;
+    voff[i] = uint32_t(row) * trow_b + uint32_t(c ^ swv<D>(row)) * 16;
+  }
+  u16* my_ring = ring + wave * NS * 2 * SG::TILE;
+
+  auto step_pos = [&](int u, int& sp, int& t0) {
+    const int j0 = j_begin + (wave + u * kWaves) * kStep;
+    const int ss = j0 / p.kps;
+    sp = p.intra ? s_unit : ss;
+    t0 = p.t_lo + (j0 - ss * p.kps);
+  };
+  auto issue = [&](int u) {
+    int sp, t0;
+    step_pos(u, sp, t0);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + (size_t)sp * stream_stride, range_b);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + (size_t)sp * stream_stride, range_b);
+    const uint32_t sbase = uint32_t(t0) * trow_b;
+    u16* kt = my_ring + (u % NS) * 2 * SG::TILE;
+    u16* vt = kt + SG::TILE;
+    // the step base goes into the per-lane offset: only that offset is
+    // range-checked, which is what turns rows t >= T into zeros
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        kreg[kb][kk] = t < p.T ? *reinterpret_cast<const uint4*>(ks + (size_t)t * trow + kk * 32 + 8 * g)
-                               : make_uint4(0, 0, 0, 0);
-    }
-    const int dg = lane % KCH, kg = lane / KCH;
+    for (int i = 0; i < NI; ++i) dma16(krs, kt + i * 512, koff[i] + sbase);
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int t = t0 + kg * VPL + i;
-      vreg[i] = t < p.T ? *reinterpret_cast<const uint4*>(vs + (size_t)t * trow + dg * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < NI; ++i) dma16(vrs, vt + i * 512, voff[i] + sbase);
   };
 
   float m = -INFINITY, lsum = 0.f;
@@ -156,45 +205,63 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
 
-  u16* vt = sm.vt[wave];
-  int st = wave;
-  if (st < nsteps) load_step(st);
-  for (; st < nsteps; st += kWaves) {
-    const int j0 = j_begin + st * kStep;
-    const int sp = p.intra ? s_unit : j0 / p.kps;
-    const int t0 = p.t_lo + (j0 - (j0 / p.kps) * p.kps);
+  // Q must be in registers before the first DMA is counted against vmcnt.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+    if (u < nu) issue(u);
 
-    // V: registers -> transposed LDS slab vt[d][key]
-    {
-      const int dg = lane % KCH, kg = lane / KCH;
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(vreg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        uint32_t pk[VPL / 2];
-#pragma unroll
-        for (int i = 0; i < VPL / 2; ++i) {
-          const uint32_t a0 = (w[(2 * i) * 4 + e / 2] >> sh) & 0xffffu;
-          const uint32_t a1 = (w[(2 * i + 1) * 4 + e / 2] >> sh) & 0xffffu;
-          pk[i] = a0 | (a1 << 16);
-        }
-        u16* dst = vt + (dg * 8 + e) * VTS + kg * VPL;
-        if constexpr (VPL == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
-      }
+  for (int u = 0; u < nu; ++u) {
+    // wait for step u: the stages issued after it may stay in flight
+    const int after = min(NS - 1, nu - 1 - u);
+    if constexpr (NS == 2) {
+      if (after >= 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NI) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      if (after >= 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(6 * NI) : "memory");
+      else if (after == 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(4 * NI) : "memory");
+      else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NI) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // S^T for the two 16-key blocks
+    int sp, t0;
+    step_pos(u, sp, t0);
+    const u16* kt = my_ring + (u % NS) * 2 * SG::TILE;
+    const u16* vt = kt + SG::TILE;
+
+    // K (A operand) and V^T fragments of the whole step
+    bf16x8 ka[2][KC];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = 8 * (l16 >> 2) + 4 * kb + (l16 & 3);
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        ka[kb][kk] = *reinterpret_cast<const bf16x8*>(kt + key * D + ((4 * kk + g) ^ swk<D>(key)) * 8);
+    }
+    // (whole 8-byte results are copied into the operand: inserting the bf16
+    // elements one by one is mis-compiled into a splat of element 0)
+    bf16x8 va[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      s16x4 x[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = 8 * g + 4 * h + (l16 >> 2);
+        const int chunk = 2 * db + ((l16 & 3) >> 1);
+        const u16* src = vt + key * D + (chunk ^ swv<D>(key)) * 8 + 4 * (l16 & 1);
+        x[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)src);
+      }
+      __builtin_memcpy(&va[db], x, 16);
+    }
+    // the stage may be refilled once every read of it has returned
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (u + NS < nu) issue(u + NS);
+
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        bf16x8 a;
-        __builtin_memcpy(&a, &kreg[kb][kk], 16);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[kb], 0, 0, 0);
-      }
-    // prefetch the next step of this wave while the math runs
-    if (st + kWaves < nsteps) load_step(st + kWaves);
+      for (int kk = 0; kk < KC; ++kk)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], qf[kk], sacc[kb], 0, 0, 0);
 
     // mask: this lane holds keys t0 + 8g + 4kb + i of row r
     const bool edge = (t0 + kStep > p.T - 1) ||
@@ -235,60 +302,63 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
         lsum += e;
         pf[kb * 4 + i] = (__bf16)e;
       }
-    // O^T += V^T P^T: A = V^T rows d, keys 8g .. 8g+7
+    // O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (db * 16 + l16) * VTS + 8 * g);
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[db], 0, 0, 0);
-    }
+    for (int db = 0; db < DB; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, oacc[db], 0, 0, 0);
   }
 
   // ---- merge the 4 waves in LDS ----
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  __syncthreads();  // every wave is done with its V slab (the merge area aliases it)
+  __syncthreads();  // every wave is done with its ring (the merge area aliases it)
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.mrg.o[wave][l16][db * 16 + 4 * g + i] = oacc[db][i];
+    for (int i = 0; i < 4; ++i) mrg.o[wave][l16][db * 16 + 4 * g + i] = oacc[db][i];
   if (g == 0) {
-    sm.mrg.m[wave][l16] = m;
-    sm.mrg.l[wave][l16] = lsum;
+    mrg.m[wave][l16] = m;
+    mrg.l[wave][l16] = lsum;
   }
   __syncthreads();
   for (int idx = tid; idx < p.R * D; idx += kThreads) {
     const int row = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.mrg.m[w][row]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg.m[w][row]);
     float acc = 0.f, lt = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(sm.mrg.m[w][row] - M);
-        acc += f * sm.mrg.o[w][row][d];
-        lt += f * sm.mrg.l[w][row];
+        const float f = __builtin_amdgcn_exp2f(mrg.m[w][row] - M);
+        acc += f * mrg.o[w][row][d];
+        lt += f * mrg.l[w][row];
       }
     }
     const int rs2 = p.intra ? s_unit : row / p.G;
     const int rh2 = kvh * p.G + (p.intra ? row : row % p.G);
     const size_t orow = (size_t)(b * p.n + rs2) * p.hq + rh2;
-    p.ws_o[(orow * p.splits + split) * D + d] = acc;
-    if (d == 0) {
-      p.ws_ml[(orow * p.splits + split) * 2 + 0] = M;
-      p.ws_ml[(orow * p.splits + split) * 2 + 1] = lt;
+    if (p.splits == 1) {
+      // every row admits at least its own key, so lt > 0
+      p.o[orow * D + d] = __builtin_bit_cast(u16, (__bf16)(acc / lt));
+    } else {
+      p.ws_o[(orow * p.splits + split) * D + d] = acc;
+      if (d == 0) {
+        p.ws_ml[(orow * p.splits + split) * 2 + 0] = M;
+        p.ws_ml[(orow * p.splits + split) * 2 + 1] = lt;
+      }
     }
   }
 }
 
-// One wave per output row. Lanes own splits (lane, lane+64, ...) for the
-// max and the normaliser, and d values (lane, lane+64) for the output; the
-// split weights exp2(m_s - M) are broadcast from LDS. Every reduction runs in
-// a fixed order, so the result is deterministic.
+// One wave per output row. For the output, lane l owns 4 consecutive d
+// values (d4 = l % (D/4)) of the splits s = cls, cls + C, ... with
+// cls = l / (D/4) and C = 64 / (D/4) classes; the classes are summed by lane
+// exchanges at the end. Every reduction runs in a fixed order, so the result
+// is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int64_t rows) {
-  constexpr int kMaxSplits = 1024;
-  __shared__ float wsh[4][kMaxSplits];
+  constexpr int LPR = D / 4;              // lanes covering one split's d values
+  constexpr int C = 64 / LPR;             // split classes per wave
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t orow = int64_t(blockIdx.x) * 4 + wave;
   if (orow >= rows) return;
@@ -300,31 +370,32 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int64_
   float lt = 0.f;
   for (int s = lane; s < p.splits; s += 64) {
     const float ms = ml[2 * s];
-    const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    wsh[wave][s] = f;
-    lt += f * ml[2 * s + 1];
+    lt += ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[2 * s + 1];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float inv = 1.f / lt;
-  const float* po = p.ws_o + orow * p.splits * D;
+
+  const int d4 = lane % LPR, cls = lane / LPR;
+  const float* po = p.ws_o + orow * p.splits * D + 4 * d4;
+  f32x4 acc = f32x4{};
+#pragma unroll 8
+  for (int s = cls; s < p.splits; s += C) {
+    const float ms = ml[2 * s];
+    const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(po + (size_t)s * D);
+    acc += f * x;
+  }
 #pragma unroll
-  for (int d0 = 0; d0 < D; d0 += 64) {
-    float acc = 0.f;
-    int s = 0;
-    for (; s + 4 <= p.splits; s += 4) {
-      const float a0 = po[(s + 0) * D + d0 + lane], a1 = po[(s + 1) * D + d0 + lane];
-      const float a2 = po[(s + 2) * D + d0 + lane], a3 = po[(s + 3) * D + d0 + lane];
-      acc += wsh[wave][s + 0] * a0;
-      acc += wsh[wave][s + 1] * a1;
-      acc += wsh[wave][s + 2] * a2;
-      acc += wsh[wave][s + 3] * a3;
-    }
-    for (; s < p.splits; ++s) acc += wsh[wave][s] * po[s * D + d0 + lane];
-    p.o[orow * D + d0 + lane] = __builtin_bit_cast(u16, (__bf16)(acc * inv));
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
+  if (cls == 0) {
+    const float inv = 1.f / lt;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc[i] * inv);
+    *reinterpret_cast<bf16x4*>(p.o + orow * D + 4 * d4) = ov;
   }
 }
 
@@ -350,9 +421,11 @@ DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t 
   pl.keys = (intra ? 1 : n) * pl.keys_per_stream;
   int64_t want = num_splits;
   if (want == 0) {
-    const int64_t target_groups = 1024;  // about 4 work groups per CU on 256 CUs
+    // A group holds 128 KiB of LDS, so one runs per CU: aim for one group per
+    // CU (256), with chunks of at least 512 keys.
+    const int64_t target_groups = 256;
     want = (target_groups + pl.units - 1) / pl.units;
-    want = std::min<int64_t>(want, std::max<int64_t>(1, pl.keys / 256));
+    want = std::min<int64_t>(want, std::max<int64_t>(1, pl.keys / 512));
   }
   want = std::max<int64_t>(1, std::min<int64_t>({want, pl.keys / kStep, int64_t(1024)}));
   pl.chunk = round_up((pl.keys + want - 1) / want, kChunkQuantum);
@@ -360,7 +433,8 @@ DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t 
   const int64_t rows = batch * n * hq;
   const size_t o_bytes = size_t(rows) * pl.splits * d * 4;
   const size_t ml_bytes = size_t(rows) * pl.splits * 2 * 4;
-  pl.ws_bytes = size_t(round_up(int64_t(o_bytes), 256)) + size_t(round_up(int64_t(ml_bytes), 256));
+  // one split: the split kernel writes the output itself and needs no workspace
+  pl.ws_bytes = pl.splits == 1 ? 0 : size_t(round_up(int64_t(o_bytes), 256)) + size_t(round_up(int64_t(ml_bytes), 256));
   return pl;
 }
 
@@ -390,12 +464,13 @@ hipError_t launch_attn_decode(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.chunk = int32_t(pl.chunk);
   p.keys = int32_t(pl.keys);
   const dim3 grid(uint32_t(pl.splits), uint32_t(pl.units));
+  const dim3 cgrid(uint32_t((rows + 3) / 4));
   if (a.d == 128) {
     hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(uint32_t((rows + 3) / 4)), dim3(256), 0, stream, p, rows);
+    if (pl.splits > 1) hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(256), 0, stream, p, rows);
   } else {
     hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(uint32_t((rows + 3) / 4)), dim3(256), 0, stream, p, rows);
+    if (pl.splits > 1) hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(256), 0, stream, p, rows);
   }
   return hipGetLastError();
 }

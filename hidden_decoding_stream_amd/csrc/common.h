@@ -32,4 +32,28 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
   return uint32_t((uint64_t(hi) + x) >> f.l);
 }
 
+// ---- buffer loads (gfx950) ----
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Offset that makes a buffer load return zeros (>= every num_records used).
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// Raw buffer resource over `bytes` bytes from `base`: loads at offsets past
+// the end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes bytes [16 i, 16 i + 16) after `dst` (one contiguous KiB per wave).
+// The global address is the buffer base + voff; voff is range-checked
+// against the buffer size (past the end: zeros written).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
 }  // namespace sfa

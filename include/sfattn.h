@@ -124,13 +124,15 @@ size_t sf_attn_decode_workspace_bytes(int64_t batch, int32_t n, int64_t T, int32
  *   the new token also sees streams 0..k of that token; under SF_INTRA it sees
  *   tokens 0..T-1 of its own stream only.
  *   workspace : device scratch of at least sf_attn_decode_workspace_bytes(...)
- *               bytes, 16-byte aligned. Its contents on entry do not matter.
+ *               bytes, 16-byte aligned; may be NULL when that size is 0 (one
+ *               split). Its contents on entry do not matter.
  *   num_splits: how many pieces each key range is cut into (0 = chosen by the
- *               library from the problem size; at most 1024 are used). The result does not depend on
- *               it beyond float rounding.
+ *               library from the problem size; at most 1024 are used). The
+ *               result does not depend on it beyond float rounding.
  * Supported: d in {64, 128}; hq % hkv == 0; n*G <= 16 query rows per key/value
  * head under the cross masks (G = hq/hkv), G <= 16 under SF_INTRA; 16-byte
- * aligned q_new, caches and o_new. */
+ * aligned q_new, caches and o_new; T_max*hkv*d*2 < 2^31 (bytes of one
+ * stream's cache of one batch element). */
 sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_cache, void* o_new,
                          int64_t batch, int32_t n, int64_t T, int64_t T_max, int32_t hq,
                          int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,

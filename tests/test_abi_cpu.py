@@ -115,8 +115,8 @@ def dec(q=P, kc=P2, vc=P3, o=P4, batch=1, n=4, T=16, Tmax=16, hq=32, hkv=8, d=12
     (dict(hq=32, hkv=1, mode=0), B.SF_ERR_UNSUPPORTED),  # G = 32 > 16 under intra
     (dict(d=80), B.SF_ERR_UNSUPPORTED),
     (dict(mode=2, window=0), B.SF_ERR_INVALID),
-    (dict(ws=None), B.SF_ERR_INVALID),
-    (dict(wsb=16), B.SF_ERR_INVALID),                 # workspace too small
+    (dict(ws=None, splits=2, T=200, Tmax=200), B.SF_ERR_INVALID),   # two splits need a workspace
+    (dict(wsb=16, splits=2, T=200, Tmax=200), B.SF_ERR_INVALID),    # workspace too small
     (dict(q=None), B.SF_ERR_INVALID),
     (dict(kc=ctypes.c_void_p(0x40000004)), B.SF_ERR_UNSUPPORTED),
 ])
@@ -131,10 +131,12 @@ def test_decode_empty_batch_is_noop():
 def test_workspace_query():
     ws = sfa.sf_attn_decode_workspace_bytes(1, 4, 8192, 32, 8, 128, "cross_full")
     assert ws > 0 and ws % 256 == 0
-    # one split: rows * (d + 2) floats, each part rounded to 256 bytes
-    one = sfa.sf_attn_decode_workspace_bytes(1, 4, 8192, 32, 8, 128, "cross_full", num_splits=1)
-    rows = 1 * 4 * 32
-    assert one == -(-rows * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
+    # one split writes the output directly: no workspace
+    assert sfa.sf_attn_decode_workspace_bytes(1, 4, 8192, 32, 8, 128, "cross_full", num_splits=1) == 0
+    # s splits: rows * s * (d + 2) floats, each part rounded to 256 bytes
+    rows, s = 1 * 4 * 32, 3
+    three = sfa.sf_attn_decode_workspace_bytes(1, 4, 8192, 32, 8, 128, "cross_full", num_splits=s)
+    assert three == -(-rows * s * 128 * 4 // 256) * 256 + -(-rows * s * 2 * 4 // 256) * 256
     assert sfa.sf_attn_decode_workspace_bytes(0, 4, 8192, 32, 8, 128, "intra") == 0
     assert sfa.sf_attn_decode_workspace_bytes(1, 4, 0, 32, 8, 128, "intra") == 0
     assert sfa.sf_attn_decode_workspace_bytes(1, 4, 16, 32, 8, 96, "intra") == 0
