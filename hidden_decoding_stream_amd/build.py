@@ -2,9 +2,11 @@
 
     python -m hidden_decoding_stream_amd.build
 
-Compiles every HIP source under csrc/ to an object in _build/ (at the repository
-root) and links them into hidden_decoding_stream_amd/libsfattn.so. Always
-recompiles: it is the "does it build" check as well as the build.
+Compiles the HIP sources under csrc/ to objects in _build/ (at the repository
+root) and links them into hidden_decoding_stream_amd/libsfattn.so (the
+attention library) and hidden_decoding_stream_amd/libsfpeaks.so (attainable-
+peak microbenchmarks, used only for measurement). Always recompiles: it is the
+"does it build" check as well as the build.
 """
 from __future__ import annotations
 
@@ -22,6 +24,8 @@ INCLUDE = ROOT / "include"
 BUILD = ROOT / "_build"
 LIB = PKG / "libsfattn.so"
 SOURCES = ["api.hip", "interleave.hip", "attn_fwd.hip", "attn_decode.hip"]
+PEAKS_LIB = PKG / "libsfpeaks.so"
+PEAKS_SOURCES = ["peaks.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled: the compiler would otherwise form them
@@ -47,23 +51,27 @@ def _run(cmd):
     return r
 
 
+def _link(cc, objs, lib):
+    tmp = lib.with_name(lib.name + ".tmp")
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)])
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False, extra_flags=()) -> pathlib.Path:
     cc = hipcc()
     BUILD.mkdir(exist_ok=True)
-    objs = []
     cmds = []
-    for src in SOURCES:
+    for src in SOURCES + PEAKS_SOURCES:
         obj = BUILD / (pathlib.Path(src).stem + ".o")
-        objs.append(obj)
-        cmds.append([cc, *FLAGS, *extra_flags, "-c", str(CSRC / src), "-o", str(obj)])
+        cmds.append((obj, [cc, *FLAGS, *extra_flags, "-c", str(CSRC / src), "-o", str(obj)]))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        for cmd, r in zip(cmds, ex.map(_run, cmds)):
+        for (_, cmd), r in zip(cmds, ex.map(_run, [c for _, c in cmds])):
             if verbose:
                 print(" ".join(cmd))
                 sys.stdout.write(r.stderr)
-    tmp = LIB.with_name(LIB.name + ".tmp")
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)])
-    os.replace(tmp, LIB)
+    objs = {pathlib.Path(o).stem: o for o, _ in cmds}
+    _link(cc, [objs[pathlib.Path(s).stem] for s in SOURCES], LIB)
+    _link(cc, [objs[pathlib.Path(s).stem] for s in PEAKS_SOURCES], PEAKS_LIB)
     return LIB
 
 

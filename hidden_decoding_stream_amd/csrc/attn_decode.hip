@@ -41,6 +41,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -110,16 +111,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   constexpr int DB = D / 16;              // 16-row d blocks of O^T
   constexpr int NS = SG::NS;
   constexpr int NI = SG::NI;
-  // per wave: NS stages of (K tile, V tile); the merge area aliases the rings
   struct Merge {
     float o[kWaves][16][D];
     float m[kWaves][16];
     float l[kWaves][16];
   };
-  constexpr int kRingElems = kWaves * NS * 2 * SG::TILE;
-  static_assert(sizeof(Merge) <= kRingElems * 2, "merge area must fit in the rings");
-  __shared__ __attribute__((aligned(16))) u16 ring[kRingElems];
-  Merge& mrg = *reinterpret_cast<Merge*>(ring);
+  // One shared array per ring stage, holding every wave's (K tile, V tile)
+  // of that stage. Each unrolled step below names its stage at compile time,
+  // so the compiler can tell that the DMA in flight writes another array
+  // than the one being read and adds no wait for it. The merge area at the
+  // end aliases stage 0.
+  constexpr int kStageElems = kWaves * 2 * SG::TILE;
+  static_assert(sizeof(Merge) <= kStageElems * 2, "merge area must fit in stage 0");
+  __shared__ __attribute__((aligned(16))) u16 st0[kStageElems];
+  __shared__ __attribute__((aligned(16))) u16 st1[kStageElems];
+  __shared__ __attribute__((aligned(16))) u16 st2[NS > 2 ? kStageElems : 8];
+  __shared__ __attribute__((aligned(16))) u16 st3[NS > 3 ? kStageElems : 8];
+  Merge& mrg = *reinterpret_cast<Merge*>(st0);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -145,13 +153,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   const int rh = kvh * p.G + (p.intra ? r : r % p.G);           // query head of the row
   const int pq = (p.T - 1) * p.n + rs;                           // its expanded position
 
-  bf16x8 qf[KC];
-  {
-    const u16* qrow = p.q + ((size_t)(b * p.n + rs) * p.hq + (rvalid ? rh : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
-      qf[kk] = rvalid ? *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * g) : bf16x8{};
-  }
 
   const size_t stream_stride = (size_t)p.Tmax * p.hkv * D;      // elements between streams
   const uint32_t trow_b = uint32_t(p.hkv) * D * 2;              // bytes between tokens
@@ -176,7 +177,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     koff[i] = uint32_t(row) * trow_b + uint32_t(c ^ swk<D>(row)) * 16;
     voff[i] = uint32_t(row) * trow_b + uint32_t(c ^ swv<D>(row)) * 16;
   }
-  u16* my_ring = ring + wave * NS * 2 * SG::TILE;
+  // this wave's slot of ring stage S (compile-time)
+  auto stage = [&](auto S) -> u16* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return st0 + wave * 2 * SG::TILE;
+    else if constexpr (st == 1) return st1 + wave * 2 * SG::TILE;
+    else if constexpr (st == 2) return st2 + wave * 2 * SG::TILE;
+    else return st3 + wave * 2 * SG::TILE;
+  };
 
   auto step_pos = [&](int u, int& sp, int& t0) {
     const int j0 = j_begin + (wave + u * kWaves) * kStep;
@@ -184,13 +192,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     sp = p.intra ? s_unit : ss;
     t0 = p.t_lo + (j0 - ss * p.kps);
   };
-  auto issue = [&](int u) {
+  auto issue = [&](int u, auto S) {
     int sp, t0;
     step_pos(u, sp, t0);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + (size_t)sp * stream_stride, range_b);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + (size_t)sp * stream_stride, range_b);
     const uint32_t sbase = uint32_t(t0) * trow_b;
-    u16* kt = my_ring + (u % NS) * 2 * SG::TILE;
+    u16* kt = stage(S);
     u16* vt = kt + SG::TILE;
     // the step base goes into the per-lane offset: only that offset is
     // range-checked, which is what turns rows t >= T into zeros
@@ -205,13 +213,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
 
-  // Q must be in registers before the first DMA is counted against vmcnt.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Q is loaded before any DMA goes out, so the wait for it that the compiler
+  // places before the first step leaves every stage in flight.
+  bf16x8 qf[KC];
+  {
+    const u16* qrow = p.q + ((size_t)(b * p.n + rs) * p.hq + (rvalid ? rh : 0)) * D;
 #pragma unroll
-  for (int u = 0; u < NS; ++u)
-    if (u < nu) issue(u);
+    for (int kk = 0; kk < KC; ++kk)
+      qf[kk] = rvalid ? *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * g) : bf16x8{};
+  }
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  if (nu > 0) issue(0, S0{});
+  if (nu > 1) issue(1, S1{});
+  if constexpr (NS > 2) {
+    if (nu > 2) issue(2, S2{});
+    if (nu > 3) issue(3, S3{});
+  }
 
-  for (int u = 0; u < nu; ++u) {
+  auto step = [&](int u, auto S) {
     // wait for step u: the stages issued after it may stay in flight
     const int after = min(NS - 1, nu - 1 - u);
     if constexpr (NS == 2) {
@@ -225,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     }
     int sp, t0;
     step_pos(u, sp, t0);
-    const u16* kt = my_ring + (u % NS) * 2 * SG::TILE;
+    const u16* kt = stage(S);
     const u16* vt = kt + SG::TILE;
 
     // K (A operand) and V^T fragments of the whole step
@@ -237,24 +259,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
       for (int kk = 0; kk < KC; ++kk)
         ka[kb][kk] = *reinterpret_cast<const bf16x8*>(kt + key * D + ((4 * kk + g) ^ swk<D>(key)) * 8);
     }
-    // (whole 8-byte results are copied into the operand: inserting the bf16
-    // elements one by one is mis-compiled into a splat of element 0)
+    // V^T: per d block two transposed reads (keys 8g..8g+3, 8g+4..8g+7),
+    // issued in two asm blocks of eight; whole 8-byte results are copied into
+    // the operand (element-wise bf16 inserts were mis-compiled into a splat).
     bf16x8 va[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      s16x4 x[2];
+    for (int half = 0; half < DB / 4; ++half) {
+      uint32_t addr[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int j = 0; j < 8; ++j) {
+        const int db = half * 4 + j / 2, h = j & 1;
         const int key = 8 * g + 4 * h + (l16 >> 2);
         const int chunk = 2 * db + ((l16 & 3) >> 1);
-        const u16* src = vt + key * D + (chunk ^ swv<D>(key)) * 8 + 4 * (l16 & 1);
-        x[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)src);
+        addr[j] = lds_addr(vt + key * D + (chunk ^ swv<D>(key)) * 8 + 4 * (l16 & 1));
       }
-      __builtin_memcpy(&va[db], x, 16);
+      u32x2 x[8];
+      tr_read8(x, addr);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) __builtin_memcpy(&va[half * 4 + j], &x[2 * j], 16);
     }
     // the stage may be refilled once every read of it has returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (u + NS < nu) issue(u + NS);
+    if (u + NS < nu) issue(u + NS, S);
 
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
@@ -305,12 +331,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, oacc[db], 0, 0, 0);
+  };
+  for (int u0 = 0; u0 < nu; u0 += NS) {
+    step(u0, S0{});
+    if (u0 + 1 < nu) step(u0 + 1, S1{});
+    if constexpr (NS > 2) {
+      if (u0 + 2 < nu) step(u0 + 2, S2{});
+      if (u0 + 3 < nu) step(u0 + 3, S3{});
+    }
   }
 
   // ---- merge the 4 waves in LDS ----
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  __syncthreads();  // every wave is done with its ring (the merge area aliases it)
+  __syncthreads();  // every wave is done with its ring (the merge area aliases stage 0)
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll

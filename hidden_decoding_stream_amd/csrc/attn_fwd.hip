@@ -113,6 +113,80 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// All V^T fragments of a tile in one asm block of ds_read_b64_tr_b16,
+// which also waits for them: output i = ((db*2 + kb)*2 + j2)*2 + tr reads
+// key row kb*32 + 4*(2*tr + j2) (+ the lane's row within its group) of the
+// 32-wide d block db, from base ae[db] (j2 = 0) or ao[db] (j2 = 1) plus an
+// immediate offset. Through the builtin, the compiler cannot tell which LDS
+// a transposed read touches and waits for every buffer->LDS load in flight
+// before it, which would drain the DMA of the next tiles on every tile.
+template <int D> __device__ __forceinline__ void gather_vt(u32x2 (&x)[D / 4], const uint32_t (&ae)[D / 32],
+                                                          const uint32_t (&ao)[D / 32]);
+template <> __device__ __forceinline__ void gather_vt<128>(u32x2 (&x)[32], const uint32_t (&ae)[4],
+                                                          const uint32_t (&ao)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %32 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %32 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %36 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %3, %36 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %4, %32 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %5, %32 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %6, %36 offset:9216\n\t"
+      "ds_read_b64_tr_b16 %7, %36 offset:11264\n\t"
+      "ds_read_b64_tr_b16 %8, %33 offset:0\n\t"
+      "ds_read_b64_tr_b16 %9, %33 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %37 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %11, %37 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %12, %33 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %13, %33 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %14, %37 offset:9216\n\t"
+      "ds_read_b64_tr_b16 %15, %37 offset:11264\n\t"
+      "ds_read_b64_tr_b16 %16, %34 offset:0\n\t"
+      "ds_read_b64_tr_b16 %17, %34 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %18, %38 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %19, %38 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %20, %34 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %21, %34 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %22, %38 offset:9216\n\t"
+      "ds_read_b64_tr_b16 %23, %38 offset:11264\n\t"
+      "ds_read_b64_tr_b16 %24, %35 offset:0\n\t"
+      "ds_read_b64_tr_b16 %25, %35 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %26, %39 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %27, %39 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %28, %35 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %29, %35 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %30, %39 offset:9216\n\t"
+      "ds_read_b64_tr_b16 %31, %39 offset:11264\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]), "=&v"(x[18]), "=&v"(x[19]), "=&v"(x[20]), "=&v"(x[21]), "=&v"(x[22]), "=&v"(x[23]), "=&v"(x[24]), "=&v"(x[25]), "=&v"(x[26]), "=&v"(x[27]), "=&v"(x[28]), "=&v"(x[29]), "=&v"(x[30]), "=&v"(x[31])
+      : "v"(ae[0]), "v"(ae[1]), "v"(ae[2]), "v"(ae[3]), "v"(ao[0]), "v"(ao[1]), "v"(ao[2]), "v"(ao[3])
+      : "memory");
+}
+template <> __device__ __forceinline__ void gather_vt<64>(u32x2 (&x)[16], const uint32_t (&ae)[2],
+                                                          const uint32_t (&ao)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:512\n\t"
+      "ds_read_b64_tr_b16 %3, %18 offset:1536\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:4608\n\t"
+      "ds_read_b64_tr_b16 %7, %18 offset:5632\n\t"
+      "ds_read_b64_tr_b16 %8, %17 offset:0\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %10, %19 offset:512\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:1536\n\t"
+      "ds_read_b64_tr_b16 %12, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %13, %17 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:4608\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:5632\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
+      : "v"(ae[0]), "v"(ae[1]), "v"(ao[0]), "v"(ao[1])
+      : "memory");
+}
+
 // Tile layouts in LDS (elements, bf16):
 //  K: BN rows of D + 16 (two 16-byte pad slots per row). A 16-byte operand
 //     read is served 8 lanes from each half wave per cycle (lanes i and i+32
@@ -286,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  __syncthreads();
+  asm volatile("s_barrier" ::: "memory");   // no fence: tile kt_begin + 1 may still fly
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int st = kt % ST;
@@ -312,6 +386,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
         for (int kk = 0; kk < KD; ++kk)
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][kk], qf[kk], sacc[kb], 0, 0, 0);
       }
+      // ---- V^T fragments by transposed LDS reads, issued while the matrix
+      // cores still work on S^T (the mask below is the first use of it) ----
+      bf16x8 va[DB][2][2];
+      {
+        const uint32_t vt = lds_addr(&vs[st][0]);
+        uint32_t ae[DB], ao[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int col = ((db ^ vsw) - db) * 32 + db * 32;
+          ae[db] = vt + uint32_t(vbase_even + col) * 2;
+          ao[db] = vt + uint32_t(vbase_odd + col) * 2;
+        }
+        u32x2 x[D / 4];
+        gather_vt<D>(x, ae, ao);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j2 = 0; j2 < 2; ++j2) __builtin_memcpy(&va[db][kb][j2], &x[((db * 2 + kb) * 2 + j2) * 2], 16);
+      }
+
       const bool full = (k0 + BN - 1 <= q0) && (window == 0 || qhi - k0 < window);
       if (!full) {
         const int vq = q0 + l32;
@@ -327,29 +423,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
               const bool ok = uint32_t(vq - key) < lim;
               sacc[kb][4 * g + r] = ok ? sacc[kb][4 * g + r] : -INFINITY;
             }
-      }
-
-      // ---- V^T fragments, gathered by transposed LDS reads; requested
-      // before the softmax so they arrive while it runs ----
-      const u16* vt = &vs[st][0];
-      bf16x8 va[DB][2][2];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = ((db ^ vsw) - db) * 32;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2) {
-            s16x4 x[2];
-#pragma unroll
-            for (int tr = 0; tr < 2; ++tr) {
-              const int c = 2 * tr + j2;
-              const int base = (c & 1) ? vbase_odd : vbase_even;
-              const int off = base + col + (kb * 32 + 4 * c) * D + db * 32;
-              x[tr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vt + off));
-            }
-            __builtin_memcpy(&va[db][kb][j2], x, 16);
-          }
       }
 
       // ---- online softmax (base 2, lazy rescale) ----
@@ -405,7 +478,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
         asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kMinChunks) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      // A bare barrier: __syncthreads() would add a release fence, which
+      // waits for every load in flight, the DMA of tile kt + 2 included.
+      // Every LDS read of this tile has been consumed by an MFMA above.
+      asm volatile("s_barrier" ::: "memory");
     }
   }
 

@@ -56,4 +56,35 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
 }
 
+// ---- transposed LDS reads (gfx950) ----
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// Eight ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+// element i % 4 of the 8 bytes that lanes 4e + i / 4 address, as its element
+// e (e = 0..3). Written as one asm block that also waits for the results,
+// so every output is complete when the statement ends. (Through the
+// builtin, the compiler cannot tell which LDS the read touches and waits
+// for every buffer->LDS load in flight before it, which would drain a
+// prefetch ring on every step.)
+__device__ __forceinline__ void tr_read8(u32x2 (&o)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 }  // namespace sfa
