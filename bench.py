@@ -118,7 +118,7 @@ def main():
     q_new = qs[:, 0, L - 1].unsqueeze(0).contiguous()                          # [1][n][hq][d]
     od = torch.empty_like(q_new)
     ws_bytes = sfa.sf_attn_decode_workspace_bytes(B, n, L, hq, hkv, d, "cross_full")
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     flops_cross = C.prefill_flops("cross_full", n, L, B, hq, d)
     flops_intra = C.prefill_flops("intra", n, L, B, hq, d)
@@ -248,7 +248,7 @@ def decode_sweep(torch, sfa, C, I, dev):
                 vc = torch.randn((batch, w.n, w.T, w.hkv, w.d), generator=g, device=dev).to(torch.bfloat16)
                 caches.append((kc, vc))
             o = torch.empty_like(q)
-            ws = torch.empty(sfa.sf_attn_decode_workspace_bytes(batch, w.n, w.T, w.hq, w.hkv, w.d, mode),
+            ws = torch.empty(sfa.sf_attn_decode_workspace_bytes(batch, w.n, w.T, w.hq, w.hkv, w.d, mode) + 16,
                              dtype=torch.uint8, device=dev)
             for i in range(3):
                 kc, vc = caches[i % copies]

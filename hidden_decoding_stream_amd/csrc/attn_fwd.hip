@@ -32,12 +32,14 @@
 //   transposed LDS read ds_read_b64_tr_b16, addressed so that each lane
 //   receives exactly the keys its P^T registers hold.
 // * Memory. K and V tiles go from HBM to LDS by buffer->LDS DMA loads (no
-//   staging registers, no LDS write instructions), double-buffered with one
-//   barrier per tile. Rows past the end of a sequence use an out-of-range
-//   offset and read as zeros, with no branch. LDS rows are padded so that all
-//   operand reads are free of bank conflicts.
-// * Occupancy. Each wave owns 32 queries; two 4-wave work groups share a CU,
-//   so one wave's softmax overlaps the other's matrix-core work.
+//   staging registers, no LDS write instructions) through a 3-stage ring:
+//   the DMA of tile t+2 is issued at the top of tile t, and one bare barrier
+//   per tile publishes tile t+1. Rows past the end of a sequence use an
+//   out-of-range offset and read as zeros, with no branch. K rows are padded
+//   and V pieces swizzled so that the operand reads are free of bank
+//   conflicts.
+// * Occupancy. A work group is 8 waves (two per SIMD), each owning 32
+//   queries of one query head; one group per CU (104 KiB of LDS at d=128).
 // * Online softmax in base 2 with lazy rescaling: the running reference max m
 //   is raised only when a tile's max exceeds it by more than 2^8; until then
 //   exp2(s - m) <= 256 and no O rescale is needed. The result is the same
@@ -425,26 +427,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
             }
       }
 
-      // ---- online softmax (base 2, lazy rescale) ----
-      float mx = -INFINITY;
+      // ---- online softmax (base 2, lazy rescale) and O^T += V^T P^T, one
+      // 32-key block at a time: block 0's VALU work needs only sacc[0], so it
+      // runs while the matrix cores finish block 1's scores, and block 1's
+      // runs while they work on block 0's P V. A raised reference max
+      // rescales O (and l) before the block's P V. ----
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        float mx = sacc[kb][0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      const float cand = pair_max(mx) * p.c;
-      const bool need = cand > m + kRescaleLog2;
-      float o_alpha = 1.f;
-      const bool o_rescale = __any(need);
-      if (o_rescale) {
-        o_alpha = need ? __builtin_amdgcn_exp2f(m - cand) : 1.f;
-        m = need ? cand : m;
-        lsum *= o_alpha;
-      }
-      const float mu = m == -INFINITY ? 0.f : m;
-      bf16x8 pf[2][2];
-      float ls = 0.f;
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        const float cand = pair_max(mx) * p.c;
+        const bool need = cand > m + kRescaleLog2;
+        if (__any(need)) {
+          const float alpha = need ? __builtin_amdgcn_exp2f(m - cand) : 1.f;
+          m = need ? cand : m;
+          lsum *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        }
+        const float mu = m == -INFINITY ? 0.f : m;
+        bf16x8 pf[2];
+        float ls = 0.f;
 #pragma unroll
         for (int j2 = 0; j2 < 2; ++j2) {
           bf16x8 pv;
@@ -454,22 +458,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
             ls += e;
             pv[i] = (__bf16)e;
           }
-          pf[kb][j2] = pv;
+          pf[j2] = pv;
         }
-      lsum += ls;
-
-      // ---- O^T += V^T P^T (a raised reference max rescales O first) ----
-      if (o_rescale) {
+        lsum += ls;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= o_alpha;
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int j2 = 0; j2 < 2; ++j2)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb][j2], pf[kb][j2], oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb][j2], pf[j2], oacc[db], 0, 0, 0);
+      }
     }
 
     if (kt + 1 < kt_end) {

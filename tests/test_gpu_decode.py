@@ -79,3 +79,30 @@ def test_full_size(batch, mode):
         assert_close(np64(o[b:b + 1]), ref, f"{w.name} b={b}")
     del q, kc, vc
     torch.cuda.empty_cache()
+
+
+def test_workspace_reused_across_calls():
+    """One workspace, its contents left over from earlier calls, serves
+    consecutive calls of different shapes, split counts and masks; each
+    result matches the oracle."""
+    ws = torch.full((1 << 22,), 0x7f, dtype=torch.uint8, device="cuda")    # not zero on purpose
+    calls = [
+        # B, n, T, T_max, hq, hkv, d, mode, window, splits
+        (2, 4, 1000, 1000, 32, 8, 128, "cross_full", 0, 7),
+        (1, 4, 300, 320, 8, 2, 64, "intra", 0, 5),
+        (2, 4, 1000, 1000, 32, 8, 128, "cross_full", 0, 7),     # same shape again
+        (1, 2, 777, 800, 8, 1, 128, "cross_window", 300, 2),
+        (1, 4, 8192, 8192, 32, 8, 128, "cross_full", 0, 0),     # library-chosen splits
+        (3, 4, 129, 129, 8, 2, 128, "cross_full", 0, 3),        # smaller after larger
+    ]
+    for i, (B, n, T, Tm, hq, hkv, d, mode, W, splits) in enumerate(calls):
+        say("decode workspace reuse", i, mode, "splits", splits)
+        w = I.DecodeWorkload("t", n, T, Tm, B, hq, hkv, d, mode, window=W, seed=100 + i)
+        q, kc, vc = I.decode_inputs(w)
+        need = sfa.sf_attn_decode_workspace_bytes(B, n, T, hq, hkv, d, mode, W, splits)
+        assert need <= ws.numel()
+        o = sfa.sf_attn_decode(q.cuda(), kc.cuda(), vc.cuda(), T, mode, window=W, scale=_scale(d),
+                               num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        ref = orc.decode(np64(q), np64(kc), np64(vc), T, mode, window=W or None, scale=_scale(d))
+        assert_close(np64(o), ref, f"reuse call {i}")
