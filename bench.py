@@ -203,7 +203,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "attn_fwd_kernel<128, 1> (cross_full) 32k",
+            "kernel": "attn_fwd_kernel<128, 1, false> (cross_full) 32k",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -223,11 +223,37 @@ def main():
         "decode_vs_prefill_max_abs": dev_err,
     }
 
+    line["last_stream"] = last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream)
     if not args.no_decode_sweep:
         line["decode"] = decode_sweep(torch, sfa, C, I, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, C, I, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream, reps=10):
+    """Attention of stream n-1's queries only (one per token) against all
+    streams' K/V of the same 32k workload: useful TFLOP/s per mode."""
+    ql = Q[:, n - 1::n].contiguous()
+    o = torch.empty_like(ql)
+    out = {}
+    for mode in ("cross_full", "intra"):
+        for _ in range(2):
+            sfa.sf_attn_fwd_last_stream(ql, K, V, mode, n, scale=scale, out=o)
+        pairs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sfa.sf_attn_fwd_last_stream(ql, K, V, mode, n, scale=scale, out=o)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in pairs) / reps
+        fl = C.last_stream_flops(mode, n, L, B, hq, d)
+        out[mode] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "useful_flop": fl}
+        print(f"[bench] last-stream {mode}: {ms:.3f} ms, {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+    return out
 
 
 def decode_sweep(torch, sfa, C, I, dev):

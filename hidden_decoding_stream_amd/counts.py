@@ -25,6 +25,24 @@ def prefill_flops(mode: str, n: int, L: int, batch: int, hq: int, d: int, window
     return 4 * d * prefill_pairs(mode, n, L, window) * batch * hq
 
 
+def last_stream_pairs(mode: str, n: int, L: int, window: int = 0) -> int:
+    """Admitted pairs of one head when only stream n-1 queries: token i's
+    query sits at position i*n + n-1 and sees that many + 1 positions
+    (cross), at most `window` of them (cross_window), or i + 1 keys of its
+    own stream (intra)."""
+    if mode == "intra":
+        return L * (L + 1) // 2
+    if mode == "cross_full" or window >= n * L:
+        return n * L * (L + 1) // 2
+    if mode == "cross_window":
+        return sum(min(i * n + n, window) for i in range(L))
+    raise ValueError(mode)
+
+
+def last_stream_flops(mode: str, n: int, L: int, batch: int, hq: int, d: int, window: int = 0) -> int:
+    return 4 * d * last_stream_pairs(mode, n, L, window) * batch * hq
+
+
 def decode_pairs(mode: str, n: int, T: int, window: int = 0) -> int:
     """Admitted pairs of the n queries of token T-1 for one head."""
     total = 0

@@ -105,36 +105,60 @@ sf_status sf_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_
                        "sf_interleave launch");
 }
 
-sf_status sf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
-                      int32_t mode, int64_t window, float scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// sf_attn_fwd and sf_attn_fwd_last_stream: the same checks, with q, o and lse
+// holding every position (n*L rows) or one row per token (L rows).
+sf_status attn_fwd_checked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch,
+                           int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d, int32_t mode,
+                           int64_t window, float scale, bool last_stream, hipStream_t stream) {
+  const char* fn = last_stream ? "sf_attn_fwd_last_stream" : "sf_attn_fwd";
   if (batch < 0 || L < 0) return fail(SF_ERR_INVALID, "batch and L must be >= 0");
   sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
   if (st != SF_OK) return st;
   if (batch == 0 || L == 0) return ok();
   if (!q || !k || !v || !o) return fail(SF_ERR_INVALID, "null q, k, v or o");
+  const int32_t qrows = last_stream ? 1 : n;   // query rows per token
   int64_t qe = batch, kve = batch;
-  if (!mul_ok(qe, n) || !mul_ok(qe, L) || !mul_ok(qe, hq) || !mul_ok(qe, d) ||
+  if (!mul_ok(qe, qrows) || !mul_ok(qe, L) || !mul_ok(qe, hq) || !mul_ok(qe, d) ||
       !mul_ok(kve, n) || !mul_ok(kve, L) || !mul_ok(kve, hkv) || !mul_ok(kve, d))
     return fail(SF_ERR_INVALID, "tensor size overflows int64");
-  if (qe > (int64_t(1) << 30))
-    return fail(SF_ERR_UNSUPPORTED, "q has %lld elements; at most 2^30 supported", (long long)qe);
+  if (qe > (int64_t(1) << 30) || kve > (int64_t(1) << 30))
+    return fail(SF_ERR_UNSUPPORTED, "q has %lld and k %lld elements; at most 2^30 each supported", (long long)qe,
+                (long long)kve);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return fail(SF_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(SF_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
   if (overlaps(o, qe * 2, q, qe * 2) || overlaps(o, qe * 2, k, kve * 2) || overlaps(o, qe * 2, v, kve * 2))
     return fail(SF_ERR_INVALID, "o overlaps an input");
   if (lse) {
-    int64_t le = batch;
-    mul_ok(le, hq);
-    mul_ok(le, n);
-    mul_ok(le, L);
+    const int64_t le = qe / d;   // batch * rows * hq
     if (overlaps(lse, le * 4, o, qe * 2) || overlaps(lse, le * 4, q, qe * 2) ||
         overlaps(lse, le * 4, k, kve * 2) || overlaps(lse, le * 4, v, kve * 2))
       return fail(SF_ERR_INVALID, "lse overlaps another tensor");
   }
-  sfa::FwdArgs a{q, k, v, o, lse, batch, n, L, hq, hkv, d, mode, window, scale};
-  return device_status(sfa::launch_attn_fwd(a, stream), "sf_attn_fwd launch");
+  sfa::FwdArgs a{q, k, v, o, lse, batch, n, L, hq, hkv, d, mode, window, scale, last_stream};
+  char what[64];
+  snprintf(what, sizeof what, "%s launch", fn);
+  return device_status(sfa::launch_attn_fwd(a, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+sf_status sf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
+                      int32_t mode, int64_t window, float scale, hipStream_t stream) {
+  return attn_fwd_checked(q, k, v, o, lse, batch, n, L, hq, hkv, d, mode, window, scale, false, stream);
+}
+
+sf_status sf_attn_fwd_last_stream(const void* q_last, const void* k, const void* v, void* o_last, float* lse,
+                                  int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
+                                  int32_t mode, int64_t window, float scale, hipStream_t stream) {
+  return attn_fwd_checked(q_last, k, v, o_last, lse, batch, n, L, hq, hkv, d, mode, window, scale, true, stream);
 }
 
 size_t sf_attn_decode_workspace_bytes(int64_t batch, int32_t n, int64_t T, int32_t hq,

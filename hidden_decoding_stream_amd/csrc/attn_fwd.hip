@@ -75,9 +75,15 @@ struct FwdParams {
   u16* o;
   float* lse;
   int32_t S;         // expanded positions per sequence
-  int32_t Lv;        // length of a virtual sequence (S cross, L intra)
-  int32_t pstride;   // virtual index -> position stride (1 cross, n intra)
+  int32_t Lv;        // keys of a virtual sequence (S cross, L intra)
+  int32_t pstride;   // virtual key index -> position stride (1 cross, n intra)
   int32_t nseq;      // virtual sequences per batch element (1 cross, n intra)
+  int32_t sq0;       // stream of the first virtual sequence (intra)
+  // Queries. Query iq of virtual sequence sq sits in Q / O row
+  // b*QS + sq*q_sq + iq*q_rs and on key index iq*qn + qoff (its diagonal).
+  int32_t Lq;        // queries per virtual sequence
+  int32_t QS, q_sq, q_rs;
+  int32_t qn, qoff;
   int32_t hq, hkv, G, HG;
   int32_t window;    // > 0: cross_window limit in positions; 0: none
   float c;           // scale * log2(e)
@@ -222,8 +228,10 @@ template <int D> __device__ __forceinline__ int vswz(int row) {
 // apart within a tile, so one's softmax overlaps the other's MFMAs.
 // MODE is the mask (0 intra, 1 causal over the expanded sequence, 2 causal
 // and windowed), fixed at compile time so that the masks and the position
-// arithmetic of the other modes fold away.
-template <int D, int MODE>
+// arithmetic of the other modes fold away. LASTQ: the queries are the last
+// stream's only (one per token) against every stream's keys, so a query's
+// diagonal lies at key index iq*n + n-1 rather than iq.
+template <int D, int MODE, bool LASTQ>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   using TL = Tile<D>;
   constexpr int KD = D / 16;              // 16-wide d steps of Q K^T
@@ -238,6 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
 
   const int pstride = MODE == 0 ? p.pstride : 1;
   const int window = MODE == 2 ? p.window : 0;
+  // key index of a query's own position (the last key it may see)
+  auto diag = [&](int iq) { return LASTQ ? iq * p.qn + p.qoff : iq; };
 
   const int tid = threadIdx.x;
   // wave index as a wave-uniform (scalar) value, so that per-wave decisions
@@ -256,17 +266,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   const int hg = rr % p.hgroups;
   const int kvh = unit % p.hkv;
   const int bs = unit / p.hkv;
-  const int sq = bs % p.nseq;
+  const int sq = p.sq0 + bs % p.nseq;
   const int b = bs / p.nseq;
   const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
   const int PS = (kWaves / p.HG) * 32;
   const int wg_q0 = qb * PS;
   const int q0 = wg_q0 + (wave / p.HG) * 32;
-  const int wg_qlast = min(wg_q0 + PS, p.Lv) - 1;
-  const int kt_begin = window > 0 ? max(0, wg_q0 - window + 1) / BN : 0;
-  const int kt_end = wg_qlast / BN + 1;
+  const int wg_qlast = min(wg_q0 + PS, p.Lq) - 1;
+  const int kt_begin = window > 0 ? max(0, diag(wg_q0) - window + 1) / BN : 0;
+  const int kt_end = diag(wg_qlast) / BN + 1;
 
-  const int base_row = b * p.S + sq;       // position of virtual index 0
+  const int base_row = b * p.S + sq;       // position of virtual key index 0
+  const int qbase_row = b * p.QS + sq * p.q_sq;   // Q / O row of query 0
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k, p.kv_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
@@ -277,8 +288,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   bf16x8 qf[KD];
   {
     const int vq = q0 + l32;
-    const uint32_t off = ((uint32_t(base_row + vq * pstride) * p.hq + h) * D + 8 * hh) * 2 +
-                         (vq < p.Lv ? 0u : kOobOffset);
+    const uint32_t off = ((uint32_t(qbase_row + vq * p.q_rs) * p.hq + h) * D + 8 * hh) * 2 +
+                         (vq < p.Lq ? 0u : kOobOffset);
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
       const uint4 x = bload16(qrs, off + kk * 32);
@@ -346,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   const int vbase = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3);
   const int vbase_even = vbase + vh * 20 * D;
   const int vbase_odd = vbase + vh * 12 * D;
-  const int qhi = min(q0 + 32, p.Lv) - 1;
-  const bool wave_live = q0 < p.Lv;
+  const int qhi = min(q0 + 32, p.Lq) - 1;
+  const bool wave_live = q0 < p.Lq;
 
   float m = -INFINITY, lsum = 0.f;
   f32x16 oacc[DB];
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
     const int pre = kt + 2;                    // tile whose DMA is issued during this one
     const bool do_pre = pre < kt_end;
     const int k0 = kt * BN;
-    const bool live = wave_live && k0 <= qhi && !(window > 0 && q0 - (k0 + BN - 1) >= window);
+    const bool live = wave_live && k0 <= diag(qhi) && !(window > 0 && diag(q0) - (k0 + BN - 1) >= window);
     if (do_pre) issue_chunks(pre, 0, NCW);
     if (live) {
       // ---- S^T = K Q^T for two 32-key blocks ----
@@ -410,9 +421,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
             for (int j2 = 0; j2 < 2; ++j2) __builtin_memcpy(&va[db][kb][j2], &x[((db * 2 + kb) * 2 + j2) * 2], 16);
       }
 
-      const bool full = (k0 + BN - 1 <= q0) && (window == 0 || qhi - k0 < window);
+      const bool full = (k0 + BN - 1 <= diag(q0)) && (window == 0 || diag(qhi) - k0 < window);
       if (!full) {
-        const int vq = q0 + l32;
+        const int vq = diag(q0 + l32);
         const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -486,9 +497,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   if (!wave_live) return;
   const float lt = pair_sum(lsum);
   const int vq = q0 + l32;
-  if (vq >= p.Lv) return;
+  if (vq >= p.Lq) return;
   const float inv = 1.f / lt;
-  const size_t prow = (size_t)(base_row + vq * pstride);
+  const size_t prow = (size_t)(qbase_row + vq * p.q_rs);
   u16* orow = p.o + (prow * p.hq + h) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -501,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
       *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hh) = ov;
     }
   if (p.lse && hh == 0)
-    p.lse[((size_t)b * p.hq + h) * p.S + (prow - (size_t)b * p.S)] = (m + log2f(lt)) * kLn2;
+    p.lse[((size_t)b * p.hq + h) * p.QS + (prow - (size_t)b * p.QS)] = (m + log2f(lt)) * kLn2;
 }
 
 }  // namespace
@@ -518,7 +529,27 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   const bool intra = a.mode == 0;
   p.Lv = int32_t(intra ? a.L : S);
   p.pstride = intra ? a.n : 1;
-  p.nseq = intra ? a.n : 1;
+  if (!a.last_stream) {
+    // every position queries: a query shares the virtual index of its key
+    p.nseq = intra ? a.n : 1;
+    p.sq0 = 0;
+    p.Lq = p.Lv;
+    p.QS = p.S;
+    p.q_sq = 1;
+    p.q_rs = p.pstride;
+    p.qn = 1;
+    p.qoff = 0;
+  } else {
+    // one query per token, stream n-1's, in a dense [B][L] tensor
+    p.nseq = 1;
+    p.sq0 = intra ? a.n - 1 : 0;
+    p.Lq = int32_t(a.L);
+    p.QS = int32_t(a.L);
+    p.q_sq = 0;
+    p.q_rs = 1;
+    p.qn = intra ? 1 : a.n;
+    p.qoff = intra ? 0 : a.n - 1;
+  }
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.G = a.hq / a.hkv;
@@ -529,18 +560,23 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   p.window = (a.mode == 2 && a.window < S) ? int32_t(a.window) : 0;
   p.c = a.scale * kLog2e;
   const int PS = (kWaves / p.HG) * 32;
-  p.nqb = (p.Lv + PS - 1) / PS;
+  p.nqb = (p.Lq + PS - 1) / PS;
   const int64_t total = int64_t(a.batch) * p.nseq * p.hkv * p.nqb * p.hgroups;
   p.total = int32_t(total);
   p.per_xcd = int32_t((total + 7) / 8);
-  p.q_bytes = uint32_t(a.batch * S * a.hq * a.d * 2);
+  p.q_bytes = uint32_t(a.batch * p.QS * a.hq * a.d * 2);
   p.kv_bytes = uint32_t(a.batch * S * a.hkv * a.d * 2);
   const dim3 grid(uint32_t(p.per_xcd) * 8u);
   using Kernel = void (*)(FwdParams);
-  static constexpr Kernel kKernels[2][3] = {
-      {attn_fwd_kernel<64, 0>, attn_fwd_kernel<64, 1>, attn_fwd_kernel<64, 2>},
-      {attn_fwd_kernel<128, 0>, attn_fwd_kernel<128, 1>, attn_fwd_kernel<128, 2>}};
-  const int kind = intra ? 0 : (p.window > 0 ? 2 : 1);
+  // [d == 128][kind]: kinds 0-2 are the masks, 3-4 cross_full / cross_window
+  // with last-stream queries (last-stream intra is plain intra on stream n-1)
+  static constexpr Kernel kKernels[2][5] = {
+      {attn_fwd_kernel<64, 0, false>, attn_fwd_kernel<64, 1, false>, attn_fwd_kernel<64, 2, false>,
+       attn_fwd_kernel<64, 1, true>, attn_fwd_kernel<64, 2, true>},
+      {attn_fwd_kernel<128, 0, false>, attn_fwd_kernel<128, 1, false>, attn_fwd_kernel<128, 2, false>,
+       attn_fwd_kernel<128, 1, true>, attn_fwd_kernel<128, 2, true>}};
+  int kind = intra ? 0 : (p.window > 0 ? 2 : 1);
+  if (a.last_stream && !intra) kind += 2;
   hipLaunchKernelGGL(kKernels[a.d == 128][kind], grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

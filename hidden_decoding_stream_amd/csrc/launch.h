@@ -25,6 +25,7 @@ struct FwdArgs {
   int32_t mode;
   int64_t window;
   float scale;
+  bool last_stream;   // queries: stream n-1 of each token only, q/o [batch][L][hq][d]
 };
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream);
 

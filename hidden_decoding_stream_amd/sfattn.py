@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.sf_attn_fwd.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                               c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32, c.c_int32,
                               c.c_int32, c.c_int64, c.c_float, c.c_void_p]
+    L.sf_attn_fwd_last_stream.restype = c.c_int
+    L.sf_attn_fwd_last_stream.argtypes = L.sf_attn_fwd.argtypes
     L.sf_attn_decode_workspace_bytes.restype = c.c_size_t
     L.sf_attn_decode_workspace_bytes.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32,
                                                  c.c_int32, c.c_int32, c.c_int64, c.c_int32]
@@ -152,6 +154,31 @@ def sf_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode, n: int,
     _check(lib().sf_attn_fwd(_dev(q, "q", bf), _dev(k, "k", bf), _dev(v, "v", bf), _dev(out, "out", bf),
                              lse_ptr, B, n, S // n, hq, hkv, d, _mode(mode), int(window), float(scale),
                              _stream(stream)))
+    return (out, lse) if want_lse else out
+
+
+def sf_attn_fwd_last_stream(q_last: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode, n: int,
+                            window: int = 0, scale: float | None = None, out: torch.Tensor | None = None,
+                            lse: torch.Tensor | bool | None = None, stream=None):
+    """Attention of the last stream's queries only. q_last [B][L][hq][d] (row i
+    = stream n-1 of token i), k/v [B][n*L][hkv][d], bf16. Returns out
+    [B][L][hq][d], or (out, lse) when lse is True or a float32 [B][hq][L] tensor."""
+    B, L, hq, d = q_last.shape
+    hkv = k.shape[2]
+    if k.shape != (B, n * L, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B][n*L][hkv][d] matching q_last")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q_last)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, hq, L), dtype=torch.float32, device=q_last.device)
+    lse_ptr = _dev(lse, "lse", torch.float32) if want_lse else None
+    bf = torch.bfloat16
+    _check(lib().sf_attn_fwd_last_stream(_dev(q_last, "q_last", bf), _dev(k, "k", bf), _dev(v, "v", bf),
+                                         _dev(out, "out", bf), lse_ptr, B, n, L, hq, hkv, d, _mode(mode),
+                                         int(window), float(scale), _stream(stream)))
     return (out, lse) if want_lse else out
 
 

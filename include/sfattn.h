@@ -103,6 +103,24 @@ sf_status sf_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
                       int32_t mode, int64_t window, float scale, hipStream_t stream);
 
+/* Attention for the last stream's queries only: for each token i, the query
+ * of stream n-1 at expanded position i*n + n-1 attends to the keys its mode
+ * admits there, exactly the rows i*n + n-1 of sf_attn_fwd with the same K, V,
+ * mode and window, at about 1/n of the work. Under the cross masks that is
+ * every stream's earlier positions; under SF_INTRA stream n-1's own tokens.
+ * This is the attention of layers that only the final stream passes through
+ * ([HD-tahou] 规模化落地的工程优化: with the KV mirror only the last stream
+ * goes through the mirrored layers; 中间流的作用验证: the final stream reads
+ * the intermediate streams).
+ *   q_last, o_last : bf16 [batch][L][hq][d], row i = stream n-1 of token i.
+ *   k, v           : bf16 [batch][n*L][hkv][d], every stream (as sf_attn_fwd).
+ *   lse            : fp32 [batch][hq][L] or NULL.
+ * Other arguments, errors and the supported set as for sf_attn_fwd, with at
+ * most 2^30 elements in q_last and in k. */
+sf_status sf_attn_fwd_last_stream(const void* q_last, const void* k, const void* v, void* o_last, float* lse,
+                                  int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
+                                  int32_t mode, int64_t window, float scale, hipStream_t stream);
+
 /* Bytes of device workspace sf_attn_decode needs for these arguments (0 if the
  * arguments are invalid or the problem is empty). num_splits as for
  * sf_attn_decode; the result depends on nothing else. */

@@ -170,6 +170,27 @@ def attn_fwd(q, k, v, mode: str, n: int, window: int | None = None, scale: float
     return (o, lse) if with_lse else o
 
 
+def attn_fwd_last_stream(q_last, k, v, mode: str, n: int, window: int | None = None,
+                         scale: float | None = None, with_lse: bool = False):
+    """Attention for the queries of the last stream only.
+
+    [HD-tahou] 规模化落地的工程优化 (KV mirror: only the final stream passes
+    through the mirrored layers) and 中间流的作用验证 (the final stream reads
+    the intermediate streams): for token i the query is stream n-1, at
+    expanded position i*n + n-1, and it attends under the same masks as every
+    other position. So the result is rows i*n + n-1 of :func:`attn_fwd`.
+
+    q_last: [B][L][Hq][D] (row i = stream n-1 of token i); k, v:
+    [B][n*L][Hkv][D]. Returns o [B][L][Hq][D] (and lse [B][Hq][L]).
+    """
+    q_last = np.asarray(q_last, dtype=np.float64)
+    B, L, Hq, D = q_last.shape
+    q = np.zeros((B, n * L, Hq, D))
+    rows = np.arange(L) * n + (n - 1)
+    q[:, rows] = q_last
+    return attn_fwd(q, k, v, mode, n, window=window, scale=scale, rows=rows, with_lse=with_lse)
+
+
 def decode(q_new, k_cache, v_cache, T: int, mode: str, window: int | None = None,
            scale: float | None = None):
     """One decode step: the n stream queries of token T-1 in one pass.

@@ -313,6 +313,41 @@ def pin_rows_subset(orc):
         assert np.allclose(full[:, rows], sub, atol=1e-14, rtol=0)
 
 
+def pin_last_stream(orc):
+    """Last-stream queries (stream n-1 of each token) against torch SDPA and a
+    pure-Python brute force, both stated in (token, stream) terms: under
+    cross_full the query of token i sees every stream of tokens 0..i; under
+    intra it is causal attention over stream n-1 alone; under cross_window the
+    (token, stream) window predicate."""
+    rng = _rng(11)
+    n, L, B, Hq, Hkv, D = 3, 5, 2, 4, 2, 4
+    G = Hq // Hkv
+    ql = _bf16ish(rng, (B, L, Hq, D))
+    # K/V listed as (token, stream) pairs in token-major order
+    ts = [(t, s) for t in range(L) for s in range(n)]
+    k, v = (_bf16ish(rng, (B, len(ts), Hkv, D)) for _ in range(2))
+    scale = 0.45
+    o = orc.attn_fwd_last_stream(ql, k, v, "cross_full", n, scale=scale)
+    for b in range(B):
+        for h in range(Hq):
+            allow = torch.tensor([[tk <= i for (tk, _) in ts] for i in range(L)])
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(ql[b, :, h])[None], torch.from_numpy(k[b, :, h // G])[None],
+                torch.from_numpy(v[b, :, h // G])[None], attn_mask=allow[None], scale=scale)[0].numpy()
+            assert np.allclose(o[b, :, h], ref, atol=1e-12), ("cross_full", b, h)
+    o = orc.attn_fwd_last_stream(ql, k, v, "intra", n, scale=scale)
+    last = [j for j, (_, sk) in enumerate(ts) if sk == n - 1]
+    for b in range(B):
+        ref = _sdpa_causal(ql[b, :, ::G], k[b, last], v[b, last], scale)    # heads h = 0, G, 2G, ...
+        assert np.allclose(o[b, :, ::G], ref, atol=1e-12), ("intra", b)
+    W = 4
+    o = orc.attn_fwd_last_stream(ql, k, v, "cross_window", n, window=W, scale=scale)
+    for h in range(Hq):
+        ok = lambda i, j: allowed_ts("cross_window", n, i, n - 1, ts[j][0], ts[j][1], W)  # noqa: E731
+        ref, _ = _py_attention(ql[0, :, h].tolist(), k[0, :, h // G].tolist(), v[0, :, h // G].tolist(), scale, ok)
+        assert np.allclose(o[0, :, h], np.array(ref), atol=1e-12), ("cross_window", h)
+
+
 ALL_PINS = [
     pin_interleave_golden,
     pin_interleave_bruteforce,
@@ -328,5 +363,6 @@ ALL_PINS = [
     pin_pure_python_bruteforce,
     pin_stream_permutation_equivariance,
     pin_decode_bruteforce,
+    pin_last_stream,
     pin_rows_subset,
 ]

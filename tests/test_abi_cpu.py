@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"sf_interleave", "sf_attn_fwd", "sf_attn_decode", "sf_attn_decode_workspace_bytes",
-            "sf_abi_version", "sf_last_error"} <= set(names)
+    assert {"sf_interleave", "sf_attn_fwd", "sf_attn_fwd_last_stream", "sf_attn_decode",
+            "sf_attn_decode_workspace_bytes", "sf_abi_version", "sf_last_error"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -41,8 +41,9 @@ def test_abi_version():
 
 
 def fwd(q=P, k=P2, v=P3, o=P4, lse=None, batch=1, n=4, Lt=64, hq=4, hkv=4, d=64, mode=1, window=0,
-        scale=0.125):
-    return L.sf_attn_fwd(q, k, v, o, lse, batch, n, Lt, hq, hkv, d, mode, window, scale, None)
+        scale=0.125, last=False):
+    f = L.sf_attn_fwd_last_stream if last else L.sf_attn_fwd
+    return f(q, k, v, o, lse, batch, n, Lt, hq, hkv, d, mode, window, scale, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -65,15 +66,18 @@ def fwd(q=P, k=P2, v=P3, o=P4, lse=None, batch=1, n=4, Lt=64, hq=4, hkv=4, d=64,
     (dict(o=P), B.SF_ERR_INVALID),                       # o aliases q
     (dict(batch=1 << 20, Lt=1 << 20), B.SF_ERR_UNSUPPORTED),  # beyond 2^30 elements
     (dict(batch=1 << 40, Lt=1 << 40), B.SF_ERR_INVALID),      # int64 overflow
+    (dict(n=1 << 10, Lt=1 << 14), B.SF_ERR_UNSUPPORTED),      # k beyond 2^30 elements
 ])
-def test_fwd_rejects(kw, status):
-    assert fwd(**kw) == status
+@pytest.mark.parametrize("last", [False, True], ids=["fwd", "last_stream"])
+def test_fwd_rejects(kw, status, last):
+    assert fwd(**kw, last=last) == status
     assert sfa.sf_last_error() != ""
 
 
 @pytest.mark.parametrize("kw", [dict(batch=0), dict(Lt=0), dict(batch=0, q=None, k=None, v=None, o=None)])
-def test_fwd_empty_is_noop(kw):
-    assert fwd(**kw) == B.SF_OK
+@pytest.mark.parametrize("last", [False, True], ids=["fwd", "last_stream"])
+def test_fwd_empty_is_noop(kw, last):
+    assert fwd(**kw, last=last) == B.SF_OK
     assert sfa.sf_last_error() == ""
 
 

@@ -40,3 +40,12 @@ def test_headline_numbers():
     assert C.prefill_pairs("intra", 4, 8192) == 134_234_112
     # decode cache: 2 * n * T * hkv * d * 2 bytes per batch element
     assert C.decode_bytes("cross_full", 4, 8192, 1, 32, 8, 128) == 134_217_728 + 2 * 4 * 32 * 128 * 2
+
+
+@pytest.mark.parametrize("mode,W", [("intra", None), ("cross_full", None), ("cross_window", 7), ("cross_window", 1),
+                                    ("cross_window", 400)])
+@pytest.mark.parametrize("n,L", [(4, 9), (3, 17), (1, 12)])
+def test_last_stream_pairs_match_oracle_mask(mode, W, n, L):
+    rows = np.arange(L) * n + (n - 1)
+    want = int(orc.mask(mode, n, L, W, rows).sum())
+    assert C.last_stream_pairs(mode, n, L, W or 0) == want

@@ -33,6 +33,8 @@ MUTANTS = {
     "lse_no_max": ("lse = m[:, 0] + np.log(den[:, 0])", "lse = np.log(den[:, 0])"),
     # decode queries one position too early
     "decode_rows_shift": ("rows = (T - 1) * n + np.arange(n)", "rows = (T - 1) * n + np.arange(n) - 1"),
+    # last-stream queries placed at stream 0 instead of stream n-1
+    "last_stream_at_stream0": ("rows = np.arange(L) * n + (n - 1)", "rows = np.arange(L) * n"),
     # decode reads one token too many from the cache
     "decode_reads_future": ("[:, :, :T]\n    vc", "[:, :, :T + 1]\n    vc"),
 }
