@@ -51,6 +51,54 @@ def deinterleave(x: np.ndarray, n: int) -> np.ndarray:
     return np.stack([x[:, k::n] for k in range(n)])
 
 
+def expand_embed(ids: np.ndarray, tables: np.ndarray) -> np.ndarray:
+    """The expanded sequence's input rows, straight from the n embedding tables.
+
+    [HD-tahou] 隐式序列缩放的技术细节, step 1: with n copies of the vocabulary
+    embedding, stream k's representation of token i is row ids[i] of table k,
+    and it is placed at expanded position (i-1)n+k (1-indexed).
+
+    ids: [B][L] integers; tables: [n][vocab][...]. Returns [B][n*L][...].
+    An id outside [0, vocab) gives a row of zeros (the kernel's documented
+    behaviour; the pages do not consider invalid ids).
+    """
+    ids = np.asarray(ids)
+    tables = np.asarray(tables)
+    n, vocab = tables.shape[:2]
+    B, L = ids.shape
+    per_stream = np.zeros((n, B, L) + tables.shape[2:], dtype=tables.dtype)
+    valid = (ids >= 0) & (ids < vocab)
+    for k in range(n):
+        per_stream[k][valid] = tables[k][ids[valid]]
+    return interleave(per_stream)
+
+
+def rope(x: np.ndarray, base: float, pos0: int = 0) -> np.ndarray:
+    """Rotary position encoding at continuous expanded positions (float64).
+
+    [HD-tahou] 隐式序列缩放的技术细节, step 2: the expanded sequence runs under
+    a continuous position encoding, so row s of the expanded sequence has
+    position pos0 + s: the streams of a token take consecutive positions. The
+    page does not name the encoding; the rotary encoding in its rotate-half
+    form is taken: for j < d/2, with theta_j = base^(-2j/d) and angle
+    a = position * theta_j,
+        y[j]       = x[j] cos a - x[j + d/2] sin a
+        y[j + d/2] = x[j + d/2] cos a + x[j] sin a.
+
+    x: [B][S][H][d]. Returns float64 [B][S][H][d].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    pos = pos0 + np.arange(x.shape[1], dtype=np.float64)
+    theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = pos[:, None] * theta[None, :]                    # [S][d/2]
+    c = np.cos(ang)[None, :, None, :]
+    s = np.sin(ang)[None, :, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
 # ---------------------------------------------------------------------------
 # Masks
 # ---------------------------------------------------------------------------

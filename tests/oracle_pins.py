@@ -348,6 +348,50 @@ def pin_last_stream(orc):
         assert np.allclose(o[0, :, h], np.array(ref), atol=1e-12), ("cross_window", h)
 
 
+def pin_expand_embed(orc):
+    """Each output row against the page's 1-indexed placement, evaluated with
+    explicit loops; ids outside the vocabulary give zero rows."""
+    rng = _rng(12)
+    n, B, L, vocab, R = 3, 2, 5, 7, 4
+    tables = rng.integers(-1000, 1000, size=(n, vocab, R))
+    ids = rng.integers(0, vocab, size=(B, L))
+    ids[1, 2] = vocab          # out of range
+    ids[0, 4] = -1             # out of range
+    out = orc.expand_embed(ids, tables)
+    assert out.shape == (B, n * L, R)
+    for b in range(B):
+        for i1 in range(1, L + 1):             # 1-indexed token
+            for k1 in range(1, n + 1):         # 1-indexed stream
+                pos = (i1 - 1) * n + k1 - 1    # the page's (i-1)n+k, made 0-indexed
+                tok = ids[b, i1 - 1]
+                want = tables[k1 - 1, tok] if 0 <= tok < vocab else np.zeros(R, dtype=tables.dtype)
+                assert np.array_equal(out[b, pos], want), (b, i1, k1)
+
+
+def pin_rope(orc):
+    """Rotate-half rotary encoding against its complex-number statement
+    (z_j = x_j + i x_{j+d/2} times e^{i p theta_j}), the identity at position
+    0, norm preservation, and the relative-position property: shifting every
+    position by the same amount leaves all q.k products unchanged."""
+    rng = _rng(13)
+    B, S, H, d, base = 2, 9, 3, 8, 500.0
+    x = rng.standard_normal((B, S, H, d))
+    y = orc.rope(x, base, pos0=5)
+    half = d // 2
+    z = x[..., :half] + 1j * x[..., half:]
+    theta = np.array([base ** (-(2 * j) / d) for j in range(half)])
+    for s_ in range(S):
+        w = z[:, s_] * np.exp(1j * (5 + s_) * theta)
+        assert np.allclose(y[:, s_, :, :half], w.real, atol=1e-12)
+        assert np.allclose(y[:, s_, :, half:], w.imag, atol=1e-12)
+    assert np.allclose(orc.rope(x[:, :1], base, pos0=0), x[:, :1], atol=0)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), atol=1e-12)
+    q, k = x, rng.standard_normal((B, S, H, d))
+    dots = np.einsum("bshd,bthd->bhst", orc.rope(q, base, 0), orc.rope(k, base, 0))
+    dots_shift = np.einsum("bshd,bthd->bhst", orc.rope(q, base, 37), orc.rope(k, base, 37))
+    assert np.allclose(dots, dots_shift, atol=1e-10)
+
+
 ALL_PINS = [
     pin_interleave_golden,
     pin_interleave_bruteforce,
@@ -364,5 +408,7 @@ ALL_PINS = [
     pin_stream_permutation_equivariance,
     pin_decode_bruteforce,
     pin_last_stream,
+    pin_expand_embed,
+    pin_rope,
     pin_rows_subset,
 ]

@@ -35,6 +35,13 @@ MUTANTS = {
     "decode_rows_shift": ("rows = (T - 1) * n + np.arange(n)", "rows = (T - 1) * n + np.arange(n) - 1"),
     # last-stream queries placed at stream 0 instead of stream n-1
     "last_stream_at_stream0": ("rows = np.arange(L) * n + (n - 1)", "rows = np.arange(L) * n"),
+    # embedding rows taken from table 0 for every stream
+    "embed_one_table": ("per_stream[k][valid] = tables[k][ids[valid]]", "per_stream[k][valid] = tables[0][ids[valid]]"),
+    # rotation in the wrong direction
+    "rope_sign": ("[a * c - b * s, b * c + a * s]", "[a * c + b * s, b * c - a * s]"),
+    # rotary frequencies with exponent 2j/half instead of 2j/d
+    "rope_freq": ("theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)",
+                  "theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / half)"),
     # decode reads one token too many from the cache
     "decode_reads_future": ("[:, :, :T]\n    vc", "[:, :, :T + 1]\n    vc"),
 }
