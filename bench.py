@@ -224,6 +224,7 @@ def main():
     }
 
     line["last_stream"] = last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream)
+    line["front_end"] = front_end_timing(torch, sfa, C, n, L, B, hq, d, dev, stream)
     if not args.no_decode_sweep:
         line["decode"] = decode_sweep(torch, sfa, C, I, dev)
     if not args.no_cpu_baseline:
@@ -253,6 +254,46 @@ def last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream, re
         out[mode] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "useful_flop": fl}
         print(f"[bench] last-stream {mode}: {ms:.3f} ms, {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+    return out
+
+
+def front_end_timing(torch, sfa, C, n, L, B, hq, d, dev, stream, vocab=32000, reps=10):
+    """The expansion front-end at the 32k workload: the gather of the n
+    embedding tables (vocab x hq*d bf16 each) into the expanded sequence, and
+    the rotary encoding of Q in place. HBM GB/s of their algorithmic bytes."""
+    hidden = hq * d
+    g = torch.Generator(device=dev).manual_seed(1005)
+    tables = torch.randn((n, vocab, hidden), generator=g, device=dev).to(torch.bfloat16)
+    ids = torch.randint(0, vocab, (B, L), generator=g, device=dev, dtype=torch.int32)
+    x = torch.empty((B, n * L, hidden), dtype=torch.bfloat16, device=dev)
+    q = torch.randn((B, n * L, hq, d), generator=g, device=dev).to(torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        pairs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in pairs) / reps
+
+    out = {}
+    ms = timed(lambda: sfa.sf_expand_embed(ids, tables, out=x))
+    by = C.expand_embed_bytes(B, n, L, hidden * 2)
+    out["expand_embed"] = {"us": round(ms * 1e3, 1), "GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(by / (ms * 1e-3) / 8e12, 4), "bytes": by}
+    ms = timed(lambda: sfa.sf_rope(q, base=10000.0))
+    by = C.rope_bytes(q.numel() * 2)
+    out["rope_q"] = {"us": round(ms * 1e3, 1), "GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(by / (ms * 1e-3) / 8e12, 4), "bytes": by}
+    for k2, v2 in out.items():
+        print(f"[bench] {k2}: {v2['us']} us, {v2['GBps']} GB/s", file=sys.stderr, flush=True)
+    del tables, x, q
+    torch.cuda.empty_cache()
     return out
 
 

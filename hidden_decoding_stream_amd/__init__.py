@@ -13,6 +13,8 @@ from .sfattn import (  # noqa: F401
     sf_attn_decode_workspace_bytes,
     sf_attn_fwd,
     sf_attn_fwd_last_stream,
+    sf_expand_embed,
     sf_interleave,
     sf_last_error,
+    sf_rope,
 )

@@ -79,3 +79,14 @@ def decode_bytes(mode: str, n: int, T: int, batch: int, hq: int, hkv: int, d: in
 def interleave_bytes(tensor_bytes: int) -> int:
     """A copy reads and writes every byte once."""
     return 2 * tensor_bytes
+
+
+def expand_embed_bytes(batch: int, n: int, L: int, row_bytes: int) -> int:
+    """Every output row is read once from its table and written once, plus
+    the token ids."""
+    return 2 * batch * n * L * row_bytes + 4 * batch * L
+
+
+def rope_bytes(tensor_bytes: int) -> int:
+    """In place: the tensor is read and written once."""
+    return 2 * tensor_bytes

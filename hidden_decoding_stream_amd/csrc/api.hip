@@ -105,6 +105,49 @@ sf_status sf_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_
                        "sf_interleave launch");
 }
 
+sf_status sf_expand_embed(const int32_t* ids, const void* tables, void* out, int64_t batch, int32_t n, int64_t L,
+                          int64_t vocab, int64_t row_bytes, hipStream_t stream) {
+  if (n < 1) return fail(SF_ERR_INVALID, "n must be >= 1 (got %d)", n);
+  if (L < 0 || batch < 0) return fail(SF_ERR_INVALID, "L and batch must be >= 0");
+  if (vocab < 1) return fail(SF_ERR_INVALID, "vocab must be >= 1");
+  if (row_bytes < 1) return fail(SF_ERR_INVALID, "row_bytes must be >= 1");
+  if (L == 0 || batch == 0) return ok();
+  if (!ids || !tables || !out) return fail(SF_ERR_INVALID, "null ids, tables or out");
+  int64_t ob = row_bytes, tb = row_bytes, ib = batch;
+  if (!mul_ok(ob, n) || !mul_ok(ob, L) || !mul_ok(ob, batch) || !mul_ok(tb, n) || !mul_ok(tb, vocab) ||
+      !mul_ok(ib, L) || !mul_ok(ib, 4))
+    return fail(SF_ERR_INVALID, "tensor size overflows int64");
+  if (overlaps(out, ob, tables, tb) || overlaps(out, ob, ids, ib)) return fail(SF_ERR_INVALID, "out overlaps an input");
+  if (!aligned(ids, 4)) return fail(SF_ERR_UNSUPPORTED, "ids must be 4-byte aligned");
+  const uint64_t align = uint64_t(reinterpret_cast<uintptr_t>(tables)) | uint64_t(reinterpret_cast<uintptr_t>(out)) |
+                         uint64_t(row_bytes);
+  const int vb = (align & 15) == 0 ? 16 : (align & 7) == 0 ? 8 : (align & 3) == 0 ? 4 : (align & 1) == 0 ? 2 : 1;
+  if (uint64_t(ob) / uint64_t(vb) >= (uint64_t(1) << 32) || uint64_t(n) * uint64_t(L) >= (uint64_t(1) << 32) ||
+      row_bytes / vb >= (int64_t(1) << 32))
+    return fail(SF_ERR_UNSUPPORTED, "expand_embed output of %lld bytes exceeds 2^32 vectors of %d bytes",
+                (long long)ob, vb);
+  return device_status(sfa::launch_expand_embed(ids, tables, out, batch, n, L, vocab, row_bytes, vb, stream),
+                       "sf_expand_embed launch");
+}
+
+sf_status sf_rope(void* x, int64_t batch, int64_t S, int32_t heads, int32_t d, float base, int64_t pos0,
+                  hipStream_t stream) {
+  if (batch < 0 || S < 0) return fail(SF_ERR_INVALID, "batch and S must be >= 0");
+  if (heads < 1) return fail(SF_ERR_INVALID, "heads must be >= 1");
+  if (d < 2 || d % 2) return fail(SF_ERR_INVALID, "d must be even and >= 2 (got %d)", d);
+  if (!(std::isfinite(base) && base > 1.0f)) return fail(SF_ERR_INVALID, "base must be finite and > 1");
+  if (pos0 < 0) return fail(SF_ERR_INVALID, "pos0 must be >= 0");
+  if (d % 8 || d > 256) return fail(SF_ERR_UNSUPPORTED, "d must be a multiple of 8 and at most 256 (got %d)", d);
+  if (batch == 0 || S == 0) return ok();
+  if (!x) return fail(SF_ERR_INVALID, "null x");
+  int64_t th = batch;
+  if (!mul_ok(th, S) || !mul_ok(th, heads) || !mul_ok(th, d / 8)) return fail(SF_ERR_INVALID, "tensor size overflows int64");
+  if (th >= (int64_t(1) << 32) || S >= (int64_t(1) << 32) || pos0 + S > (int64_t(1) << 40))
+    return fail(SF_ERR_UNSUPPORTED, "rope problem too large");
+  if (!aligned(x, 8)) return fail(SF_ERR_UNSUPPORTED, "x must be 8-byte aligned");
+  return device_status(sfa::launch_rope(x, batch, S, heads, d, double(base), pos0, stream), "sf_rope launch");
+}
+
 }  // extern "C"
 
 namespace {

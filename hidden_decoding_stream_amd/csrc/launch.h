@@ -12,6 +12,11 @@ namespace sfa {
 hipError_t launch_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_t batch,
                              int64_t row_bytes, int inverse, hipStream_t stream);
 
+hipError_t launch_expand_embed(const int32_t* ids, const void* tables, void* out, int64_t batch, int32_t n,
+                               int64_t L, int64_t vocab, int64_t row_bytes, int vb, hipStream_t stream);
+hipError_t launch_rope(void* x, int64_t batch, int64_t S, int32_t heads, int32_t d, double base, int64_t pos0,
+                       hipStream_t stream);
+
 struct FwdArgs {
   const void* q;
   const void* k;

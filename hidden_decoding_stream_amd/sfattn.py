@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
     L.sf_attn_fwd.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                               c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32, c.c_int32,
                               c.c_int32, c.c_int64, c.c_float, c.c_void_p]
+    L.sf_expand_embed.restype = c.c_int
+    L.sf_expand_embed.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_int32, c.c_int64, c.c_int64,
+                                  c.c_int64, c.c_void_p]
+    L.sf_rope.restype = c.c_int
+    L.sf_rope.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int32, c.c_int32, c.c_float, c.c_int64, c.c_void_p]
     L.sf_attn_fwd_last_stream.restype = c.c_int
     L.sf_attn_fwd_last_stream.argtypes = L.sf_attn_fwd.argtypes
     L.sf_attn_decode_workspace_bytes.restype = c.c_size_t
@@ -129,6 +134,32 @@ def sf_interleave(src: torch.Tensor, n: int, inverse: bool = False, out: torch.T
     _check(lib().sf_interleave(_dev(src, "src"), _dev(out, "out"), n, L, B, row_bytes, int(inverse),
                                _stream(stream)))
     return out
+
+
+def sf_expand_embed(ids: torch.Tensor, tables: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """Gather and interleave: ids int32 [B][L], tables [n][vocab][...] (any
+    dtype) -> out [B][n*L][...] with out[b][i*n+k] = tables[k][ids[b][i]]
+    (zeros for an id outside the vocabulary)."""
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise ValueError("ids must be an int32 [B][L] tensor")
+    B, L = ids.shape
+    n, vocab = tables.shape[:2]
+    row = tables[0, 0].numel() * tables.element_size()
+    if out is None:
+        out = torch.empty((B, n * L) + tuple(tables.shape[2:]), dtype=tables.dtype, device=tables.device)
+    if out.numel() * out.element_size() != B * n * L * row:
+        raise ValueError("out has the wrong size")
+    _check(lib().sf_expand_embed(_dev(ids, "ids"), _dev(tables, "tables"), _dev(out, "out"), B, n, L, vocab, row,
+                                 _stream(stream)))
+    return out
+
+
+def sf_rope(x: torch.Tensor, base: float = 10000.0, pos0: int = 0, stream=None) -> torch.Tensor:
+    """Rotary encoding in place at continuous positions pos0 + s: x bf16
+    [B][S][heads][d]. Returns x."""
+    B, S, H, d = x.shape
+    _check(lib().sf_rope(_dev(x, "x", torch.bfloat16), B, S, H, d, float(base), int(pos0), _stream(stream)))
+    return x
 
 
 def sf_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode, n: int, window: int = 0,

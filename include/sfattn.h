@@ -86,6 +86,34 @@ const char* sf_last_error(void);
 sf_status sf_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_t batch,
                         int64_t row_bytes, int32_t inverse, hipStream_t stream);
 
+/* Expansion of the input: with n copies of the vocabulary embedding, stream
+ * k's representation of token i (row ids[b][i] of table k) is placed at
+ * expanded position i*n + k ([HD-tahou] 隐式序列缩放的技术细节, step 1, there
+ * 1-based as (i-1)n+k). One pass gathers and interleaves:
+ *   out[b][i*n + k][:] = tables[k][ids[b][i]][:].
+ *   ids    : int32 [batch][L], device.
+ *   tables : [n][vocab][row_bytes] bytes (any dtype), device.
+ *   out    : [batch][n*L][row_bytes], device; must not overlap the inputs.
+ * An id outside [0, vocab) gives a row of zeros. Supported: at most 2^32
+ * vectors in out (vectors of 16, 8, 4, 2 or 1 bytes, the widest the row size
+ * and the pointers allow); ids 4-byte aligned. */
+sf_status sf_expand_embed(const int32_t* ids, const void* tables, void* out, int64_t batch, int32_t n, int64_t L,
+                          int64_t vocab, int64_t row_bytes, hipStream_t stream);
+
+/* Rotary position encoding, in place, at continuous expanded positions: row s
+ * of the expanded sequence has position pos0 + s ([HD-tahou]
+ * 隐式序列缩放的技术细节, step 2: the expanded sequence runs under a
+ * continuous position encoding, so a token's streams take consecutive
+ * positions). The page does not name the encoding; the rotary encoding in its
+ * rotate-half form is used: for j < d/2, with a = (pos0 + s) * base^(-2j/d),
+ *   y[j] = x[j] cos a - x[j + d/2] sin a,   y[j + d/2] = x[j + d/2] cos a + x[j] sin a.
+ * The angle is formed and reduced in fp64, sin/cos and the rotation in fp32,
+ * the result rounded to bf16 once.
+ *   x : bf16 [batch][S][heads][d], 8-byte aligned (Q or K before attention).
+ * Supported: d a multiple of 8, at most 256; base > 1. */
+sf_status sf_rope(void* x, int64_t batch, int64_t S, int32_t heads, int32_t d, float base, int64_t pos0,
+                  hipStream_t stream);
+
 /* Prefill attention over the expanded sequence, one of the three masks above,
  * with grouped-query attention ([HD-aiflow] "Tencent's ecosystem first scaling
  * strategy"): query head h reads key/value head h / (hq/hkv).

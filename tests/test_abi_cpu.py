@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"sf_interleave", "sf_attn_fwd", "sf_attn_fwd_last_stream", "sf_attn_decode",
-            "sf_attn_decode_workspace_bytes", "sf_abi_version", "sf_last_error"} <= set(names)
+    assert {"sf_interleave", "sf_expand_embed", "sf_rope", "sf_attn_fwd", "sf_attn_fwd_last_stream",
+            "sf_attn_decode", "sf_attn_decode_workspace_bytes", "sf_abi_version", "sf_last_error"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -144,3 +144,49 @@ def test_workspace_query():
     assert sfa.sf_attn_decode_workspace_bytes(0, 4, 8192, 32, 8, 128, "intra") == 0
     assert sfa.sf_attn_decode_workspace_bytes(1, 4, 0, 32, 8, 128, "intra") == 0
     assert sfa.sf_attn_decode_workspace_bytes(1, 4, 16, 32, 8, 96, "intra") == 0
+
+
+def emb(ids=P, tables=P2, out=P3, batch=2, n=4, Lt=16, vocab=100, row=64):
+    return L.sf_expand_embed(ids, tables, out, batch, n, Lt, vocab, row, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), B.SF_ERR_INVALID),
+    (dict(Lt=-1), B.SF_ERR_INVALID),
+    (dict(vocab=0), B.SF_ERR_INVALID),
+    (dict(row=0), B.SF_ERR_INVALID),
+    (dict(ids=None), B.SF_ERR_INVALID),
+    (dict(out=ctypes.c_void_p(0x40000000 + 64)), B.SF_ERR_INVALID),     # out overlaps tables
+    (dict(ids=ctypes.c_void_p(0x10002)), B.SF_ERR_UNSUPPORTED),         # ids misaligned
+    (dict(row=1 << 40, Lt=1 << 30), B.SF_ERR_INVALID),                 # int64 overflow
+    (dict(row=1 << 30, Lt=1 << 10, n=64, out=ctypes.c_void_p(1 << 50)), B.SF_ERR_UNSUPPORTED),
+])
+def test_expand_embed_rejects(kw, status):
+    assert emb(**kw) == status
+    assert sfa.sf_last_error() != ""
+
+
+def test_expand_embed_empty_is_noop():
+    assert emb(batch=0) == B.SF_OK
+    assert emb(Lt=0, ids=None, tables=None, out=None) == B.SF_OK
+
+
+def rope(x=P, batch=1, S=16, heads=4, d=128, base=10000.0, pos0=0):
+    return L.sf_rope(x, batch, S, heads, d, base, pos0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), B.SF_ERR_INVALID),
+    (dict(heads=0), B.SF_ERR_INVALID),
+    (dict(d=7), B.SF_ERR_INVALID),
+    (dict(base=1.0), B.SF_ERR_INVALID),
+    (dict(base=float("nan")), B.SF_ERR_INVALID),
+    (dict(pos0=-1), B.SF_ERR_INVALID),
+    (dict(d=12), B.SF_ERR_UNSUPPORTED),
+    (dict(d=512), B.SF_ERR_UNSUPPORTED),
+    (dict(x=None), B.SF_ERR_INVALID),
+    (dict(x=ctypes.c_void_p(0x10004)), B.SF_ERR_UNSUPPORTED),
+])
+def test_rope_rejects(kw, status):
+    assert rope(**kw) == status
+    assert sfa.sf_last_error() != ""

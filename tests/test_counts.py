@@ -49,3 +49,9 @@ def test_last_stream_pairs_match_oracle_mask(mode, W, n, L):
     rows = np.arange(L) * n + (n - 1)
     want = int(orc.mask(mode, n, L, W, rows).sum())
     assert C.last_stream_pairs(mode, n, L, W or 0) == want
+
+
+def test_front_end_bytes():
+    # n=4 tables, L=8192 tokens, 8 KiB rows: read + write of 32768 rows, plus the ids
+    assert C.expand_embed_bytes(1, 4, 8192, 8192) == 2 * 32768 * 8192 + 4 * 8192
+    assert C.rope_bytes(1 << 28) == 1 << 29
