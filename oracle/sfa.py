@@ -239,6 +239,53 @@ def attn_fwd_last_stream(q_last, k, v, mode: str, n: int, window: int | None = N
     return attn_fwd(q, k, v, mode, n, window=window, scale=scale, rows=rows, with_lse=with_lse)
 
 
+def attn_bwd(q, k, v, dout, mode: str, n: int, window: int | None = None, scale: float | None = None,
+             block: int = 512):
+    """Gradients of :func:`attn_fwd` for the loss sum(dout * o), in float64.
+
+    The pages report training step times for the method ([HD-tahou]
+    实验效果与成本分析); training needs the backward of each attention layer.
+    With P the masked softmax of S = scale * Q K^T (rows over admitted keys),
+    O = P V and the upstream gradient dO:
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(dP * P)),
+        dQ = scale dS K,   dK = scale dS^T Q,
+    and under grouped-query attention a key/value head's gradients are the
+    sums over the query heads that read it.
+
+    q, dout: [B][S][Hq][D]; k, v: [B][S][Hkv][D]. Returns (dq, dk, dv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    L = S // n
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, S, block):
+        rr = np.arange(r0, min(S, r0 + block))
+        allowed = mask(mode, n, L, window, rr)
+        for b in range(B):
+            for h in range(Hq):
+                kh = h // G
+                s = float(scale) * (q[b, rr, h] @ k[b, :, kh].T)
+                s = np.where(allowed, s, -np.inf)
+                w = np.exp(s - s.max(axis=1, keepdims=True))
+                pr = w / w.sum(axis=1, keepdims=True)           # P rows, zero where masked
+                do = dout[b, rr, h]
+                dv[b, :, kh] += pr.T @ do
+                dp = do @ v[b, :, kh].T
+                ds = pr * (dp - (dp * pr).sum(axis=1, keepdims=True))
+                dq[b, rr, h] = float(scale) * (ds @ k[b, :, kh])
+                dk[b, :, kh] += float(scale) * (ds.T @ q[b, rr, h])
+    return dq, dk, dv
+
+
 def decode(q_new, k_cache, v_cache, T: int, mode: str, window: int | None = None,
            scale: float | None = None):
     """One decode step: the n stream queries of token T-1 in one pass.

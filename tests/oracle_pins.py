@@ -392,6 +392,53 @@ def pin_rope(orc):
     assert np.allclose(dots, dots_shift, atol=1e-10)
 
 
+def pin_backward(orc):
+    """Gradients against central finite differences of the scalar loss
+    sum(dout * o) (all three masks, GQA), against torch autograd through
+    causal SDPA (cross_full), and GQA against MHA with repeated K/V whose
+    key/value gradients are summed over each group."""
+    rng = _rng(14)
+    n, L, B, Hq, Hkv, D = 2, 3, 1, 4, 2, 3
+    S = n * L
+    q = rng.standard_normal((B, S, Hq, D))
+    k = rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    do = rng.standard_normal((B, S, Hq, D))
+    scale, eps = 0.6, 1e-6
+    for mode, W in (("intra", None), ("cross_full", None), ("cross_window", 3)):
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, mode, n, window=W, scale=scale)
+        loss = lambda q_, k_, v_: float(np.sum(do * orc.attn_fwd(q_, k_, v_, mode, n, window=W, scale=scale)))  # noqa: E731
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert np.allclose(g, num, atol=1e-6), (mode, name)
+    # torch autograd through causal SDPA, one head group at a time
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q[0], k[0], v[0]))
+    G = Hq // Hkv
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.transpose(0, 1), kt.repeat_interleave(G, dim=1).transpose(0, 1),
+        vt.repeat_interleave(G, dim=1).transpose(0, 1), is_causal=True, scale=scale).transpose(0, 1)
+    (o * torch.tensor(do[0])).sum().backward()
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, "cross_full", n, scale=scale)
+    assert np.allclose(dq[0], qt.grad.numpy(), atol=1e-12)
+    assert np.allclose(dk[0], kt.grad.numpy(), atol=1e-12)
+    assert np.allclose(dv[0], vt.grad.numpy(), atol=1e-12)
+    # GQA: repeated K/V as MHA, gradients summed over each group
+    k_rep, v_rep = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+    for mode, W in (("intra", None), ("cross_window", 4)):
+        a = orc.attn_bwd(q, k, v, do, mode, n, window=W, scale=scale)
+        m = orc.attn_bwd(q, k_rep, v_rep, do, mode, n, window=W, scale=scale)
+        assert np.allclose(a[0], m[0], atol=1e-12)
+        assert np.allclose(a[1], m[1].reshape(B, S, Hkv, G, D).sum(axis=3), atol=1e-12)
+        assert np.allclose(a[2], m[2].reshape(B, S, Hkv, G, D).sum(axis=3), atol=1e-12)
+
+
 ALL_PINS = [
     pin_interleave_golden,
     pin_interleave_bruteforce,
@@ -410,5 +457,6 @@ ALL_PINS = [
     pin_last_stream,
     pin_expand_embed,
     pin_rope,
+    pin_backward,
     pin_rows_subset,
 ]

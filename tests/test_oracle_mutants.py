@@ -42,6 +42,11 @@ MUTANTS = {
     # rotary frequencies with exponent 2j/half instead of 2j/d
     "rope_freq": ("theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)",
                   "theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / half)"),
+    # backward: dS without the rowsum correction
+    "bwd_no_rowsum": ("ds = pr * (dp - (dp * pr).sum(axis=1, keepdims=True))", "ds = pr * dp"),
+    # backward: dK built from dP instead of dS
+    "bwd_dk_from_dp": ("dk[b, :, kh] += float(scale) * (ds.T @ q[b, rr, h])",
+                       "dk[b, :, kh] += float(scale) * (dp.T @ q[b, rr, h])"),
     # decode reads one token too many from the cache
     "decode_reads_future": ("[:, :, :T]\n    vc", "[:, :, :T + 1]\n    vc"),
 }
