@@ -225,6 +225,7 @@ def main():
 
     line["last_stream"] = last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream)
     line["front_end"] = front_end_timing(torch, sfa, C, n, L, B, hq, d, dev, stream)
+    line["backward"] = backward_timing(torch, sfa, C, Q, K, V, Oc, n, L, B, hq, hkv, d, scale, dev, stream)
     if not args.no_decode_sweep:
         line["decode"] = decode_sweep(torch, sfa, C, I, dev)
     if not args.no_cpu_baseline:
@@ -294,6 +295,37 @@ def front_end_timing(torch, sfa, C, n, L, B, hq, d, dev, stream, vocab=32000, re
         print(f"[bench] {k2}: {v2['us']} us, {v2['GBps']} GB/s", file=sys.stderr, flush=True)
     del tables, x, q
     torch.cuda.empty_cache()
+    return out
+
+
+def backward_timing(torch, sfa, C, Q, K, V, Oc, n, L, B, hq, hkv, d, scale, dev, stream, reps=5):
+    """sf_attn_bwd (all three of its kernels) on the 32k workload: useful
+    TFLOP/s for cross_full and intra."""
+    g = torch.Generator(device=dev).manual_seed(1053)
+    dout = torch.randn(Q.shape, generator=g, device=dev).to(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    ws = torch.empty(int(sfa.lib().sf_attn_bwd_workspace_bytes(B, n, L, hq, hkv, d, 1, 0)) + 16,
+                     dtype=torch.uint8, device=dev)
+    out = {}
+    for mode in ("cross_full", "intra"):
+        o, lse = sfa.sf_attn_fwd(Q, K, V, mode, n, scale=scale, lse=True)
+        call = lambda: sfa.sf_attn_bwd(Q, K, V, o, dout, lse, mode, n, scale=scale, out=(dq, dk, dv),  # noqa: E731
+                                       workspace=ws)
+        call()
+        pairs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in pairs) / reps
+        fl = C.backward_flops(mode, n, L, B, hq, d)
+        out[mode] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "useful_flop": fl}
+        print(f"[bench] backward {mode}: {ms:.3f} ms, {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del o, lse
     return out
 
 

@@ -9,6 +9,7 @@ from .sfattn import (  # noqa: F401
     SFError,
     lib,
     sf_abi_version,
+    sf_attn_bwd,
     sf_attn_decode,
     sf_attn_decode_workspace_bytes,
     sf_attn_fwd,

@@ -23,7 +23,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 BUILD = ROOT / "_build"
 LIB = PKG / "libsfattn.so"
-SOURCES = ["api.hip", "interleave.hip", "frontend.hip", "attn_fwd.hip", "attn_decode.hip"]
+SOURCES = ["api.hip", "interleave.hip", "frontend.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
 PEAKS_LIB = PKG / "libsfpeaks.so"
 PEAKS_SOURCES = ["peaks.hip"]
 

@@ -90,3 +90,10 @@ def expand_embed_bytes(batch: int, n: int, L: int, row_bytes: int) -> int:
 def rope_bytes(tensor_bytes: int) -> int:
     """In place: the tensor is read and written once."""
     return 2 * tensor_bytes
+
+
+def backward_flops(mode: str, n: int, L: int, batch: int, hq: int, d: int, window: int = 0) -> int:
+    """Useful work of the backward: dV = P^T dO, dP = dO V^T, dQ = dS K and
+    dK = dS^T Q, plus recomputing S = Q K^T: five products of 2*d flops per
+    admitted pair, 2.5 times the forward's."""
+    return 10 * d * prefill_pairs(mode, n, L, window) * batch * hq

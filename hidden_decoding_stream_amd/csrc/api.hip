@@ -204,6 +204,56 @@ sf_status sf_attn_fwd_last_stream(const void* q_last, const void* k, const void*
   return attn_fwd_checked(q_last, k, v, o_last, lse, batch, n, L, hq, hkv, d, mode, window, scale, true, stream);
 }
 
+size_t sf_attn_bwd_workspace_bytes(int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
+                                   int32_t mode, int64_t window) {
+  if (batch <= 0 || L <= 0) return 0;
+  if (check_heads(n, hq, hkv, d, mode, window, 1.0f) != SF_OK) return 0;
+  return sfa::attn_bwd_workspace_bytes(batch, n, L, hq, mode);
+}
+
+sf_status sf_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv,
+                      int32_t d, int32_t mode, int64_t window, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (batch < 0 || L < 0) return fail(SF_ERR_INVALID, "batch and L must be >= 0");
+  sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
+  if (st != SF_OK) return st;
+  if (batch == 0 || L == 0) return ok();
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(SF_ERR_INVALID, "null tensor pointer");
+  int64_t qe = batch, kve = batch;
+  if (!mul_ok(qe, n) || !mul_ok(qe, L) || !mul_ok(qe, hq) || !mul_ok(qe, d) || !mul_ok(kve, n) ||
+      !mul_ok(kve, L) || !mul_ok(kve, hkv) || !mul_ok(kve, d))
+    return fail(SF_ERR_INVALID, "tensor size overflows int64");
+  if (qe > (int64_t(1) << 30))
+    return fail(SF_ERR_UNSUPPORTED, "q has %lld elements; at most 2^30 supported", (long long)qe);
+  for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv)})
+    if (!aligned(ptr, 16)) return fail(SF_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(SF_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
+  const int64_t le = qe / d * 4;   // lse bytes
+  const void* outs[3] = {dq, dk, dv};
+  const int64_t out_bytes[3] = {qe * 2, kve * 2, kve * 2};
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const int64_t in_bytes[6] = {qe * 2, kve * 2, kve * 2, qe * 2, qe * 2, le};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return fail(SF_ERR_INVALID, "an output overlaps an input");
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return fail(SF_ERR_INVALID, "outputs overlap");
+  }
+  const size_t need = sfa::attn_bwd_workspace_bytes(batch, n, L, hq, mode);
+  if (!workspace || workspace_bytes < need)
+    return fail(SF_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(SF_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(workspace, int64_t(need), outs[i], out_bytes[i])) return fail(SF_ERR_INVALID, "workspace overlaps a tensor");
+  for (int j = 0; j < 6; ++j)
+    if (overlaps(workspace, int64_t(need), ins[j], in_bytes[j])) return fail(SF_ERR_INVALID, "workspace overlaps a tensor");
+  sfa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, batch, n, L, hq, hkv, d, mode, window, scale, workspace};
+  return device_status(sfa::launch_attn_bwd(a, stream), "sf_attn_bwd launch");
+}
+
 size_t sf_attn_decode_workspace_bytes(int64_t batch, int32_t n, int64_t T, int32_t hq,
                                       int32_t hkv, int32_t d, int32_t mode, int64_t window,
                                       int32_t num_splits) {

@@ -1,0 +1,663 @@
+// Backward of stream-factorized attention on gfx950 (bf16 MFMA).
+//
+// What is computed: the gradients of the prefill attention for the loss
+// sum(dO * O) (training; the page "微信WeLM提出Hidden Decoding：大模型推理新范式",
+// section 实验效果与成本分析, reports the method's cost as training step
+// times). With S = scale * Q K^T over the admitted keys, P = exp(S - lse),
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
+//   dQ = scale * dS K,  dK = scale * dS^T Q,
+// and under grouped-query attention a key/value head's gradients are the sums
+// over its G query heads. The masks and the virtual sequences (intra: each
+// stream as a strided view) are those of the forward.
+//
+// Three kernels, all deterministic (no atomics):
+// * bwd_prep_kernel: D and lse*log2(e) per query row, into a workspace laid
+//   out by virtual sequence ([B][nseq][hq][Lv][2]) so that a run of queries of
+//   one virtual sequence is contiguous.
+// * bwd_dq_kernel: query-stationary, shaped like the forward. Per 64-key tile
+//   S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS as A operands, Q^T
+//   and dO^T in registers), then P^T = exp2(S^T c - lse2) with the lane's own
+//   lse, dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T, with dS^T taken straight
+//   from the accumulators as the B operand (rows read in the sigma order) and
+//   K^T gathered by transposed LDS reads.
+// * bwd_dkdv_kernel: key-stationary. A wave owns 32 keys (K and V in registers
+//   as B operands); the Q and dO tiles of 64 queries stream through LDS, for
+//   each of the G query heads in turn. S = Q K^T and dP = dO V^T (lane = key
+//   column), P and dS with each register's own query lse / D, then
+//   dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposed reads).
+// Tiles are K-style: rows padded to D+16 elements (the sigma-order 16-byte
+// reads hit distinct bank groups), loaded by buffer->LDS DMA through a
+// 2-stage ring with one bare barrier per tile; transposed reads are asm blocks
+// that wait for their own results (see common.h).
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace sfa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16;
+
+constexpr int kWaves = 4;                 // one wave per SIMD: room for the extra accumulators
+constexpr int kThreads = 64 * kWaves;
+constexpr int BT = 64;                    // rows per staged tile
+constexpr int ST = 2;                     // LDS stages
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+  const u16* q;
+  const u16* k;
+  const u16* v;
+  const u16* o;
+  const u16* dout;
+  const float* lse;   // [B][hq][S], natural log (from the forward)
+  float* lsed;        // [B][nseq][hq][Lv][2]: lse*log2(e), D
+  u16* dq;
+  u16* dk;
+  u16* dv;
+  int32_t batch;
+  int32_t S, Lv, pstride, nseq;
+  int32_t hq, hkv, G, HG, hgroups;
+  int32_t window;     // > 0: cross_window limit; 0: none
+  float c;            // scale * log2(e)
+  float scale;
+  int32_t nqb, nkb;   // query blocks (dQ), key blocks (dK/dV) per virtual sequence
+  int32_t total_q, per_xcd_q, total_k, per_xcd_k;
+  uint32_t q_bytes, kv_bytes, lsed_bytes;
+};
+
+template <int D> struct BTile {
+  static constexpr int ROW = D + 16;                       // padded row (elements)
+  static constexpr int SLOTS = ROW / 8;                    // 16-byte slots per row
+  static constexpr int CH = BT * SLOTS / 64;               // 1 KiB DMA chunks per tile
+  static constexpr int ELEMS = BT * ROW;
+  static_assert(BT * SLOTS % 64 == 0, "tile must be whole KiB chunks");
+};
+
+// 16 transposed reads gathering, for one 32-row block of a padded tile, the
+// A operand X^T (rows d, k = tile rows in the accumulator order of
+// reg_key_offset): output (db*2 + j2)*2 + t holds rows 16h + 4*((2t + j2) ^ h)
+// + e of 32-wide d block db, from base ae[db] (j2 = 0) or ao[db] (j2 = 1)
+// plus an immediate offset of (8t + 4j2) rows. One asm block that waits for
+// its results (a builtin read would wait for every buffer->LDS load in flight).
+template <int D> __device__ __forceinline__ void gather16(u32x2 (&x)[D / 8], const uint32_t (&ae)[D / 32],
+                                                          const uint32_t (&ao)[D / 32]);
+template <> __device__ __forceinline__ void gather16<128>(u32x2 (&x)[16], const uint32_t (&ae)[4],
+                                                          const uint32_t (&ao)[4]) {
+  // row offsets (8t + 4j2) * 144 elements * 2 bytes: t0j0 0, t1j0 2304, t0j1 1152, t1j1 3456
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:2304\n\t"
+      "ds_read_b64_tr_b16 %2, %20 offset:1152\n\t"
+      "ds_read_b64_tr_b16 %3, %20 offset:3456\n\t"
+      "ds_read_b64_tr_b16 %4, %17 offset:0\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:2304\n\t"
+      "ds_read_b64_tr_b16 %6, %21 offset:1152\n\t"
+      "ds_read_b64_tr_b16 %7, %21 offset:3456\n\t"
+      "ds_read_b64_tr_b16 %8, %18 offset:0\n\t"
+      "ds_read_b64_tr_b16 %9, %18 offset:2304\n\t"
+      "ds_read_b64_tr_b16 %10, %22 offset:1152\n\t"
+      "ds_read_b64_tr_b16 %11, %22 offset:3456\n\t"
+      "ds_read_b64_tr_b16 %12, %19 offset:0\n\t"
+      "ds_read_b64_tr_b16 %13, %19 offset:2304\n\t"
+      "ds_read_b64_tr_b16 %14, %23 offset:1152\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:3456\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+        "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]),
+        "=&v"(x[15])
+      : "v"(ae[0]), "v"(ae[1]), "v"(ae[2]), "v"(ae[3]), "v"(ao[0]), "v"(ao[1]), "v"(ao[2]), "v"(ao[3])
+      : "memory");
+}
+template <> __device__ __forceinline__ void gather16<64>(u32x2 (&x)[8], const uint32_t (&ae)[2],
+                                                         const uint32_t (&ao)[2]) {
+  // row offsets (8t + 4j2) * 80 elements * 2 bytes: t0j0 0, t1j0 1280, t0j1 640, t1j1 1920
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:1280\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:640\n\t"
+      "ds_read_b64_tr_b16 %3, %10 offset:1920\n\t"
+      "ds_read_b64_tr_b16 %4, %9 offset:0\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:1280\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:640\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:1920\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(ae[0]), "v"(ae[1]), "v"(ao[0]), "v"(ao[1])
+      : "memory");
+}
+
+// Per-lane pieces of the transposed-read addressing (elements, within a
+// padded tile): lane i of 16-lane group grp sources tile row i/4 of its group's
+// 4 rows at column 16*(grp%2) + 4*(i%4); half vh = grp/2 starts 20 rows
+// further for even register groups and 12 rows for odd ones.
+template <int D> struct TrBase {
+  int even, odd;
+  __device__ TrBase(int lane) {
+    constexpr int ROW = BTile<D>::ROW;
+    const int grp = lane >> 4, gi = lane & 15, vh = grp >> 1;
+    const int base = (gi >> 2) * ROW + 16 * (grp & 1) + 4 * (gi & 3);
+    even = base + vh * 20 * ROW;
+    odd = base + vh * 12 * ROW;
+  }
+};
+
+// A^T fragments of one 32-row block (starting at row r0 of the tile at LDS
+// byte address tile): out[db][j2] is the A operand for the k slice whose
+// B operand comes from accumulator registers 8*j2 .. 8*j2+7.
+template <int D>
+__device__ __forceinline__ void gather_block(bf16x8 (&out)[D / 32][2], uint32_t tile, int r0, const TrBase<D>& tb) {
+  constexpr int ROW = BTile<D>::ROW;
+  constexpr int DB = D / 32;
+  uint32_t ae[DB], ao[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    ae[db] = tile + uint32_t(tb.even + r0 * ROW + db * 32) * 2;
+    ao[db] = tile + uint32_t(tb.odd + r0 * ROW + db * 32) * 2;
+  }
+  u32x2 x[D / 8];
+  gather16<D>(x, ae, ao);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) __builtin_memcpy(&out[db][j2], &x[(db * 2 + j2) * 2], 16);
+}
+
+// Register operand of a 32-row block of a [.][heads][D] tensor: lane holds
+// X[row0 + l32][kk*16 + 8*hh .. +8] (the B operand of a product over d, or,
+// identically laid out, an A operand with rows = the 32 rows).
+template <int D>
+__device__ __forceinline__ void load_rows(bf16x8 (&f)[D / 16], __amdgpu_buffer_rsrc_t rs, uint32_t row_off_bytes,
+                                          bool valid, int hh) {
+  const uint32_t off = row_off_bytes + 16 * hh + (valid ? 0u : kOobOffset);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint4 x = bload16(rs, off + kk * 32);
+    __builtin_memcpy(&f[kk], &x, 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O) and lse in log2 units, per (batch, position, query head)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rows = int64_t(p.batch) * p.S * p.hq;
+  if (t >= rows) return;
+  const int h = int(t % p.hq);
+  const int64_t bp = t / p.hq;
+  const int pos = int(bp % p.S);
+  const int b = int(bp / p.S);
+  const u16* orow = p.o + t * D;
+  const u16* drow = p.dout + t * D;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < D / 8; ++c) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + 8 * c);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(drow + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(float(a[e]), float(g[e]), acc);
+  }
+  const int seq = pos % p.pstride;          // intra: the stream; cross: 0
+  const int iq = pos / p.pstride;
+  const size_t idx = ((size_t(b) * p.nseq + seq) * p.hq + h) * p.Lv + iq;
+  const float l2 = p.lse[(size_t(b) * p.hq + h) * p.S + pos] * kLog2e;
+  *reinterpret_cast<float2*>(p.lsed + 2 * idx) = make_float2(l2, acc);
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query-stationary
+// ---------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  using TL = BTile<D>;
+  constexpr int KD = D / 16, DB = D / 32;
+  constexpr int NCH = 2 * TL::CH;                       // K then V chunks per tile
+  constexpr int NCW = (NCH + kWaves - 1) / kWaves;
+  __shared__ __attribute__((aligned(16))) u16 ks[ST][TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 vs[ST][TL::ELEMS];
+
+  const int pstride = MODE == 0 ? p.pstride : 1;
+  const int window = MODE == 2 ? p.window : 0;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  const int t = (blockIdx.x & 7) * p.per_xcd_q + (blockIdx.x >> 3);
+  if (t >= p.total_q) return;
+  const int ipu = p.nqb * p.hgroups;
+  const int unit = t / ipu;
+  const int rr = t - unit * ipu;
+  const int qb = p.nqb - 1 - rr / p.hgroups;
+  const int hg = rr % p.hgroups;
+  const int kvh = unit % p.hkv;
+  const int bs = unit / p.hkv;
+  const int sq = bs % p.nseq;
+  const int b = bs / p.nseq;
+  const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
+  const int PS = (kWaves / p.HG) * 32;
+  const int wg_q0 = qb * PS;
+  const int q0 = wg_q0 + (wave / p.HG) * 32;
+  const int wg_qlast = min(wg_q0 + PS, p.Lv) - 1;
+  const int kt_begin = window > 0 ? max(0, wg_q0 - window + 1) / BT : 0;
+  const int kt_end = wg_qlast / BT + 1;
+  const int base_row = b * p.S + sq;
+
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t dors = make_rsrc(p.dout, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lsed, p.lsed_bytes);
+  const uint32_t kv_pos_bytes = uint32_t(p.hkv) * D * 2;
+  const uint32_t kv_head_bytes = uint32_t(kvh) * D * 2;
+
+  // Q^T and dO^T (B operands) and the lane's query lse2 and D
+  const int vq = q0 + l32;
+  const bool qvalid = vq < p.Lv;
+  bf16x8 qf[KD], dof[KD];
+  const uint32_t qoff = (uint32_t(base_row + vq * pstride) * p.hq + h) * D * 2;
+  load_rows<D>(qf, qrs, qoff, qvalid, hh);
+  load_rows<D>(dof, dors, qoff, qvalid, hh);
+  float lse2 = 0.f, dq_d = 0.f;
+  {
+    const uint32_t li = ((uint32_t(b * p.nseq + sq) * p.hq + h) * p.Lv + vq) * 8 + (qvalid ? 0u : kOobOffset);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(lrs, int(li & ~15u), 0, 0);
+    const int w = (li >> 2) & 3;   // 8-byte pair within the 16 bytes
+    lse2 = __uint_as_float(w == 0 ? x[0] : x[2]);
+    dq_d = __uint_as_float(w == 0 ? x[1] : x[3]);
+  }
+
+  // DMA chunks: chunk c < CH is K chunk c, else V chunk c - CH; slot
+  // sl = 64*chunk + lane is row sl / SLOTS, 16-byte slot sl % SLOTS
+  uint32_t coff[NCW];
+#pragma unroll
+  for (int j = 0; j < NCW; ++j) {
+    const int c = wave + j * kWaves;
+    const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + lane;
+    const int row = sl / TL::SLOTS, ch = sl % TL::SLOTS;
+    coff[j] = ch >= D / 8 ? kOobOffset : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
+  }
+  auto issue = [&](int kt) {
+    const int st = kt % ST;
+    const uint32_t tbase = uint32_t(base_row + kt * BT * pstride) * kv_pos_bytes;
+    const bool ragged = (kt + 1) * BT > p.Lv;
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) {
+      const int c = wave + j * kWaves;
+      if (c < NCH) {
+        uint32_t off = tbase + coff[j];
+        if (ragged) {
+          const int row = ((c < TL::CH ? c : c - TL::CH) * 64 + lane) / TL::SLOTS;
+          off += kt * BT + row < p.Lv ? 0u : kOobOffset;
+        }
+        if (c < TL::CH) dma16(krs, &ks[st][c * 512], off);
+        else dma16(vrs, &vs[st][(c - TL::CH) * 512], off);
+      }
+    }
+  };
+
+  const int rowA = sigma(l32);               // tile row (within a 32-row block) this lane reads as A
+  const TrBase<D> tb(lane);
+  const int qhi = min(q0 + 32, p.Lv) - 1;
+  const bool wave_live = q0 < p.Lv;
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
+
+  issue(kt_begin);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int st = kt % ST;
+    const int k0 = kt * BT;
+    if (kt + 1 < kt_end) issue(kt + 1);
+    const bool live = wave_live && k0 <= qhi && !(window > 0 && q0 - (k0 + BT - 1) >= window);
+    if (live) {
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u16* kr = &ks[st][(kb * 32 + rowA) * TL::ROW + 8 * hh];
+        const u16* vr = &vs[st][(kb * 32 + rowA) * TL::ROW + 8 * hh];
+        bf16x8 ka[KD], va[KD];
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          ka[kk] = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
+          va[kk] = *reinterpret_cast<const bf16x8*>(vr + kk * 16);
+        }
+        sacc[kb] = f32x16{};
+        pacc[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], sacc[kb], 0, 0, 0);
+          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], dof[kk], pacc[kb], 0, 0, 0);
+        }
+      }
+      // K^T fragments for dQ^T += K^T dS^T
+      bf16x8 kT[2][DB][2];
+      const uint32_t kt_lds = lds_addr(&ks[st][0]);
+      gather_block<D>(kT[0], kt_lds, 0, tb);
+      gather_block<D>(kT[1], kt_lds, 32, tb);
+
+      const bool full = (k0 + BT - 1 <= q0) && (window == 0 || qhi - k0 < window);
+      const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int reg = j2 * 8 + i;
+            float s = sacc[kb][reg];
+            if (!full) {
+              const int key = k0 + kb * 32 + reg_key_offset(reg >> 2, hh) + (reg & 3);
+              if (!(uint32_t(vq - key) < lim)) s = -INFINITY;
+            }
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s, p.c, -lse2));
+            dsf[j2][i] = (__bf16)(pr * (pacc[kb][reg] - dq_d));
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j2 = 0; j2 < 2; ++j2)
+            dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT[kb][db][j2], dsf[j2], dqacc[db], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < kt_end) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");   // no fence needed: every read of stage st was consumed above
+    }
+  }
+
+  if (!qvalid) return;
+  u16* orow = p.dq + (size_t(base_row + vq * pstride) * p.hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 ov;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(dqacc[db][4 * g + r] * p.scale);
+      *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hh) = ov;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key-stationary
+// ---------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
+  using TL = BTile<D>;
+  constexpr int KD = D / 16, DB = D / 32;
+  constexpr int NCH = 2 * TL::CH;                       // Q then dO chunks per tile
+  constexpr int NCW = (NCH + kWaves - 1) / kWaves;
+  constexpr int KB = kWaves * 32;                       // keys per work group
+  __shared__ __attribute__((aligned(16))) u16 qs[ST][TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 ds_[ST][TL::ELEMS];
+
+  const int pstride = MODE == 0 ? p.pstride : 1;
+  const int window = MODE == 2 ? p.window : 0;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  // work item: (batch, virtual sequence, kv head, key block), heaviest first
+  const int t = (blockIdx.x & 7) * p.per_xcd_k + (blockIdx.x >> 3);
+  if (t >= p.total_k) return;
+  const int unit = t / p.nkb;
+  const int kbk = t - unit * p.nkb;          // key block 0 has the most queries above it
+  const int kvh = unit % p.hkv;
+  const int bs = unit / p.hkv;
+  const int sq = bs % p.nseq;
+  const int b = bs / p.nseq;
+  const int base_row = b * p.S + sq;
+  const int wg_k0 = kbk * KB;
+  const int k0 = wg_k0 + wave * 32;
+  const int vk = k0 + l32;                    // this lane's key (virtual index)
+  const bool kvalid = vk < p.Lv;
+  const int wg_klast = min(wg_k0 + KB, p.Lv) - 1;
+  // query tiles that can see a key of the block: from the block's first key
+  // to its last key plus the window
+  const int qt_begin = wg_k0 / BT;
+  const int qlast = window > 0 ? min(p.Lv - 1, wg_klast + window - 1) : p.Lv - 1;
+  const int qt_end = qlast / BT + 1;
+  const int nsteps = (qt_end - qt_begin) * p.G;
+
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t dors = make_rsrc(p.dout, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lsed, p.lsed_bytes);
+  const uint32_t q_pos_bytes = uint32_t(p.hq) * D * 2;
+
+  // K and V of this lane's key as B operands (K^T, V^T: k = d, n = key)
+  bf16x8 kf[KD], vf[KD];
+  {
+    const uint32_t koff = (uint32_t(base_row + vk * pstride) * p.hkv + kvh) * D * 2;
+    load_rows<D>(kf, krs, koff, kvalid, hh);
+    load_rows<D>(vf, vrs, koff, kvalid, hh);
+  }
+
+  uint32_t coff[NCW];
+#pragma unroll
+  for (int j = 0; j < NCW; ++j) {
+    const int c = wave + j * kWaves;
+    const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + lane;
+    const int row = sl / TL::SLOTS, ch = sl % TL::SLOTS;
+    coff[j] = ch >= D / 8 ? kOobOffset : uint32_t(row * pstride) * q_pos_bytes + ch * 16;
+  }
+  // step s: query tile qt_begin + s / G, query head kvh*G + s % G
+  auto issue = [&](int s) {
+    const int st = s % ST;
+    const int qt = qt_begin + s / p.G;
+    const int h = kvh * p.G + s % p.G;
+    const uint32_t tbase = uint32_t(base_row + qt * BT * pstride) * q_pos_bytes + uint32_t(h) * D * 2;
+    const bool ragged = (qt + 1) * BT > p.Lv;
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) {
+      const int c = wave + j * kWaves;
+      if (c < NCH) {
+        uint32_t off = tbase + coff[j];
+        if (ragged) {
+          const int row = ((c < TL::CH ? c : c - TL::CH) * 64 + lane) / TL::SLOTS;
+          off += qt * BT + row < p.Lv ? 0u : kOobOffset;
+        }
+        if (c < TL::CH) dma16(qrs, &qs[st][c * 512], off);
+        else dma16(dors, &ds_[st][(c - TL::CH) * 512], off);
+      }
+    }
+  };
+
+  const int rowA = sigma(l32);
+  const TrBase<D> tb(lane);
+  const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  if (nsteps > 0) {
+    issue(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const int st = s % ST;
+    const int qt = qt_begin + s / p.G;
+    const int h = kvh * p.G + s % p.G;
+    if (s + 1 < nsteps) issue(s + 1);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qf0 = qt * BT + qb * 32;        // first query of the block
+      const int qfl = min(qf0 + 31, p.Lv - 1);   // last valid one
+      // any admitted pair: a query at or after the first key, within the window of the last
+      // (wave-uniform: lanes past the last key only fill columns that are never stored)
+      const bool live = qf0 < p.Lv && k0 < p.Lv && qfl >= k0 && !(window > 0 && qf0 - (k0 + 31) >= window);
+      if (!live) continue;
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      {
+        const u16* qr = &qs[st][(qb * 32 + rowA) * TL::ROW + 8 * hh];
+        const u16* dr = &ds_[st][(qb * 32 + rowA) * TL::ROW + 8 * hh];
+        bf16x8 qa[KD], da[KD];
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          qa[kk] = *reinterpret_cast<const bf16x8*>(qr + kk * 16);
+          da[kk] = *reinterpret_cast<const bf16x8*>(dr + kk * 16);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vf[kk], pacc, 0, 0, 0);
+        }
+      }
+      // dO^T and Q^T fragments of the block
+      bf16x8 doT[DB][2], qT[DB][2];
+      gather_block<D>(doT, lds_addr(&ds_[st][0]), qb * 32, tb);
+      gather_block<D>(qT, lds_addr(&qs[st][0]), qb * 32, tb);
+      // lse2 and D of the 4 queries of each register group: 32 contiguous bytes
+      float l2[16], dd[16];
+      const uint32_t lbase = (uint32_t(b * p.nseq + sq) * p.hq + h) * p.Lv;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int iq = qf0 + reg_key_offset(g, hh);
+        const uint32_t off = (lbase + iq) * 8 + (iq < p.Lv ? 0u : kOobOffset);
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(lrs, int(off), 0, 0);
+        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(lrs, int(off + 16), 0, 0);
+        l2[4 * g + 0] = __uint_as_float(a[0]);
+        dd[4 * g + 0] = __uint_as_float(a[1]);
+        l2[4 * g + 1] = __uint_as_float(a[2]);
+        dd[4 * g + 1] = __uint_as_float(a[3]);
+        l2[4 * g + 2] = __uint_as_float(c[0]);
+        dd[4 * g + 2] = __uint_as_float(c[1]);
+        l2[4 * g + 3] = __uint_as_float(c[2]);
+        dd[4 * g + 3] = __uint_as_float(c[3]);
+      }
+      // the block is full when every query sees every key of the wave and all queries are valid
+      const bool full = qf0 + 31 < p.Lv && k0 + 31 <= qf0 && (window == 0 || qf0 + 31 - k0 < window);
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int reg = j2 * 8 + i;
+          float sc = sacc[reg];
+          if (!full) {
+            const int iq = qf0 + reg_key_offset(reg >> 2, hh) + (reg & 3);
+            if (!(iq < p.Lv && uint32_t(iq - vk) < lim)) sc = -INFINITY;
+          }
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sc, p.c, -l2[reg]));
+          pf[j2][i] = (__bf16)pr;
+          dsf[j2][i] = (__bf16)(pr * (pacc[reg] - dd[reg]));
+        }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doT[db][j2], pf[j2], dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT[db][j2], dsf[j2], dkacc[db], 0, 0, 0);
+        }
+    }
+    if (s + 1 < nsteps) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
+    }
+  }
+
+  if (!kvalid) return;
+  const size_t krow = (size_t(base_row + vk * pstride) * p.hkv + kvh) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 kv, vv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kv[r] = (__bf16)(dkacc[db][4 * g + r] * p.scale);
+        vv[r] = (__bf16)dvacc[db][4 * g + r];
+      }
+      *reinterpret_cast<bf16x4*>(p.dk + krow + db * 32 + 8 * g + 4 * hh) = kv;
+      *reinterpret_cast<bf16x4*>(p.dv + krow + db * 32 + 8 * g + 4 * hh) = vv;
+    }
+}
+
+size_t round_up(size_t x, size_t q) { return (x + q - 1) / q * q; }
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t mode) {
+  // lse2 and D for every (batch, position, query head), 8 bytes each
+  (void)mode;
+  return round_up(size_t(batch) * n * L * hq * 8, 256);
+}
+
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const u16*>(a.q);
+  p.k = static_cast<const u16*>(a.k);
+  p.v = static_cast<const u16*>(a.v);
+  p.o = static_cast<const u16*>(a.o);
+  p.dout = static_cast<const u16*>(a.dout);
+  p.lse = a.lse;
+  p.lsed = static_cast<float*>(a.ws);
+  p.dq = static_cast<u16*>(a.dq);
+  p.dk = static_cast<u16*>(a.dk);
+  p.dv = static_cast<u16*>(a.dv);
+  p.batch = int32_t(a.batch);
+  const int64_t S = int64_t(a.n) * a.L;
+  p.S = int32_t(S);
+  const bool intra = a.mode == 0;
+  p.Lv = int32_t(intra ? a.L : S);
+  p.pstride = intra ? a.n : 1;
+  p.nseq = intra ? a.n : 1;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.G = a.hq / a.hkv;
+  p.HG = 1;
+  while (p.HG * 2 <= kWaves && p.G % (p.HG * 2) == 0) p.HG *= 2;
+  p.hgroups = p.G / p.HG;
+  p.window = (a.mode == 2 && a.window < S) ? int32_t(a.window) : 0;
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  const int PS = (kWaves / p.HG) * 32;
+  p.nqb = (p.Lv + PS - 1) / PS;
+  p.nkb = (p.Lv + kWaves * 32 - 1) / (kWaves * 32);
+  const int64_t units = int64_t(a.batch) * p.nseq * p.hkv;
+  p.total_q = int32_t(units * p.nqb * p.hgroups);
+  p.per_xcd_q = (p.total_q + 7) / 8;
+  p.total_k = int32_t(units * p.nkb);
+  p.per_xcd_k = (p.total_k + 7) / 8;
+  p.q_bytes = uint32_t(a.batch * S * a.hq * a.d * 2);
+  p.kv_bytes = uint32_t(a.batch * S * a.hkv * a.d * 2);
+  p.lsed_bytes = uint32_t(a.batch * S * a.hq * 8);
+
+  const int64_t rows = a.batch * S * a.hq;
+  const dim3 pgrid(uint32_t((rows + 255) / 256));
+  const dim3 qgrid(uint32_t(p.per_xcd_q) * 8u), kgrid(uint32_t(p.per_xcd_k) * 8u);
+  using Kernel = void (*)(BwdParams);
+  static constexpr Kernel kDq[2][3] = {
+      {bwd_dq_kernel<64, 0>, bwd_dq_kernel<64, 1>, bwd_dq_kernel<64, 2>},
+      {bwd_dq_kernel<128, 0>, bwd_dq_kernel<128, 1>, bwd_dq_kernel<128, 2>}};
+  static constexpr Kernel kDkdv[2][3] = {
+      {bwd_dkdv_kernel<64, 0>, bwd_dkdv_kernel<64, 1>, bwd_dkdv_kernel<64, 2>},
+      {bwd_dkdv_kernel<128, 0>, bwd_dkdv_kernel<128, 1>, bwd_dkdv_kernel<128, 2>}};
+  const int kind = intra ? 0 : (p.window > 0 ? 2 : 1);
+  const int di = a.d == 128;
+  if (di)
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, pgrid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, pgrid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(kDkdv[di][kind], kgrid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(kDq[di][kind], qgrid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sfa

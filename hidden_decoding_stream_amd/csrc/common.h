@@ -87,4 +87,32 @@ __device__ __forceinline__ void tr_read8(u32x2 (&o)[8], const uint32_t (&a)[8]) 
       : "memory");
 }
 
+// ---- 32x32x16 MFMA operand order shared by the attention kernels ----
+// Row group (4 rows) that MFMA A-operand row group m>>2 reads from a tile of
+// 32 rows (keys in the forward). After C = A B^T-style products, accumulator
+// register 4g+r of lane half h then holds C row 8g + 4h + r, i.e. tile row
+// 4*kSigmaG[2g+h] + r: rows 16h .. 16h+15 of the block, so the accumulator
+// registers can feed the next MFMA's B operand (k index = 8h + j) directly.
+// The 16 rows that lanes 0-15 (or 16-31) read are distinct modulo 16, which
+// with a padded row of D+16 elements puts them in distinct LDS bank groups.
+__device__ __forceinline__ int sigma(int m) {
+  constexpr uint32_t kSigmaG = 0x63417250u;  // m>>2 = 0..7 -> 0 5 2 7 1 4 3 6 (nibbles, lowest first)
+  return 4 * int((kSigmaG >> (4 * (m >> 2))) & 7u) + (m & 3);
+}
+// Offset (within a 32-key block) of the 4 keys held in registers 4g..4g+3 by
+// lane half h: 16h + 4*(((g&1)*2 + (g>>1)) ^ h).
+__device__ __forceinline__ int reg_key_offset(int g, int h) { return 16 * h + 4 * ((((g & 1) * 2 + (g >> 1))) ^ h); }
+// Combine a value with the one held by lane l^32 (the other half of the
+// wave): v_permlane32_swap exchanges the two halves without going through LDS,
+// and the max / sum of the two results is the same whichever half lands where.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+
 }  // namespace sfa

@@ -34,6 +34,28 @@ struct FwdArgs {
 };
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream);
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t batch;
+  int32_t n;
+  int64_t L;
+  int32_t hq, hkv, d;
+  int32_t mode;
+  int64_t window;
+  float scale;
+  void* ws;
+};
+size_t attn_bwd_workspace_bytes(int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t mode);
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* kc;

@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
     L.sf_rope.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int32, c.c_int32, c.c_float, c.c_int64, c.c_void_p]
     L.sf_attn_fwd_last_stream.restype = c.c_int
     L.sf_attn_fwd_last_stream.argtypes = L.sf_attn_fwd.argtypes
+    L.sf_attn_bwd_workspace_bytes.restype = c.c_size_t
+    L.sf_attn_bwd_workspace_bytes.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32, c.c_int32,
+                                              c.c_int32, c.c_int64]
+    L.sf_attn_bwd.restype = c.c_int
+    L.sf_attn_bwd.argtypes = [c.c_void_p] * 9 + [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32, c.c_int32,
+                                                 c.c_int32, c.c_int64, c.c_float, c.c_void_p, c.c_size_t, c.c_void_p]
     L.sf_attn_decode_workspace_bytes.restype = c.c_size_t
     L.sf_attn_decode_workspace_bytes.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32,
                                                  c.c_int32, c.c_int32, c.c_int64, c.c_int32]
@@ -211,6 +217,31 @@ def sf_attn_fwd_last_stream(q_last: torch.Tensor, k: torch.Tensor, v: torch.Tens
                                          _dev(out, "out", bf), lse_ptr, B, n, L, hq, hkv, d, _mode(mode),
                                          int(window), float(scale), _stream(stream)))
     return (out, lse) if want_lse else out
+
+
+def sf_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+                lse: torch.Tensor, mode, n: int, window: int = 0, scale: float | None = None,
+                out=None, workspace: torch.Tensor | None = None, stream=None):
+    """Gradients (dq, dk, dv) of sf_attn_fwd for the loss sum(dout * o).
+    q, o, dout [B][n*L][hq][d]; k, v [B][n*L][hkv][d]; bf16; lse float32
+    [B][hq][n*L] as returned by sf_attn_fwd(..., lse=True)."""
+    B, S, hq, d = q.shape
+    hkv = k.shape[2]
+    if S % n:
+        raise ValueError("sequence length must be a multiple of n")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    need = int(lib().sf_attn_bwd_workspace_bytes(B, n, S // n, hq, hkv, d, _mode(mode), int(window)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    bf = torch.bfloat16
+    _check(lib().sf_attn_bwd(_dev(q, "q", bf), _dev(k, "k", bf), _dev(v, "v", bf), _dev(o, "o", bf),
+                             _dev(dout, "dout", bf), _dev(lse, "lse", torch.float32), _dev(dq, "dq", bf),
+                             _dev(dk, "dk", bf), _dev(dv, "dv", bf), B, n, S // n, hq, hkv, d, _mode(mode),
+                             int(window), float(scale), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
 
 
 def sf_attn_decode_workspace_bytes(batch: int, n: int, T: int, hq: int, hkv: int, d: int, mode,

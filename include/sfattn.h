@@ -149,6 +149,32 @@ sf_status sf_attn_fwd_last_stream(const void* q_last, const void* k, const void*
                                   int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
                                   int32_t mode, int64_t window, float scale, hipStream_t stream);
 
+/* Bytes of device workspace sf_attn_bwd needs (0 if the arguments are invalid
+ * or the problem is empty): lse*log2(e) and D = rowsum(dout * o) for every
+ * (batch, position, query head), 8 bytes each. */
+size_t sf_attn_bwd_workspace_bytes(int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv, int32_t d,
+                                   int32_t mode, int64_t window);
+
+/* Backward of sf_attn_fwd: the gradients of the loss sum(dout * o) with
+ * respect to q, k and v, for training ([HD-tahou] 实验效果与成本分析 states
+ * the method's cost as training step times). With P the masked softmax of
+ * scale * q k^T (as in sf_attn_fwd):
+ *   dv = P^T dout,  dP = dout v^T,  dS = P * (dP - rowsum(dout * o)),
+ *   dq = scale dS k,  dk = scale dS^T q,
+ * summed over the query heads of a group for dk and dv.
+ *   q, o, dout, dq : bf16 [batch][n*L][hq][d];  k, v, dk, dv : bf16 [batch][n*L][hkv][d].
+ *   lse : fp32 [batch][hq][n*L], the natural-log LSE that sf_attn_fwd returned for o.
+ *   workspace : at least sf_attn_bwd_workspace_bytes(...) bytes, 16-byte
+ *               aligned; contents on entry do not matter.
+ * dq, dk, dv are overwritten (not accumulated); they must not overlap each
+ * other, the inputs or the workspace. Results are deterministic (no
+ * atomics). Other arguments, errors and the supported set as for
+ * sf_attn_fwd. */
+sf_status sf_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int64_t batch, int32_t n, int64_t L, int32_t hq, int32_t hkv,
+                      int32_t d, int32_t mode, int64_t window, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* Bytes of device workspace sf_attn_decode needs for these arguments (0 if the
  * arguments are invalid or the problem is empty). num_splits as for
  * sf_attn_decode; the result depends on nothing else. */

@@ -239,8 +239,20 @@ def attn_fwd_last_stream(q_last, k, v, mode: str, n: int, window: int | None = N
     return attn_fwd(q, k, v, mode, n, window=window, scale=scale, rows=rows, with_lse=with_lse)
 
 
+def _probs_and_dscores(qh, kh, vh, do, allowed, scale):
+    """One head's P (masked softmax rows of scale * Q K^T, zero where masked)
+    and dS = P * (dP - rowsum(dP * P)) with dP = dO V^T."""
+    s = float(scale) * (qh @ kh.T)
+    s = np.where(allowed, s, -np.inf)
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    pr = w / w.sum(axis=1, keepdims=True)
+    dp = do @ vh.T
+    ds = pr * (dp - (dp * pr).sum(axis=1, keepdims=True))
+    return pr, ds
+
+
 def attn_bwd(q, k, v, dout, mode: str, n: int, window: int | None = None, scale: float | None = None,
-             block: int = 512):
+             block: int = 512, rows=None, key_rows=None):
     """Gradients of :func:`attn_fwd` for the loss sum(dout * o), in float64.
 
     The pages report training step times for the method ([HD-tahou]
@@ -253,7 +265,14 @@ def attn_bwd(q, k, v, dout, mode: str, n: int, window: int | None = None, scale:
     sums over the query heads that read it.
 
     q, dout: [B][S][Hq][D]; k, v: [B][S][Hkv][D]. Returns (dq, dk, dv).
+    With ``rows`` and ``key_rows`` (position arrays) only dq at those query
+    rows and dk, dv at those key rows are returned; the query rows that see
+    one of the keys are found from the mask and computed in full.
     """
+    if rows is not None or key_rows is not None:
+        return _attn_bwd_subset(q, k, v, dout, mode, n, window, scale, block,
+                                np.arange(0) if rows is None else np.asarray(rows, dtype=np.int64),
+                                np.arange(0) if key_rows is None else np.asarray(key_rows, dtype=np.int64))
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -273,16 +292,51 @@ def attn_bwd(q, k, v, dout, mode: str, n: int, window: int | None = None, scale:
         for b in range(B):
             for h in range(Hq):
                 kh = h // G
-                s = float(scale) * (q[b, rr, h] @ k[b, :, kh].T)
-                s = np.where(allowed, s, -np.inf)
-                w = np.exp(s - s.max(axis=1, keepdims=True))
-                pr = w / w.sum(axis=1, keepdims=True)           # P rows, zero where masked
                 do = dout[b, rr, h]
+                pr, ds = _probs_and_dscores(q[b, rr, h], k[b, :, kh], v[b, :, kh], do, allowed, scale)
                 dv[b, :, kh] += pr.T @ do
-                dp = do @ v[b, :, kh].T
-                ds = pr * (dp - (dp * pr).sum(axis=1, keepdims=True))
                 dq[b, rr, h] = float(scale) * (ds @ k[b, :, kh])
                 dk[b, :, kh] += float(scale) * (ds.T @ q[b, rr, h])
+    return dq, dk, dv
+
+
+def _attn_bwd_subset(q, k, v, dout, mode, n, window, scale, block, rows, key_rows):
+    """dq at ``rows`` and dk, dv at ``key_rows`` (same formulas as attn_bwd)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    L = S // n
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    # query rows whose softmax touches one of the keys
+    seeing = np.zeros(S, dtype=bool)
+    for r0 in range(0, S, block):
+        rr = np.arange(r0, min(S, r0 + block))
+        if len(key_rows):
+            seeing[rr] = mask(mode, n, L, window, rr)[:, key_rows].any(axis=1)
+    need = np.union1d(rows, np.nonzero(seeing)[0])
+    dq = np.zeros((B, len(rows), Hq, D))
+    dk = np.zeros((B, len(key_rows), Hkv, D))
+    dv = np.zeros((B, len(key_rows), Hkv, D))
+    row_at = {int(r): i for i, r in enumerate(rows)}
+    for r0 in range(0, len(need), block):
+        rr = need[r0:r0 + block]
+        allowed = mask(mode, n, L, window, rr)
+        for b in range(B):
+            for h in range(Hq):
+                kh = h // G
+                do = dout[b, rr, h]
+                pr, ds = _probs_and_dscores(q[b, rr, h], k[b, :, kh], v[b, :, kh], do, allowed, scale)
+                for i, r in enumerate(rr):
+                    if int(r) in row_at:
+                        dq[b, row_at[int(r)], h] = float(scale) * (ds[i] @ k[b, :, kh])
+                if len(key_rows):
+                    dv[b, :, kh] += pr[:, key_rows].T @ do
+                    dk[b, :, kh] += float(scale) * (ds[:, key_rows].T @ q[b, rr, h])
     return dq, dk, dv
 
 

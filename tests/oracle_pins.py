@@ -429,6 +429,14 @@ def pin_backward(orc):
     assert np.allclose(dq[0], qt.grad.numpy(), atol=1e-12)
     assert np.allclose(dk[0], kt.grad.numpy(), atol=1e-12)
     assert np.allclose(dv[0], vt.grad.numpy(), atol=1e-12)
+    # selected query rows and key rows equal the same rows of the full gradients
+    rows, keys = np.array([0, 3, S - 1]), np.array([1, 4, S - 2])
+    for mode, W in (("intra", None), ("cross_full", None), ("cross_window", 3)):
+        full = orc.attn_bwd(q, k, v, do, mode, n, window=W, scale=scale)
+        sub = orc.attn_bwd(q, k, v, do, mode, n, window=W, scale=scale, rows=rows, key_rows=keys, block=2)
+        assert np.allclose(sub[0], full[0][:, rows], atol=1e-13), mode
+        assert np.allclose(sub[1], full[1][:, keys], atol=1e-13), mode
+        assert np.allclose(sub[2], full[2][:, keys], atol=1e-13), mode
     # GQA: repeated K/V as MHA, gradients summed over each group
     k_rep, v_rep = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
     for mode, W in (("intra", None), ("cross_window", 4)):

@@ -31,7 +31,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"sf_interleave", "sf_expand_embed", "sf_rope", "sf_attn_fwd", "sf_attn_fwd_last_stream",
-            "sf_attn_decode", "sf_attn_decode_workspace_bytes", "sf_abi_version", "sf_last_error"} <= set(names)
+            "sf_attn_bwd", "sf_attn_bwd_workspace_bytes", "sf_attn_decode", "sf_attn_decode_workspace_bytes",
+            "sf_abi_version", "sf_last_error"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -190,3 +191,41 @@ def rope(x=P, batch=1, S=16, heads=4, d=128, base=10000.0, pos0=0):
 def test_rope_rejects(kw, status):
     assert rope(**kw) == status
     assert sfa.sf_last_error() != ""
+
+
+PB = [ctypes.c_void_p(a << 32) for a in range(1, 11)]   # ten disjoint fake device buffers
+
+
+def bwd(ptrs=None, batch=1, n=4, Lt=16, hq=4, hkv=2, d=64, mode=1, window=0, scale=0.125, wsb=1 << 20, **over):
+    p = list(PB if ptrs is None else ptrs)
+    names = ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"]
+    for key, val in over.items():
+        p[names.index(key)] = val
+    return L.sf_attn_bwd(*p[:9], batch, n, Lt, hq, hkv, d, mode, window, scale, p[9], wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), B.SF_ERR_INVALID),
+    (dict(n=0), B.SF_ERR_INVALID),
+    (dict(hq=6, hkv=4), B.SF_ERR_INVALID),
+    (dict(mode=2, window=0), B.SF_ERR_INVALID),
+    (dict(d=96), B.SF_ERR_UNSUPPORTED),
+    (dict(dq=None), B.SF_ERR_INVALID),
+    (dict(lse=None), B.SF_ERR_INVALID),
+    (dict(ws=None), B.SF_ERR_INVALID),
+    (dict(wsb=16), B.SF_ERR_INVALID),                               # workspace too small
+    (dict(dk=PB[0]), B.SF_ERR_INVALID),                             # dk aliases q
+    (dict(dv=PB[6]), B.SF_ERR_INVALID),                             # dv aliases dq
+    (dict(q=ctypes.c_void_p((1 << 32) + 8)), B.SF_ERR_UNSUPPORTED),  # misaligned
+    (dict(batch=1 << 20, Lt=1 << 20), B.SF_ERR_UNSUPPORTED),        # beyond 2^30 elements
+])
+def test_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+    assert sfa.sf_last_error() != ""
+
+
+def test_bwd_workspace_query():
+    # lse*log2(e) and D per (batch, position, query head), 8 bytes each, rounded to 256
+    assert sfa.lib().sf_attn_bwd_workspace_bytes(2, 4, 100, 8, 2, 128, 1, 0) == -(-2 * 400 * 8 * 8 // 256) * 256
+    assert sfa.lib().sf_attn_bwd_workspace_bytes(0, 4, 100, 8, 2, 128, 1, 0) == 0
+    assert bwd(batch=0) == B.SF_OK

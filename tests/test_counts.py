@@ -55,3 +55,8 @@ def test_front_end_bytes():
     # n=4 tables, L=8192 tokens, 8 KiB rows: read + write of 32768 rows, plus the ids
     assert C.expand_embed_bytes(1, 4, 8192, 8192) == 2 * 32768 * 8192 + 4 * 8192
     assert C.rope_bytes(1 << 28) == 1 << 29
+
+
+def test_backward_flops_is_two_and_a_half_forwards():
+    for mode, W in (("intra", 0), ("cross_full", 0), ("cross_window", 4096)):
+        assert 2 * C.backward_flops(mode, 4, 4096, 2, 32, 128, W) == 5 * C.prefill_flops(mode, 4, 4096, 2, 32, 128, W)

@@ -1,0 +1,116 @@
+"""sf_attn_bwd on the GPU against the fp64 oracle's gradients.
+
+Small problems are compared on every element of dq, dk and dv (all three
+masks, GQA and MHA, d = 64 and 128, several tiles and ragged tails). At full
+size dq is compared on sampled query rows, dk and dv on keys near the end of
+each sequence (whose few queries the oracle computes in full), and two
+identities are checked over every key: the dv of a kv head sums to the sum of
+dout over its queries (each softmax row sums to one) and its dk sums to zero
+(each row of dS sums to zero).
+
+Tolerance: the gradients are products of bf16-rounded probabilities and
+operands with fp32 accumulation, rounded to bf16; their size grows with the
+number of queries a key sees, so the bar is relative to the reference's
+magnitude: max |err| <= 2e-2 * max(1, max |ref|) and
+mean |err| <= 2e-3 * max(1, mean |ref|).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hidden_decoding_stream_amd as sfa
+import hidden_decoding_stream_amd.inputs as I
+import oracle.sfa as orc
+from gpu_util import assert_close, np64, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _scale(d):
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def _close(got, ref, what):
+    ref = np.asarray(ref)
+    mx = max(1.0, float(np.abs(ref).max()))
+    mn = max(1.0, float(np.abs(ref).mean()))
+    assert_close(got, ref, what, max_abs=2e-2 * mx, mean_abs=2e-3 * mn)
+
+
+def _run(q, k, v, do, mode, n, W):
+    q, k, v, do = (t.cuda() for t in (q, k, v, do))
+    o, lse = sfa.sf_attn_fwd(q, k, v, mode, n, window=W, scale=_scale(q.shape[-1]), lse=True)
+    grads = sfa.sf_attn_bwd(q, k, v, o, do, lse, mode, n, window=W, scale=_scale(q.shape[-1]))
+    torch.cuda.synchronize()
+    return grads
+
+
+CASES = [
+    # n, L, B, hq, hkv, d, mode, window
+    (4, 40, 1, 4, 2, 64, "cross_full", 0),
+    (4, 40, 1, 4, 2, 64, "intra", 0),
+    (4, 40, 1, 4, 2, 64, "cross_window", 37),
+    (4, 70, 1, 8, 2, 128, "cross_full", 0),
+    (4, 70, 1, 8, 2, 128, "intra", 0),
+    (3, 50, 2, 4, 4, 128, "cross_window", 64),
+    (2, 100, 1, 4, 1, 128, "cross_full", 0),
+    (1, 130, 1, 2, 2, 64, "cross_full", 0),         # n = 1: ordinary causal attention
+    (4, 1, 1, 4, 2, 64, "cross_full", 0),           # one token
+    (2, 90, 1, 8, 8, 64, "cross_window", 1000),     # window >= S
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_small_all_elements(case):
+    n, L, B, hq, hkv, d, mode, W = case
+    say("bwd small", case)
+    q, k, v = I.expanded_qkv(n * L, B, hq, hkv, d, seed=41 + L)
+    g = torch.Generator().manual_seed(43 + L)
+    do = I.to_bf16(torch.randn(q.shape, generator=g))
+    dq, dk, dv = _run(q, k, v, do, mode, n, W)
+    rq, rk, rv = orc.attn_bwd(np64(q), np64(k), np64(v), np64(do), mode, n, window=W or None, scale=_scale(d))
+    _close(np64(dq), rq, f"dq {case}")
+    _close(np64(dk), rk, f"dk {case}")
+    _close(np64(dv), rv, f"dv {case}")
+
+
+def test_deterministic_and_repeatable():
+    n, L, hq, hkv, d = 4, 300, 8, 2, 128
+    say("bwd determinism")
+    q, k, v = (t.cuda() for t in I.expanded_qkv(n * L, 1, hq, hkv, d, seed=9))
+    do = torch.randn(q.shape, device="cuda").to(torch.bfloat16)
+    o, lse = sfa.sf_attn_fwd(q, k, v, "cross_full", n, lse=True)
+    a = sfa.sf_attn_bwd(q, k, v, o, do, lse, "cross_full", n)
+    b = sfa.sf_attn_bwd(q, k, v, o, do, lse, "cross_full", n)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("w", [I.INTRA_16K, I.WINDOW_16K, I.CROSS_32K], ids=lambda w: w.name)
+def test_full_size(w):
+    say("bwd full size", w.name)
+    q, k, v = I.workload_qkv(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 50)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    dq, dk, dv = _run(q, k, v, do, w.mode, w.n, w.window)
+    S, n, G = w.S, w.n, w.hq // w.hkv
+    # identities over every key, per batch element and kv head
+    sdv = dv.double().sum(dim=1)                                          # [B][hkv][d]
+    sdo = do.double().sum(dim=1).view(w.batch, w.hkv, G, w.d).sum(dim=2)  # [B][hkv][d]
+    _close(np64(sdv), np64(sdo), f"{w.name} sum_k dv")
+    # sum_k dk vanishes up to the bf16 rounding of dS: a small fraction of sum_k |dk|
+    resid = float(dk.double().sum(dim=1).abs().max())
+    scale_ = float(dk.double().abs().sum(dim=1).max())
+    say(f"{w.name} sum_k dk: {resid:.3e} of sum_k |dk| {scale_:.3e}")
+    assert resid <= 1e-2 * scale_, "sum_k dk must vanish"
+    # dq on sampled rows; dk, dv on the last keys of each stream (few queries see them)
+    rows = sample_rows(S, seed=w.seed, window=w.window)[::3]
+    keys = np.array(sorted({S - 1, S - 2, S - 5, S - n, S - 2 * n - 1, S - 64, S - 65, S - 130}))
+    rq, rk, rv = orc.attn_bwd(np64(q), np64(k), np64(v), np64(do), w.mode, n, window=w.window or None,
+                              scale=w.scale, rows=rows, key_rows=keys)
+    _close(np64(dq[:, rows]), rq, f"{w.name} dq rows")
+    _close(np64(dk[:, keys]), rk, f"{w.name} dk keys")
+    _close(np64(dv[:, keys]), rv, f"{w.name} dv keys")
