@@ -183,30 +183,50 @@ __device__ __forceinline__ void load_rows(bf16x8 (&f)[D / 16], __amdgpu_buffer_r
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O) and lse in log2 units, per (batch, position, query head)
 // ---------------------------------------------------------------------------
+// One block covers kPrepRows consecutive rows of one (batch, query head) in
+// the workspace's order (virtual sequence, then query), so its lse reads and
+// workspace writes are contiguous; a row's O and dO are read by D/8 lanes,
+// 16 bytes each, and reduced across those lanes.
+constexpr int kPrepRows = 64;
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t rows = int64_t(p.batch) * p.S * p.hq;
-  if (t >= rows) return;
-  const int h = int(t % p.hq);
-  const int64_t bp = t / p.hq;
-  const int pos = int(bp % p.S);
-  const int b = int(bp / p.S);
-  const u16* orow = p.o + t * D;
-  const u16* drow = p.dout + t * D;
-  float acc = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + 8 * c);
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(drow + 8 * c);
+  constexpr int R = D / 8;                  // lanes per row
+  constexpr int SLOTS = 256 / R;            // rows per pass
+  constexpr int ITER = kPrepRows / SLOTS;
+  const int nblk = (p.S + kPrepRows - 1) / kPrepRows;
+  const int bh = int(blockIdx.x) / nblk;    // b * hq + h
+  const int j0 = (int(blockIdx.x) - bh * nblk) * kPrepRows;
+  const int b = bh / p.hq, h = bh - b * p.hq;
+  const int slot = int(threadIdx.x) / R, part = int(threadIdx.x) % R;
+  float acc[ITER];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(float(a[e]), float(g[e]), acc);
+  for (int it = 0; it < ITER; ++it) {
+    acc[it] = 0.f;
+    const int j = j0 + it * SLOTS + slot;   // (seq, iq) flattened: j = seq * Lv + iq
+    if (j < p.S) {
+      const int seq = j / p.Lv, iq = j - seq * p.Lv;
+      const int pos = iq * p.pstride + seq;
+      const size_t row = (size_t(b) * p.S + pos) * p.hq + h;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(p.o + row * D + 8 * part);
+      const bf16x8 g = *reinterpret_cast<const bf16x8*>(p.dout + row * D + 8 * part);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[it] = fmaf(float(a[e]), float(g[e]), acc[it]);
+    }
   }
-  const int seq = pos % p.pstride;          // intra: the stream; cross: 0
-  const int iq = pos / p.pstride;
-  const size_t idx = ((size_t(b) * p.nseq + seq) * p.hq + h) * p.Lv + iq;
-  const float l2 = p.lse[(size_t(b) * p.hq + h) * p.S + pos] * kLog2e;
-  *reinterpret_cast<float2*>(p.lsed + 2 * idx) = make_float2(l2, acc);
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+#pragma unroll
+    for (int m = R / 2; m >= 1; m /= 2) acc[it] += __shfl_xor(acc[it], m, R);
+    const int j = j0 + it * SLOTS + slot;
+    if (j < p.S && part == 0) {
+      const int seq = j / p.Lv, iq = j - seq * p.Lv;
+      const int pos = iq * p.pstride + seq;
+      const size_t idx = ((size_t(b) * p.nseq + seq) * p.hq + h) * p.Lv + iq;
+      const float l2 = p.lse[size_t(bh) * p.S + pos] * kLog2e;
+      *reinterpret_cast<float2*>(p.lsed + 2 * idx) = make_float2(l2, acc[it]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -639,8 +659,7 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
   p.kv_bytes = uint32_t(a.batch * S * a.hkv * a.d * 2);
   p.lsed_bytes = uint32_t(a.batch * S * a.hq * 8);
 
-  const int64_t rows = a.batch * S * a.hq;
-  const dim3 pgrid(uint32_t((rows + 255) / 256));
+  const dim3 pgrid(uint32_t(a.batch * a.hq * ((S + kPrepRows - 1) / kPrepRows)));
   const dim3 qgrid(uint32_t(p.per_xcd_q) * 8u), kgrid(uint32_t(p.per_xcd_k) * 8u);
   using Kernel = void (*)(BwdParams);
   static constexpr Kernel kDq[2][3] = {
