@@ -373,3 +373,46 @@ def decode(q_new, k_cache, v_cache, T: int, mode: str, window: int | None = None
             kh = h // G
             o[b, :, h], _ = attend(q_new[b, :, h], K[b, :, kh], V[b, :, kh], allowed, scale)
     return o
+
+
+def gather_pages(pages, block_table, T: int):
+    """The logical per-stream cache of one sequence from a paged pool.
+
+    pages: [num_pages][P][Hkv][D]; block_table: [n][max_pages] (ints).
+    Token t of stream k lives in row t mod P of page block_table[k][t div P].
+    Returns [n][T][Hkv][D].
+    """
+    pages = np.asarray(pages)
+    P = pages.shape[1]
+    bt = np.asarray(block_table)
+    n = bt.shape[0]
+    t = np.arange(T)
+    return np.stack([pages[bt[k, t // P], t % P] for k in range(n)])
+
+
+def decode_paged(q_new, k_pages, v_pages, block_table, seq_lens, mode: str,
+                 window: int | None = None, scale: float | None = None):
+    """Decode of a batch of sequences of different lengths against a paged
+    per-stream cache.
+
+    Each sequence b runs :func:`decode` at its own length T_b = seq_lens[b]
+    (its n stream queries of token T_b - 1, [HD-tahou] 实验效果与成本分析)
+    against its per-stream caches ([HD-aiflow] "Latent computation scaling and
+    Hidden Decoding"), which here are spread over fixed-size pages: stream k's
+    token t is row t mod P of page block_table[b][k][t div P].
+
+    q_new: [B][n][Hq][D]; k_pages, v_pages: [num_pages][P][Hkv][D];
+    block_table: [B][n][max_pages]; seq_lens: [B], each >= 1.
+    Returns o [B][n][Hq][D].
+    """
+    q_new = np.asarray(q_new, dtype=np.float64)
+    B = q_new.shape[0]
+    out = np.empty_like(q_new)
+    for b in range(B):
+        T = int(seq_lens[b])
+        if T < 1:
+            raise ValueError("every sequence holds at least its newest token")
+        kc = gather_pages(np.asarray(k_pages, dtype=np.float64), block_table[b], T)
+        vc = gather_pages(np.asarray(v_pages, dtype=np.float64), block_table[b], T)
+        out[b] = decode(q_new[b:b + 1], kc[None], vc[None], T, mode, window=window, scale=scale)[0]
+    return out

@@ -447,6 +447,55 @@ def pin_backward(orc):
         assert np.allclose(a[2], m[2].reshape(B, S, Hkv, G, D).sum(axis=3), atol=1e-12)
 
 
+def pin_decode_paged(orc):
+    """Paged decode with per-sequence lengths: a (token, stream) brute force
+    that walks the block table by explicit loops, the last n prefill rows of
+    each sequence at its own length, and invariance under a permutation of the
+    physical pages. Includes n = 8 with n*G = 32 rows per kv head."""
+    rng = _rng(21)
+    for n, Hq, Hkv, P, lens, W in ((3, 4, 2, 2, (5, 1, 3), 4), (8, 8, 2, 3, (2, 4), 11)):
+        B = len(lens)
+        D = 3
+        G = Hq // Hkv
+        maxp = max((t + P - 1) // P for t in lens) + 1
+        npages = B * n * maxp + 2
+        kp = _bf16ish(rng, (npages, P, Hkv, D))
+        vp = _bf16ish(rng, (npages, P, Hkv, D))
+        table = rng.permutation(npages)[:B * n * maxp].reshape(B, n, maxp)
+        q = _bf16ish(rng, (B, n, Hq, D))
+        for mode in ("intra", "cross_full", "cross_window"):
+            o = orc.decode_paged(q, kp, vp, table, np.array(lens), mode, window=W, scale=0.6)
+            for b in range(B):
+                T = lens[b]
+
+                def key(arr, t, s, kh):
+                    page = int(table[b][s][t // P])
+                    return arr[page][t - (t // P) * P][kh]
+                for h in range(Hq):
+                    kh = h // G
+                    for kq in range(n):
+                        sel = [(t, s) for t in range(T) for s in range(n)
+                               if allowed_ts(mode, n, T - 1, kq, t, s, W)]
+                        sc = [0.6 * float(np.dot(q[b, kq, h], key(kp, t, s, kh))) for t, s in sel]
+                        mx = max(sc)
+                        w = [math.exp(x - mx) for x in sc]
+                        want = sum(wi * key(vp, t, s, kh) for wi, (t, s) in zip(w, sel)) / sum(w)
+                        assert np.allclose(o[b, kq, h], want, atol=1e-12), (mode, b, h, kq)
+                # the last n rows of prefill over this sequence's T tokens
+                K = np.stack([key(kp, t, s, slice(None)) for t in range(T) for s in range(n)])[None]
+                V = np.stack([key(vp, t, s, slice(None)) for t in range(T) for s in range(n)])[None]
+                Q = np.zeros((1, n * T, Hq, D))
+                Q[0, (T - 1) * n:] = q[b]
+                full = orc.attn_fwd(Q, K, V, mode, n, window=W, scale=0.6)
+                assert np.allclose(full[0, (T - 1) * n:], o[b], atol=1e-12), (mode, b)
+            # moving the pages and rewriting the table changes nothing
+            perm = rng.permutation(npages)
+            kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+            kp2[perm], vp2[perm] = kp, vp
+            o2 = orc.decode_paged(q, kp2, vp2, perm[table], np.array(lens), mode, window=W, scale=0.6)
+            assert np.array_equal(o, o2), mode
+
+
 ALL_PINS = [
     pin_interleave_golden,
     pin_interleave_bruteforce,
@@ -462,6 +511,7 @@ ALL_PINS = [
     pin_pure_python_bruteforce,
     pin_stream_permutation_equivariance,
     pin_decode_bruteforce,
+    pin_decode_paged,
     pin_last_stream,
     pin_expand_embed,
     pin_rope,

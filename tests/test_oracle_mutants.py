@@ -42,6 +42,12 @@ MUTANTS = {
     # rotary frequencies with exponent 2j/half instead of 2j/d
     "rope_freq": ("theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)",
                   "theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / half)"),
+    # paged cache: every stream reads stream 0's pages
+    "paged_stream0_table": ("pages[bt[k, t // P], t % P]", "pages[bt[0, t // P], t % P]"),
+    # paged cache: row within the page off by one
+    "paged_row_shift": ("pages[bt[k, t // P], t % P]", "pages[bt[k, t // P], (t + 1) % P]"),
+    # per-sequence lengths ignored: every sequence decodes at the first one's length
+    "paged_one_length": ("T = int(seq_lens[b])", "T = int(seq_lens[0])"),
     # backward: dS without the rowsum correction
     "bwd_no_rowsum": ("ds = pr * (dp - (dp * pr).sum(axis=1, keepdims=True))", "ds = pr * dp"),
     # backward: dK built from dP instead of dS
