@@ -274,8 +274,8 @@ sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_c
   sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
   if (st != SF_OK) return st;
   const int32_t G = hq / hkv;
-  if (mode == SF_INTRA ? G > 16 : int64_t(n) * G > 16)
-    return fail(SF_ERR_UNSUPPORTED, "%s decode supports at most 16 query rows per kv head (n=%d, G=%d)",
+  if (mode == SF_INTRA ? G > 64 : int64_t(n) * G > 64)
+    return fail(SF_ERR_UNSUPPORTED, "%s decode supports at most 64 query rows per kv head (n=%d, G=%d)",
                 mode_name(mode), n, G);
   if (batch == 0) return ok();
   if (!q_new || !k_cache || !v_cache || !o_new) return fail(SF_ERR_INVALID, "null q_new, cache or o_new");
@@ -308,6 +308,79 @@ sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_c
   sfa::DecodeArgs a{q_new, k_cache, v_cache, o_new, batch, n, T, T_max, hq, hkv, d, mode,
                     window, scale, num_splits, workspace};
   return device_status(sfa::launch_attn_decode(a, plan, stream), "sf_attn_decode launch");
+}
+
+size_t sf_attn_decode_paged_workspace_bytes(int64_t batch, int32_t n, int64_t max_T, int32_t hq,
+                                            int32_t hkv, int32_t d, int32_t mode, int64_t window,
+                                            int32_t num_splits) {
+  if (batch <= 0 || max_T < 1 || num_splits < 0) return 0;
+  if (check_heads(n, hq, hkv, d, mode, window, 1.0f) != SF_OK) return 0;
+  return sfa::plan_decode(batch, n, max_T, hq, hkv, d, mode, window, num_splits, true).ws_bytes;
+}
+
+sf_status sf_attn_decode_paged(const void* q_new, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seq_lens, void* o_new,
+                               int64_t batch, int32_t n, int64_t max_T, int64_t num_pages,
+                               int32_t page_size, int64_t max_pages, int32_t hq, int32_t hkv, int32_t d,
+                               int32_t mode, int64_t window, float scale, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (batch < 0) return fail(SF_ERR_INVALID, "batch must be >= 0");
+  if (max_T < 1) return fail(SF_ERR_INVALID, "max_T must be >= 1 (got %lld)", (long long)max_T);
+  if (num_pages < 1) return fail(SF_ERR_INVALID, "num_pages must be >= 1");
+  if (page_size < 1 || max_pages < 1) return fail(SF_ERR_INVALID, "page_size and max_pages must be >= 1");
+  if (page_size % 32)
+    return fail(SF_ERR_UNSUPPORTED, "page_size must be a multiple of 32 tokens (got %d)", page_size);
+  if (max_pages < (max_T + page_size - 1) / page_size)
+    return fail(SF_ERR_INVALID, "max_pages (%lld) x page_size (%d) does not cover max_T (%lld)",
+                (long long)max_pages, page_size, (long long)max_T);
+  if (num_splits < 0) return fail(SF_ERR_INVALID, "num_splits must be >= 0");
+  sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
+  if (st != SF_OK) return st;
+  const int32_t G = hq / hkv;
+  if (mode == SF_INTRA ? G > 64 : int64_t(n) * G > 64)
+    return fail(SF_ERR_UNSUPPORTED, "%s decode supports at most 64 query rows per kv head (n=%d, G=%d)",
+                mode_name(mode), n, G);
+  if (int64_t(n) * max_T > INT32_MAX)
+    return fail(SF_ERR_UNSUPPORTED, "n * max_T must be below 2^31 expanded positions");
+  if (int64_t(page_size) * hkv * d * 2 > INT32_MAX)
+    return fail(SF_ERR_UNSUPPORTED, "a page must be below 2^31 bytes (page_size * hkv * d * 2)");
+  if (batch == 0) return ok();
+  if (!q_new || !k_pages || !v_pages || !block_table || !seq_lens || !o_new)
+    return fail(SF_ERR_INVALID, "null q_new, page pool, block_table, seq_lens or o_new");
+  int64_t pe = num_pages, qe = batch, te = batch;
+  if (!mul_ok(pe, page_size) || !mul_ok(pe, hkv) || !mul_ok(pe, d) || !mul_ok(qe, n) || !mul_ok(qe, hq) ||
+      !mul_ok(qe, d) || !mul_ok(te, n) || !mul_ok(te, max_pages) || pe > (int64_t(1) << 40))
+    return fail(SF_ERR_INVALID, "tensor size overflows");
+  if (!aligned(q_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o_new, 16))
+    return fail(SF_ERR_UNSUPPORTED, "q_new, page pools and o_new must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(SF_ERR_INVALID, "block_table and seq_lens must be 4-byte aligned");
+  if (overlaps(o_new, qe * 2, q_new, qe * 2) || overlaps(o_new, qe * 2, k_pages, pe * 2) ||
+      overlaps(o_new, qe * 2, v_pages, pe * 2) || overlaps(o_new, qe * 2, block_table, te * 4) ||
+      overlaps(o_new, qe * 2, seq_lens, batch * 4))
+    return fail(SF_ERR_INVALID, "o_new overlaps an input");
+  const sfa::DecodePlan plan = sfa::plan_decode(batch, n, max_T, hq, hkv, d, mode, window, num_splits, true);
+  if (plan.units > 65535)
+    return fail(SF_ERR_UNSUPPORTED, "decode supports at most 65535 key ranges (batch*hkv%s = %lld)",
+                mode == SF_INTRA ? "*n" : "", (long long)plan.units);
+  if ((plan.ws_bytes > 0 && !workspace) || workspace_bytes < plan.ws_bytes)
+    return fail(SF_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                plan.ws_bytes);
+  if (plan.ws_bytes > 0 && !aligned(workspace, 16))
+    return fail(SF_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  const int64_t wb = int64_t(plan.ws_bytes);
+  if (overlaps(workspace, wb, o_new, qe * 2) || overlaps(workspace, wb, q_new, qe * 2) ||
+      overlaps(workspace, wb, k_pages, pe * 2) || overlaps(workspace, wb, v_pages, pe * 2) ||
+      overlaps(workspace, wb, block_table, te * 4) || overlaps(workspace, wb, seq_lens, batch * 4))
+    return fail(SF_ERR_INVALID, "workspace overlaps a tensor");
+  sfa::DecodeArgs a{q_new, k_pages, v_pages, o_new, batch, n, max_T, max_T, hq, hkv, d, mode,
+                    window, scale, num_splits, workspace};
+  a.seq_lens = seq_lens;
+  a.table = block_table;
+  a.page = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  return device_status(sfa::launch_attn_decode(a, plan, stream), "sf_attn_decode_paged launch");
 }
 
 }  // extern "C"

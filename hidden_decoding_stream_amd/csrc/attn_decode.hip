@@ -75,6 +75,12 @@ struct DecParams {
   int32_t window;    // 0: none
   float c;           // scale * log2(e)
   int32_t splits, chunk, keys;
+  // paged cache (T above is then the largest valid length, max_T)
+  const int32_t* seq_lens;   // [batch]
+  const int32_t* table;      // [batch][n][max_pages] page of each (stream, logical page)
+  FastDiv page;              // tokens per page (a multiple of the step)
+  int64_t max_pages, num_pages;
+  size_t page_elems;         // elements per page: page * hkv * d
 };
 
 // One wave's step: 32 rows of K then 32 rows of V, d elements each.
@@ -104,7 +110,7 @@ template <int D> __device__ __forceinline__ int swv(int k) {
   else return (k & 2) | ((k >> 1) & 4);
 }
 
-template <int D>
+template <int D, int RB, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   using SG = Stage<D>;
   constexpr int KC = D / 32;              // 32-wide d steps of the 16x16x32 MFMA
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   // of that stage. Each unrolled step below names its stage at compile time,
   // so the compiler can tell that the DMA in flight writes another array
   // than the one being read and adds no wait for it. The merge area at the
-  // end aliases stage 0.
+  // end (one 16-row block at a time) aliases stage 0.
   constexpr int kStageElems = kWaves * 2 * SG::TILE;
   static_assert(sizeof(Merge) <= kStageElems * 2, "merge area must fit in stage 0");
   __shared__ __attribute__((aligned(16))) u16 st0[kStageElems];
@@ -146,24 +152,49 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     kvh = unit % p.hkv;
     b = unit / p.hkv;
   }
-  // query row of this lane's B-operand column
-  const int r = l16;
-  const bool rvalid = r < p.R;
-  const int rs = p.intra ? s_unit : (rvalid ? r / p.G : 0);     // stream of the row
-  const int rh = kvh * p.G + (p.intra ? r : r % p.G);           // query head of the row
-  const int pq = (p.T - 1) * p.n + rs;                           // its expanded position
+  // Cache length of this batch element and its key index space. A paged
+  // sequence brings its own length; one outside [1, max_T] gets no keys (its
+  // rows come out NaN). Its first visited token is rounded down to a multiple
+  // of the step so that no step straddles two pages (the mask drops the
+  // extra tokens).
+  int T = p.T, t_lo = p.t_lo, kps = p.kps, keys = p.keys;
+  if constexpr (PAGED) {
+    T = p.seq_lens[b];
+    if (T < 1 || T > p.T) T = 0;
+    t_lo = 0;
+    if (p.window > 0) {
+      const int oldest = (T - 1) * p.n - p.window + 1;
+      if (oldest > 0) t_lo = (oldest / p.n) & ~(kStep - 1);
+    }
+    kps = (T - t_lo + kStep - 1) / kStep * kStep;
+    keys = (p.intra ? 1 : p.n) * kps;
+  }
+  // query rows of this lane's B-operand columns, one per 16-row block
+  bool rvalid[RB];
+  int rs[RB], rh[RB], pq[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + l16;
+    rvalid[rb] = r < p.R;
+    rs[rb] = p.intra ? s_unit : (rvalid[rb] ? r / p.G : 0);       // stream of the row
+    rh[rb] = kvh * p.G + (p.intra ? r : r % p.G);                 // query head of the row
+    pq[rb] = (T - 1) * p.n + rs[rb];                              // its expanded position
+  }
 
-
-  const size_t stream_stride = (size_t)p.Tmax * p.hkv * D;      // elements between streams
   const uint32_t trow_b = uint32_t(p.hkv) * D * 2;              // bytes between tokens
-  // Bytes from a stream's (token 0, kv head) to the end of token T-1's rows:
-  // every row t < T lies inside, every row t >= T outside (reads zeros).
-  const uint32_t range_b = uint32_t(p.T) * trow_b - uint32_t(kvh) * D * 2;
-  const u16* kbase = p.kc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
-  const u16* vbase = p.vc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
+  const size_t stream_stride = (size_t)p.Tmax * p.hkv * D;      // elements between streams (contiguous cache)
+  const u16* kbase;
+  const u16* vbase;
+  if constexpr (PAGED) {
+    kbase = p.kc + (size_t)kvh * D;
+    vbase = p.vc + (size_t)kvh * D;
+  } else {
+    kbase = p.kc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
+    vbase = p.vc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
+  }
 
   const int j_begin = split * p.chunk;
-  const int j_end = min(p.keys, j_begin + p.chunk);
+  const int j_end = min(keys, j_begin + p.chunk);
   const int nsteps = j_end > j_begin ? (j_end - j_begin + kStep - 1) / kStep : 0;
   const int nu = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;   // steps of this wave
 
@@ -188,16 +219,38 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
 
   auto step_pos = [&](int u, int& sp, int& t0) {
     const int j0 = j_begin + (wave + u * kWaves) * kStep;
-    const int ss = j0 / p.kps;
+    const int ss = j0 / kps;
     sp = p.intra ? s_unit : ss;
-    t0 = p.t_lo + (j0 - ss * p.kps);
+    t0 = t_lo + (j0 - ss * kps);
   };
   auto issue = [&](int u, auto S) {
     int sp, t0;
     step_pos(u, sp, t0);
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + (size_t)sp * stream_stride, range_b);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + (size_t)sp * stream_stride, range_b);
-    const uint32_t sbase = uint32_t(t0) * trow_b;
+    const u16* kb;
+    const u16* vb;
+    uint32_t range, sbase;
+    if constexpr (PAGED) {
+      // the step lies in one page: look it up; rows past token T-1 (and a
+      // page index outside the pool) fall outside the range and read zeros
+      const uint32_t lp = fdiv(uint32_t(t0), p.page);
+      const int tp0 = int(lp * p.page.d);
+      const int pg = p.table[((size_t)b * p.n + sp) * p.max_pages + lp];
+      const bool pg_ok = pg >= 0 && int64_t(pg) < p.num_pages;
+      const size_t pbase = size_t(pg_ok ? pg : 0) * p.page_elems;
+      kb = kbase + pbase;
+      vb = vbase + pbase;
+      range = pg_ok ? uint32_t(min(int(p.page.d), T - tp0)) * trow_b - uint32_t(kvh) * D * 2 : 0u;
+      sbase = uint32_t(t0 - tp0) * trow_b;
+    } else {
+      // bytes from a stream's (token 0, kv head) to the end of token T-1's
+      // rows: every row t < T lies inside, every row t >= T outside
+      kb = kbase + (size_t)sp * stream_stride;
+      vb = vbase + (size_t)sp * stream_stride;
+      range = uint32_t(T) * trow_b - uint32_t(kvh) * D * 2;
+      sbase = uint32_t(t0) * trow_b;
+    }
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, range);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, range);
     u16* kt = stage(S);
     u16* vt = kt + SG::TILE;
     // the step base goes into the per-lane offset: only that offset is
@@ -208,19 +261,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     for (int i = 0; i < NI; ++i) dma16(vrs, vt + i * 512, voff[i] + sbase);
   };
 
-  float m = -INFINITY, lsum = 0.f;
-  f32x4 oacc[DB];
+  float m[RB], lsum[RB];
+  f32x4 oacc[RB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    lsum[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4{};
+  }
 
   // Q is loaded before any DMA goes out, so the wait for it that the compiler
   // places before the first step leaves every stage in flight.
-  bf16x8 qf[KC];
-  {
-    const u16* qrow = p.q + ((size_t)(b * p.n + rs) * p.hq + (rvalid ? rh : 0)) * D;
+  bf16x8 qf[RB][KC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const u16* qrow = p.q + ((size_t)(b * p.n + rs[rb]) * p.hq + (rvalid[rb] ? rh[rb] : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk)
-      qf[kk] = rvalid ? *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * g) : bf16x8{};
+      qf[rb][kk] = rvalid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * g) : bf16x8{};
   }
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -250,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     const u16* kt = stage(S);
     const u16* vt = kt + SG::TILE;
 
-    // K (A operand) and V^T fragments of the whole step
+    // K (A operand) and V^T fragments of the whole step, shared by the row blocks
     bf16x8 ka[2][KC];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -282,55 +341,63 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (u + NS < nu) issue(u + NS, S);
 
-    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    f32x4 sacc[RB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], qf[kk], sacc[kb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[rb][kb] = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk)
+          sacc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], qf[rb][kk], sacc[rb][kb], 0, 0, 0);
+      }
 
-    // mask: this lane holds keys t0 + 8g + 4kb + i of row r
-    const bool edge = (t0 + kStep > p.T - 1) ||
-                      (p.window > 0 && ((p.T - 1) * p.n + p.n - 1) - (t0 * p.n + sp) >= p.window);
-    if (edge || !rvalid) {
+    // mask: this lane holds keys t0 + 8g + 4kb + i of row rb*16 + l16
+    const bool edge = (t0 + kStep > T - 1) ||
+                      (p.window > 0 && ((T - 1) * p.n + p.n - 1) - (t0 * p.n + sp) >= p.window);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (edge || !rvalid[rb]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 8 * g + 4 * kb + i;
+            const int pk = t * p.n + sp;
+            bool ok = rvalid[rb] && t < T;
+            if (!p.intra) ok = ok && pk <= pq[rb];
+            if (p.window > 0) ok = ok && pq[rb] - pk < p.window;
+            if (!ok) sacc[rb][kb][i] = -INFINITY;
+          }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sacc[rb][0][0], sacc[rb][0][1]), fmaxf(sacc[rb][0][2], sacc[rb][0][3])),
+                       fmaxf(fmaxf(sacc[rb][1][0], sacc[rb][1][1]), fmaxf(sacc[rb][1][2], sacc[rb][1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float cand = mx * p.c;
+      const bool need = cand > m[rb] + kRescaleLog2;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m[rb] - cand) : 1.f;
+        if (need) m[rb] = cand;
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+      }
+      const float mu = m[rb] == -INFINITY ? 0.f : m[rb];
+      bf16x8 pf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 8 * g + 4 * kb + i;
-          const int pk = t * p.n + sp;
-          bool ok = rvalid && t < p.T;
-          if (!p.intra) ok = ok && pk <= pq;
-          if (p.window > 0) ok = ok && pq - pk < p.window;
-          if (!ok) sacc[kb][i] = -INFINITY;
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][i], p.c, -mu));
+          lsum[rb] += e;
+          pf[kb * 4 + i] = (__bf16)e;
         }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, oacc[rb][db], 0, 0, 0);
     }
-    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float cand = mx * p.c;
-    const bool need = cand > m + kRescaleLog2;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m - cand) : 1.f;
-      if (need) m = cand;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
-    const float mu = m == -INFINITY ? 0.f : m;
-    bf16x8 pf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], p.c, -mu));
-        lsum += e;
-        pf[kb * 4 + i] = (__bf16)e;
-      }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, oacc[db], 0, 0, 0);
   };
   for (int u0 = 0; u0 < nu; u0 += NS) {
     step(u0, S0{});
@@ -341,44 +408,55 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     }
   }
 
-  // ---- merge the 4 waves in LDS ----
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  __syncthreads();  // every wave is done with its ring (the merge area aliases stage 0)
+  // ---- merge the 4 waves in LDS, one 16-row block at a time ----
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mrg.o[wave][l16][db * 16 + 4 * g + i] = oacc[db][i];
-  if (g == 0) {
-    mrg.m[wave][l16] = m;
-    mrg.l[wave][l16] = lsum;
+  for (int rb = 0; rb < RB; ++rb) {
+    lsum[rb] += __shfl_xor(lsum[rb], 16);
+    lsum[rb] += __shfl_xor(lsum[rb], 32);
   }
-  __syncthreads();
-  for (int idx = tid; idx < p.R * D; idx += kThreads) {
-    const int row = idx / D, d = idx % D;
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg.m[w][row]);
-    float acc = 0.f, lt = 0.f;
-    if (M != -INFINITY) {
+  for (int rb = 0; rb < RB; ++rb) {
+    // every wave is done with its ring (the merge area aliases stage 0), or
+    // with the previous block's merge
+    __syncthreads();
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(mrg.m[w][row] - M);
-        acc += f * mrg.o[w][row][d];
-        lt += f * mrg.l[w][row];
-      }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mrg.o[wave][l16][db * 16 + 4 * g + i] = oacc[rb][db][i];
+    if (g == 0) {
+      mrg.m[wave][l16] = m[rb];
+      mrg.l[wave][l16] = lsum[rb];
     }
-    const int rs2 = p.intra ? s_unit : row / p.G;
-    const int rh2 = kvh * p.G + (p.intra ? row : row % p.G);
-    const size_t orow = (size_t)(b * p.n + rs2) * p.hq + rh2;
-    if (p.splits == 1) {
-      // every row admits at least its own key, so lt > 0
-      p.o[orow * D + d] = __builtin_bit_cast(u16, (__bf16)(acc / lt));
-    } else {
-      p.ws_o[(orow * p.splits + split) * D + d] = acc;
-      if (d == 0) {
-        p.ws_ml[(orow * p.splits + split) * 2 + 0] = M;
-        p.ws_ml[(orow * p.splits + split) * 2 + 1] = lt;
+    __syncthreads();
+    const int nrows = min(16, p.R - rb * 16);
+    for (int idx = tid; idx < nrows * D; idx += kThreads) {
+      const int row = idx / D, d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg.m[w][row]);
+      float acc = 0.f, lt = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = __builtin_amdgcn_exp2f(mrg.m[w][row] - M);
+          acc += f * mrg.o[w][row][d];
+          lt += f * mrg.l[w][row];
+        }
+      }
+      const int r = rb * 16 + row;
+      const int rs2 = p.intra ? s_unit : r / p.G;
+      const int rh2 = kvh * p.G + (p.intra ? r : r % p.G);
+      const size_t orow = (size_t)(b * p.n + rs2) * p.hq + rh2;
+      if (p.splits == 1) {
+        // every row of a valid sequence admits at least its own key, so lt > 0
+        // (an invalid paged length leaves lt = 0: NaN)
+        p.o[orow * D + d] = __builtin_bit_cast(u16, (__bf16)(acc / lt));
+      } else {
+        p.ws_o[(orow * p.splits + split) * D + d] = acc;
+        if (d == 0) {
+          p.ws_ml[(orow * p.splits + split) * 2 + 0] = M;
+          p.ws_ml[(orow * p.splits + split) * 2 + 1] = lt;
+        }
       }
     }
   }
@@ -438,20 +516,30 @@ int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
 }  // namespace
 
 DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t hkv, int32_t d,
-                       int32_t mode, int64_t window, int32_t num_splits) {
+                       int32_t mode, int64_t window, int32_t num_splits, bool paged) {
   DecodePlan pl{};
   const int32_t G = hq / hkv;
   const bool intra = mode == 0;
   pl.rows_per_unit = intra ? G : n * G;
   pl.units = intra ? batch * hkv * n : batch * hkv;
-  // Oldest token any query may see: the earliest query (stream 0 of token T-1)
-  // looks back window-1 positions.
   pl.t_lo = 0;
-  if (mode == 2) {
-    const int64_t oldest = (T - 1) * n - window + 1;
-    if (oldest > 0) pl.t_lo = oldest / n;
+  if (!paged) {
+    // Oldest token any query may see: the earliest query (stream 0 of token
+    // T-1) looks back window-1 positions.
+    if (mode == 2) {
+      const int64_t oldest = (T - 1) * n - window + 1;
+      if (oldest > 0) pl.t_lo = oldest / n;
+    }
+    pl.keys_per_stream = round_up(T - pl.t_lo, kStep);
+  } else {
+    // T is the largest length; each sequence finds its own first token on the
+    // device (oldest / n rounded down to a step). Its span T_b - t_lo is below
+    // 34 + (window-1)/n tokens: oldest / n > T_b - 2 - (window-1)/n and the
+    // rounding takes off at most 31 more.
+    int64_t span = T;
+    if (mode == 2) span = std::min<int64_t>(T, 34 + (window - 1) / n);
+    pl.keys_per_stream = round_up(span, kStep);
   }
-  pl.keys_per_stream = round_up(T - pl.t_lo, kStep);
   pl.keys = (intra ? 1 : n) * pl.keys_per_stream;
   int64_t want = num_splits;
   if (want == 0) {
@@ -497,14 +585,31 @@ hipError_t launch_attn_decode(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.splits = pl.splits;
   p.chunk = int32_t(pl.chunk);
   p.keys = int32_t(pl.keys);
+  const bool paged = a.seq_lens != nullptr;
+  p.seq_lens = a.seq_lens;
+  p.table = a.table;
+  p.page = make_fastdiv(uint32_t(paged ? a.page : 1));
+  p.max_pages = a.max_pages;
+  p.num_pages = a.num_pages;
+  p.page_elems = size_t(a.page) * a.hkv * a.d;
   const dim3 grid(uint32_t(pl.splits), uint32_t(pl.units));
   const dim3 cgrid(uint32_t((rows + 3) / 4));
-  if (a.d == 128) {
-    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-    if (pl.splits > 1) hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(256), 0, stream, p, rows);
-  } else {
-    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(kThreads), 0, stream, p);
-    if (pl.splits > 1) hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(256), 0, stream, p, rows);
+  using Kernel = void (*)(DecParams);
+  // [d == 128][row blocks 1, 2, 4][paged]
+  static constexpr Kernel kSplit[2][3][2] = {
+      {{decode_split_kernel<64, 1, false>, decode_split_kernel<64, 1, true>},
+       {decode_split_kernel<64, 2, false>, decode_split_kernel<64, 2, true>},
+       {decode_split_kernel<64, 4, false>, decode_split_kernel<64, 4, true>}},
+      {{decode_split_kernel<128, 1, false>, decode_split_kernel<128, 1, true>},
+       {decode_split_kernel<128, 2, false>, decode_split_kernel<128, 2, true>},
+       {decode_split_kernel<128, 4, false>, decode_split_kernel<128, 4, true>}}};
+  const int rbi = p.R <= 16 ? 0 : (p.R <= 32 ? 1 : 2);
+  hipLaunchKernelGGL(kSplit[a.d == 128][rbi][paged], grid, dim3(kThreads), 0, stream, p);
+  if (pl.splits > 1) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(256), 0, stream, p, rows);
+    else
+      hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(256), 0, stream, p, rows);
   }
   return hipGetLastError();
 }

@@ -70,6 +70,12 @@ struct DecodeArgs {
   float scale;
   int32_t num_splits;
   void* ws;
+  // paged cache: kc/vc are page pools [num_pages][page][hkv][d], T is the
+  // largest valid length; null seq_lens means the contiguous cache
+  const int32_t* seq_lens = nullptr;
+  const int32_t* table = nullptr;
+  int32_t page = 0;
+  int64_t max_pages = 0, num_pages = 0;
 };
 // Split plan shared by the workspace query and the launcher.
 struct DecodePlan {
@@ -82,8 +88,9 @@ struct DecodePlan {
   int64_t chunk;           // keys per piece (multiple of the step)
   size_t ws_bytes;
 };
+// paged: T is the largest length; the key space then covers any length up to T
 DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t hkv, int32_t d,
-                       int32_t mode, int64_t window, int32_t num_splits);
+                       int32_t mode, int64_t window, int32_t num_splits, bool paged = false);
 hipError_t launch_attn_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
 
 }  // namespace sfa

@@ -159,3 +159,58 @@ def uniform_keys(shape, value: float = 0.0) -> torch.Tensor:
     """Constant keys: every score in a row is equal, so the softmax is uniform
     over whatever keys the mask admits (used to probe masks exactly)."""
     return torch.full(shape, value, dtype=torch.bfloat16)
+
+
+@dataclasses.dataclass(frozen=True)
+class PagedDecodeWorkload:
+    """Decode of a batch of sequences of different lengths (lens[b] tokens in
+    sequence b's per-stream caches) whose caches are spread over pages of
+    `page` tokens."""
+    name: str
+    n: int
+    lens: tuple
+    page: int
+    hq: int
+    hkv: int
+    d: int
+    mode: str
+    window: int = 0
+    seed: int = 0
+    spare_pages: int = 3
+
+    @property
+    def batch(self) -> int:
+        return len(self.lens)
+
+    @property
+    def max_pages(self) -> int:
+        return max(1, max(-(-t // self.page) for t in self.lens))
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32))
+
+
+def paged_decode_inputs(w: PagedDecodeWorkload, device="cpu"):
+    """q_new [batch][n][hq][d], page pools k_pages, v_pages
+    [num_pages][page][hkv][d] (bf16), block_table int32 [batch][n][max_pages]
+    and seq_lens int32 [batch]. Each (sequence, stream) gets its own pages
+    for its tokens, at places drawn by a random permutation of the pool;
+    table entries past a sequence's last page are -1 (never read). Drawn in
+    that order: q_new, K pages, V pages, the permutation."""
+    g = _gen(w.seed, device)
+    used = [-(-t // w.page) for t in w.lens]
+    need = sum(u * w.n for u in used)
+    num_pages = need + w.spare_pages
+    q = to_bf16(normal((w.batch, w.n, w.hq, w.d), g))
+    kp = to_bf16(normal((num_pages, w.page, w.hkv, w.d), g))
+    vp = to_bf16(normal((num_pages, w.page, w.hkv, w.d), g))
+    perm = torch.randperm(num_pages, generator=g, device=device).to(torch.int32)
+    table = torch.full((w.batch, w.n, w.max_pages), -1, dtype=torch.int32, device=device)
+    i = 0
+    for b, u in enumerate(used):
+        for k in range(w.n):
+            table[b, k, :u] = perm[i:i + u]
+            i += u
+    lens = torch.tensor(w.lens, dtype=torch.int32, device=device)
+    return q, kp, vp, table, lens

@@ -74,6 +74,13 @@ def lib() -> ctypes.CDLL:
                                  c.c_int64, c.c_int32, c.c_int64, c.c_int64, c.c_int32, c.c_int32,
                                  c.c_int32, c.c_int32, c.c_int64, c.c_float, c.c_int32,
                                  c.c_void_p, c.c_size_t, c.c_void_p]
+    L.sf_attn_decode_paged_workspace_bytes.restype = c.c_size_t
+    L.sf_attn_decode_paged_workspace_bytes.argtypes = L.sf_attn_decode_workspace_bytes.argtypes
+    L.sf_attn_decode_paged.restype = c.c_int
+    L.sf_attn_decode_paged.argtypes = [c.c_void_p] * 6 + [c.c_int64, c.c_int32, c.c_int64, c.c_int64, c.c_int32,
+                                                          c.c_int64, c.c_int32, c.c_int32, c.c_int32, c.c_int32,
+                                                          c.c_int64, c.c_float, c.c_int32, c.c_void_p, c.c_size_t,
+                                                          c.c_void_p]
     _lib_handle = L
     return L
 
@@ -273,4 +280,48 @@ def sf_attn_decode(q_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                 hq, hkv, d, _mode(mode), int(window), float(scale), int(num_splits),
                                 _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
+    return out
+
+
+def sf_attn_decode_paged_workspace_bytes(batch: int, n: int, max_T: int, hq: int, hkv: int, d: int, mode,
+                                         window: int = 0, num_splits: int = 0) -> int:
+    return int(lib().sf_attn_decode_paged_workspace_bytes(batch, n, int(max_T), hq, hkv, d, _mode(mode),
+                                                          int(window), int(num_splits)))
+
+
+def sf_attn_decode_paged(q_new: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                         block_table: torch.Tensor, seq_lens: torch.Tensor, mode, max_T: int | None = None,
+                         window: int = 0, scale: float | None = None, num_splits: int = 0,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Decode each sequence's n stream queries of its newest token against a
+    paged per-stream cache. q_new [B][n][hq][d]; page pools
+    [num_pages][page][hkv][d] bf16; block_table int32 [B][n][max_pages];
+    seq_lens int32 [B] on the device. max_T bounds seq_lens (default: what
+    the block table can hold). The workspace is allocated with torch when not
+    given."""
+    B, n, hq, d = q_new.shape
+    num_pages, page, hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if k_pages.shape != (num_pages, page, hkv, d) or v_pages.shape != k_pages.shape:
+        raise ValueError("page pools must be [num_pages][page][hkv][d] matching q_new")
+    if block_table.dim() != 3 or block_table.shape[:2] != (B, n):
+        raise ValueError("block_table must be [B][n][max_pages]")
+    if seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be [B]")
+    max_pages = block_table.shape[2]
+    if max_T is None:
+        max_T = max_pages * page
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q_new)
+    need = sf_attn_decode_paged_workspace_bytes(B, n, max_T, hq, hkv, d, mode, window, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_new.device)
+    bf, i32 = torch.bfloat16, torch.int32
+    _check(lib().sf_attn_decode_paged(
+        _dev(q_new, "q_new", bf), _dev(k_pages, "k_pages", bf), _dev(v_pages, "v_pages", bf),
+        _dev(block_table, "block_table", i32), _dev(seq_lens, "seq_lens", i32), _dev(out, "out", bf),
+        B, n, int(max_T), num_pages, page, max_pages, hq, hkv, d, _mode(mode), int(window), float(scale),
+        int(num_splits), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return out

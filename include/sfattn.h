@@ -201,8 +201,8 @@ size_t sf_attn_decode_workspace_bytes(int64_t batch, int32_t n, int64_t T, int32
  *   num_splits: how many pieces each key range is cut into (0 = chosen by the
  *               library from the problem size; at most 1024 are used). The
  *               result does not depend on it beyond float rounding.
- * Supported: d in {64, 128}; hq % hkv == 0; n*G <= 16 query rows per key/value
- * head under the cross masks (G = hq/hkv), G <= 16 under SF_INTRA; 16-byte
+ * Supported: d in {64, 128}; hq % hkv == 0; n*G <= 64 query rows per key/value
+ * head under the cross masks (G = hq/hkv), G <= 64 under SF_INTRA; 16-byte
  * aligned q_new, caches and o_new; T_max*hkv*d*2 < 2^31 (bytes of one
  * stream's cache of one batch element). */
 sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_cache, void* o_new,
@@ -210,6 +210,43 @@ sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_c
                          int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,
                          int32_t num_splits, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Bytes of device workspace sf_attn_decode_paged needs (0 if the arguments
+ * are invalid or the problem is empty); max_T and num_splits as there. */
+size_t sf_attn_decode_paged_workspace_bytes(int64_t batch, int32_t n, int64_t max_T, int32_t hq,
+                                            int32_t hkv, int32_t d, int32_t mode, int64_t window,
+                                            int32_t num_splits);
+
+/* sf_attn_decode for a batch of sequences of different lengths whose
+ * per-stream caches are spread over fixed-size pages. For serving: the
+ * production decode the pages describe ([HD-tahou] 实验效果与成本分析, decode
+ * at small batch is bound by memory bandwidth) runs many sequences of
+ * different lengths at once.
+ *   q_new, o_new : bf16 [batch][n][hq][d]; row k of sequence b is stream k of
+ *                  its newest token T_b - 1 (expanded position (T_b-1)*n + k).
+ *   k_pages, v_pages : bf16 page pools [num_pages][page_size][hkv][d].
+ *   block_table : int32 [batch][n][max_pages], device: token t of stream k of
+ *                  sequence b is row t mod page_size of page
+ *                  block_table[b][k][t / page_size]. Only the entries of pages
+ *                  below T_b are read; an entry outside [0, num_pages) is read
+ *                  as a page of zeros (nothing outside the pools is touched).
+ *   seq_lens : int32 [batch], device: T_b, the tokens in sequence b's cache,
+ *              token T_b - 1's n rows already written. A value outside
+ *              [1, max_T] makes that sequence's output rows NaN.
+ *   max_T : an upper bound of every T_b, known on the host; it sizes the
+ *           split plan and the workspace (with SF_CROSS_WINDOW only the last
+ *           window positions count, so a large max_T costs nothing there).
+ * Each sequence's result equals sf_attn_decode over its own T_b tokens with
+ * the cache gathered from its pages.
+ * Supported: as sf_attn_decode, plus page_size a multiple of 32 tokens,
+ * max_pages * page_size >= max_T, page_size*hkv*d*2 < 2^31 and
+ * n*max_T < 2^31; block_table and seq_lens 4-byte aligned. */
+sf_status sf_attn_decode_paged(const void* q_new, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seq_lens, void* o_new,
+                               int64_t batch, int32_t n, int64_t max_T, int64_t num_pages,
+                               int32_t page_size, int64_t max_pages, int32_t hq, int32_t hkv, int32_t d,
+                               int32_t mode, int64_t window, float scale, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

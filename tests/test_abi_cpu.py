@@ -32,6 +32,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"sf_interleave", "sf_expand_embed", "sf_rope", "sf_attn_fwd", "sf_attn_fwd_last_stream",
             "sf_attn_bwd", "sf_attn_bwd_workspace_bytes", "sf_attn_decode", "sf_attn_decode_workspace_bytes",
+            "sf_attn_decode_paged", "sf_attn_decode_paged_workspace_bytes",
             "sf_abi_version", "sf_last_error"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
@@ -116,8 +117,8 @@ def dec(q=P, kc=P2, vc=P3, o=P4, batch=1, n=4, T=16, Tmax=16, hq=32, hkv=8, d=12
     (dict(T=17), B.SF_ERR_INVALID),                  # T > T_max
     (dict(batch=-1), B.SF_ERR_INVALID),
     (dict(splits=-1), B.SF_ERR_INVALID),
-    (dict(n=8), B.SF_ERR_UNSUPPORTED),                # n*G = 32 > 16 rows under cross
-    (dict(hq=32, hkv=1, mode=0), B.SF_ERR_UNSUPPORTED),  # G = 32 > 16 under intra
+    (dict(n=17), B.SF_ERR_UNSUPPORTED),               # n*G = 68 > 64 rows under cross
+    (dict(hq=128, hkv=1, mode=0), B.SF_ERR_UNSUPPORTED),  # G = 128 > 64 under intra
     (dict(d=80), B.SF_ERR_UNSUPPORTED),
     (dict(mode=2, window=0), B.SF_ERR_INVALID),
     (dict(ws=None, splits=2, T=200, Tmax=200), B.SF_ERR_INVALID),   # two splits need a workspace
@@ -145,6 +146,60 @@ def test_workspace_query():
     assert sfa.sf_attn_decode_workspace_bytes(0, 4, 8192, 32, 8, 128, "intra") == 0
     assert sfa.sf_attn_decode_workspace_bytes(1, 4, 0, 32, 8, 128, "intra") == 0
     assert sfa.sf_attn_decode_workspace_bytes(1, 4, 16, 32, 8, 96, "intra") == 0
+
+
+def test_decode_accepts_more_rows_per_kv_head():
+    """n*G up to 64 rows per kv head (e.g. n = 8 streams with G = 8): only
+    the argument checks run, on a null-sized workspace query."""
+    assert sfa.sf_attn_decode_workspace_bytes(1, 8, 1024, 64, 8, 128, "cross_full") > 0
+    assert dec(batch=0, n=8, hq=64) == B.SF_OK
+    assert dec(batch=0, n=16, hq=32) == B.SF_OK
+    assert dec(batch=0, hq=64, hkv=1, mode=0) == B.SF_OK
+
+
+def pdec(q=P, kp=P2, vp=P3, table=ctypes.c_void_p(0x20000000), lens=ctypes.c_void_p(0x30000000), o=P4,
+         batch=2, n=4, max_T=100, num_pages=64, page=32, max_pages=4, hq=32, hkv=8, d=128, mode=1, window=0,
+         scale=0.088, splits=0, ws=ctypes.c_void_p(0x100000000), wsb=1 << 30):
+    return L.sf_attn_decode_paged(q, kp, vp, table, lens, o, batch, n, max_T, num_pages, page, max_pages, hq,
+                                  hkv, d, mode, window, scale, splits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(max_T=0), B.SF_ERR_INVALID),
+    (dict(batch=-1), B.SF_ERR_INVALID),
+    (dict(num_pages=0), B.SF_ERR_INVALID),
+    (dict(page=0), B.SF_ERR_INVALID),
+    (dict(page=48), B.SF_ERR_UNSUPPORTED),            # not a multiple of 32 tokens
+    (dict(max_pages=3), B.SF_ERR_INVALID),            # 3 pages of 32 cannot hold 100 tokens
+    (dict(splits=-1), B.SF_ERR_INVALID),
+    (dict(n=17), B.SF_ERR_UNSUPPORTED),               # 68 rows per kv head
+    (dict(d=96), B.SF_ERR_UNSUPPORTED),
+    (dict(mode=2, window=0), B.SF_ERR_INVALID),
+    (dict(page=1 << 20, max_pages=1), B.SF_ERR_UNSUPPORTED),   # a page of 2^31 bytes
+    (dict(max_T=1 << 30, max_pages=1 << 25), B.SF_ERR_UNSUPPORTED),   # n * max_T >= 2^31
+    (dict(table=None), B.SF_ERR_INVALID),
+    (dict(lens=None), B.SF_ERR_INVALID),
+    (dict(lens=ctypes.c_void_p(0x30000002)), B.SF_ERR_INVALID),
+    (dict(kp=ctypes.c_void_p(0x40000008)), B.SF_ERR_UNSUPPORTED),
+    (dict(o=ctypes.c_void_p(0x20000000)), B.SF_ERR_INVALID),   # output overlaps the block table
+    (dict(ws=None, splits=2), B.SF_ERR_INVALID),
+    (dict(wsb=16, splits=2), B.SF_ERR_INVALID),
+])
+def test_decode_paged_rejects(kw, status):
+    assert pdec(**kw) == status
+
+
+def test_decode_paged_empty_batch_and_workspace_query():
+    assert pdec(batch=0) == B.SF_OK
+    # one split: no workspace; two: rows * 2 * (d + 2) floats
+    assert sfa.sf_attn_decode_paged_workspace_bytes(2, 4, 100, 32, 8, 128, "cross_full", num_splits=1) == 0
+    rows = 2 * 4 * 32
+    assert (sfa.sf_attn_decode_paged_workspace_bytes(2, 4, 100, 32, 8, 128, "cross_full", num_splits=2)
+            == -(-rows * 2 * 128 * 4 // 256) * 256 + -(-rows * 2 * 2 * 4 // 256) * 256)
+    assert sfa.sf_attn_decode_paged_workspace_bytes(2, 4, 0, 32, 8, 128, "intra") == 0
+    # a window bounds the keys a sequence can see, whatever max_T is
+    w = sfa.sf_attn_decode_paged_workspace_bytes(1, 4, 1 << 20, 32, 8, 128, "cross_window", window=4096)
+    assert 0 < w <= sfa.sf_attn_decode_workspace_bytes(1, 4, 1 << 20, 32, 8, 128, "cross_full")
 
 
 def emb(ids=P, tables=P2, out=P3, batch=2, n=4, Lt=16, vocab=100, row=64):

@@ -29,6 +29,15 @@ SMALL = [
     (1, 3, 1, 4, 6, 2, 128, "cross_full", 0),          # a single token
     (1, 1, 500, 512, 16, 1, 128, "cross_full", 0),     # n = 1, G = 16
     (2, 4, 1000, 1000, 32, 8, 128, "cross_full", 0),
+    # more query rows per kv head than one 16-row block: n = 8 (the pages' probe), larger G
+    (1, 8, 70, 80, 16, 4, 128, "cross_full", 0),         # 32 rows
+    (1, 8, 70, 80, 16, 4, 128, "cross_window", 100),
+    (2, 8, 40, 40, 8, 1, 64, "cross_full", 0),           # 64 rows
+    (1, 16, 33, 40, 8, 2, 128, "cross_full", 0),         # n = 16: 64 rows
+    (1, 3, 50, 60, 16, 2, 128, "cross_full", 0),         # 24 rows: second block half used
+    (1, 6, 45, 50, 16, 2, 64, "cross_window", 40),       # 48 rows
+    (1, 4, 60, 64, 64, 2, 128, "intra", 0),              # G = 32 under intra
+    (1, 2, 60, 64, 64, 1, 64, "intra", 0),               # G = 64 under intra
 ]
 
 
@@ -45,10 +54,11 @@ def test_small_vs_oracle(case, splits):
     assert_close(np64(o), ref, f"{case} splits={splits}")
 
 
+@pytest.mark.parametrize("n,hq,hkv", [(4, 8, 2), (8, 16, 2)])
 @pytest.mark.parametrize("mode,W", [("intra", 0), ("cross_full", 0), ("cross_window", 45)])
-def test_decode_is_last_rows_of_prefill(mode, W):
-    B, n, T, hq, hkv, d = 1, 4, 300, 8, 2, 128
-    say("decode vs prefill", mode)
+def test_decode_is_last_rows_of_prefill(mode, W, n, hq, hkv):
+    B, T, d = 1, 300, 128
+    say("decode vs prefill", mode, n)
     w = I.DecodeWorkload("t", n, T, T, B, hq, hkv, d, mode, window=W, seed=3)
     q, kc, vc = (t.cuda() for t in I.decode_inputs(w))
     o = sfa.sf_attn_decode(q, kc, vc, T, mode, window=W, scale=_scale(d))

@@ -1,0 +1,127 @@
+"""sf_attn_decode_paged on the GPU: sequences of different lengths against a
+paged per-stream cache, compared with the fp64 oracle (decode_paged), with the
+contiguous-cache decode on identically paged data (bitwise), and on invalid
+lengths and page indices."""
+import numpy as np
+import pytest
+import torch
+
+import hidden_decoding_stream_amd as sfa
+import hidden_decoding_stream_amd.inputs as I
+import oracle.sfa as orc
+from gpu_util import assert_close, np64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(w, q, kp, vp, table, lens, rows=None):
+    """Oracle on the sequences `rows` (all by default), fed only their pages."""
+    rows = range(w.batch) if rows is None else rows
+    out = []
+    for b in rows:
+        tb = table[b].cpu().numpy()
+        used = np.unique(tb[tb >= 0])
+        remap = np.full(tb.shape, 0, dtype=np.int64)
+        remap[tb >= 0] = np.searchsorted(used, tb[tb >= 0])
+        idx = torch.from_numpy(used).to(kp.device).long()
+        out.append(orc.decode_paged(np64(q[b:b + 1]), np64(kp[idx]), np64(vp[idx]), remap[None],
+                                    lens[b:b + 1].cpu().numpy(), w.mode, window=w.window or None,
+                                    scale=w.scale)[0])
+    return np.stack(out)
+
+
+CASES = [
+    # n, lens, page, hq, hkv, d, mode, window
+    (4, (37, 1, 64), 32, 8, 2, 128, "cross_full", 0),
+    (4, (37, 1, 64), 32, 8, 2, 128, "intra", 0),
+    (4, (37, 1, 64), 32, 8, 2, 128, "cross_window", 33),
+    (8, (100, 65), 64, 16, 4, 128, "cross_window", 70),       # 32 rows per kv head
+    (8, (100, 65), 64, 16, 4, 128, "cross_full", 0),
+    (2, (300, 5, 129, 256), 32, 8, 1, 64, "intra", 0),
+    (4, (500, 1000), 256, 32, 8, 128, "cross_full", 0),
+    (4, (1000, 997, 31), 128, 32, 8, 128, "cross_window", 130),
+    (3, (40, 90), 32, 32, 2, 64, "cross_full", 0),           # G = 16: 48 rows, the last row block unused
+]
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_small_vs_oracle(case, splits):
+    n, lens, page, hq, hkv, d, mode, W = case
+    say("paged decode", case, "splits", splits)
+    w = I.PagedDecodeWorkload("t", n, lens, page, hq, hkv, d, mode, window=W, seed=sum(lens) + page)
+    q, kp, vp, table, sl = (t.cuda() for t in I.paged_decode_inputs(w))
+    o = sfa.sf_attn_decode_paged(q, kp, vp, table, sl, mode, max_T=max(lens), window=W, scale=w.scale,
+                                 num_splits=splits)
+    torch.cuda.synchronize()
+    assert_close(np64(o), _oracle(w, q, kp, vp, table, sl), f"paged {case} splits={splits}")
+
+
+@pytest.mark.parametrize("mode", ["intra", "cross_full"])
+def test_equals_contiguous_decode_bitwise(mode):
+    """A contiguous cache [B][n][T_max][hkv][d] is a paged pool whose table
+    walks it in order; with the same split count the two entry points run the
+    same arithmetic."""
+    B, n, T, Tm, page, hq, hkv, d = 2, 4, 1000, 1024, 64, 32, 8, 128
+    say("paged == contiguous", mode)
+    w = I.DecodeWorkload("t", n, T, Tm, B, hq, hkv, d, mode, seed=77)
+    q, kc, vc = (t.cuda() for t in I.decode_inputs(w))
+    per = Tm // page
+    table = torch.arange(B * n * per, dtype=torch.int32, device="cuda").view(B, n, per)
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    kp, vp = kc.view(B * n * per, page, hkv, d), vc.view(B * n * per, page, hkv, d)
+    for splits in (1, 5):
+        a = sfa.sf_attn_decode(q, kc, vc, T, mode, scale=w.scale, num_splits=splits)
+        b = sfa.sf_attn_decode_paged(q, kp, vp, table, lens, mode, max_T=T, scale=w.scale, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (mode, splits)
+
+
+def test_invalid_lengths_give_nan_rows():
+    """Lengths outside [1, max_T] (seq_lens lives on the device, so the host
+    cannot reject them) make that sequence's rows NaN; the others are exact."""
+    w = I.PagedDecodeWorkload("t", 4, (50, 50, 50, 50), 32, 8, 2, 128, "cross_full", seed=5)
+    q, kp, vp, table, sl = (t.cuda() for t in I.paged_decode_inputs(w))
+    sl_bad = torch.tensor([50, 0, -3, 51], dtype=torch.int32, device="cuda")
+    say("paged invalid lengths")
+    for splits in (1, 2):
+        o = sfa.sf_attn_decode_paged(q, kp, vp, table, sl_bad, "cross_full", max_T=50, scale=w.scale,
+                                     num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.isnan(o[1:].float()).all(), splits
+        assert_close(np64(o[:1]), _oracle(w, q, kp, vp, table, sl, rows=[0]), f"valid row, splits={splits}")
+
+
+def test_page_outside_pool_reads_zeros():
+    """A table entry outside [0, num_pages) reads as a page of zeros: the
+    result equals the oracle on a pool with an all-zero page in its place."""
+    w = I.PagedDecodeWorkload("t", 4, (100, 70), 32, 8, 2, 128, "cross_full", seed=6)
+    q, kp, vp, table, sl = (t.cuda() for t in I.paged_decode_inputs(w))
+    bad = table.clone()
+    bad[0, 1, 1] = kp.shape[0] + 7
+    bad[1, 3, 0] = -5
+    say("paged page outside the pool")
+    o = sfa.sf_attn_decode_paged(q, kp, vp, bad, sl, "cross_full", max_T=100, scale=w.scale)
+    zk = torch.cat([kp, torch.zeros_like(kp[:1])])
+    zv = torch.cat([vp, torch.zeros_like(vp[:1])])
+    fixed = bad.clone()
+    fixed[0, 1, 1] = kp.shape[0]
+    fixed[1, 3, 0] = kp.shape[0]
+    torch.cuda.synchronize()
+    assert_close(np64(o), _oracle(w, q, zk, zv, fixed, sl), "zero pages")
+
+
+@pytest.mark.parametrize("mode,W", [("cross_full", 0), ("intra", 0), ("cross_window", 4096)])
+def test_full_size_mixed_lengths(mode, W):
+    """Serving batch: 8 sequences of 1..8192 tokens x 4 streams, 32/8 heads,
+    d = 128, pages of 256 tokens; the oracle on three of them."""
+    lens = (8192, 1, 4096, 8191, 33, 2048, 7000, 257)
+    w = I.PagedDecodeWorkload("serve", 4, lens, 256, 32, 8, 128, mode, window=W, seed=1006)
+    say("paged full size", mode)
+    q, kp, vp, table, sl = I.paged_decode_inputs(w, device="cuda")
+    o = sfa.sf_attn_decode_paged(q, kp, vp, table, sl, mode, max_T=8192, window=W, scale=w.scale)
+    o2 = sfa.sf_attn_decode_paged(q, kp, vp, table, sl, mode, max_T=8192, window=W, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2), "deterministic"
+    rows = [0, 1, 4, 6]
+    assert_close(np64(o[rows]), _oracle(w, q, kp, vp, table, sl, rows=rows), f"serve {mode}")
