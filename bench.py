@@ -228,6 +228,7 @@ def main():
     line["backward"] = backward_timing(torch, sfa, C, Q, K, V, Oc, n, L, B, hq, hkv, d, scale, dev, stream)
     if not args.no_decode_sweep:
         line["decode"] = decode_sweep(torch, sfa, C, I, dev)
+        line["serving"] = serving_sweep(torch, sfa, C, I, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, C, I, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -369,6 +370,81 @@ def decode_sweep(torch, sfa, C, I, dev):
                                        "caches_rotated": copies}
             print(f"[bench] decode b={batch} {mode}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
             del caches, q, o, ws
+            torch.cuda.empty_cache()
+    return out
+
+
+def _rotated_time(torch, calls, reps=20):
+    """Mean microseconds per call, cycling through `calls` (one per distinct
+    copy of the data) after 3 untimed calls."""
+    for i in range(3):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        calls[i % len(calls)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def serving_sweep(torch, sfa, C, I, dev, budget=16 << 30):
+    """Decode in its serving variants: the cross_window mask (W = 4096
+    positions), n = 8 streams (32 query rows per kv head), and the paged cache
+    with per-sequence lengths. Every call's data is rotated over >= 1 GiB of
+    distinct reads (within `budget` bytes of caches)."""
+    out = {}
+
+    def record(key, us, nbytes, copies):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[key] = {"us": round(us, 2), "GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                    "bytes": nbytes, "copies_rotated": copies}
+        print(f"[bench] serving {key}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+
+    g = torch.Generator(device=dev).manual_seed(1007)
+
+    def bf16(*shape):
+        return torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+
+    # contiguous cache: windowed decode and n = 8
+    for tag, n, T, mode, W in (("window4096", 4, 8192, "cross_window", 4096),
+                               ("n8_cross_full", 8, 4096, "cross_full", 0),
+                               ("n8_intra", 8, 4096, "intra", 0)):
+        for batch in (1, 8, 64):
+            hq, hkv, d = 32, 8, 128
+            nbytes = C.decode_bytes(mode, n, T, batch, hq, hkv, d, window=W)
+            cache_bytes = 2 * batch * n * T * hkv * d * 2
+            copies = max(1, min(math.ceil((1 << 30) / nbytes), budget // cache_bytes))
+            q = bf16(batch, n, hq, d)
+            caches = [(bf16(batch, n, T, hkv, d), bf16(batch, n, T, hkv, d)) for _ in range(copies)]
+            o = torch.empty_like(q)
+            ws = torch.empty(sfa.sf_attn_decode_workspace_bytes(batch, n, T, hq, hkv, d, mode, W) + 16,
+                             dtype=torch.uint8, device=dev)
+            scale = 1.0 / math.sqrt(d)
+            calls = [lambda kc=kc, vc=vc: sfa.sf_attn_decode(q, kc, vc, T, mode, window=W, scale=scale, out=o,
+                                                             workspace=ws) for kc, vc in caches]
+            record(f"{tag}_b{batch}", _rotated_time(torch, calls), nbytes, copies)
+            del caches, calls, q, o, ws
+            torch.cuda.empty_cache()
+
+    # paged cache, pages of 256 tokens: every sequence at 8192 tokens, and a
+    # batch of lengths drawn uniformly from 1..8192
+    n, hq, hkv, d, page = 4, 32, 8, 128, 256
+    lg = torch.Generator().manual_seed(1008)
+    for tag, batch, lens in (("paged_b8_8192", 8, [8192] * 8), ("paged_b64_8192", 64, [8192] * 64),
+                             ("paged_b64_mixed", 64, torch.randint(1, 8193, (64,), generator=lg).tolist())):
+        for mode in ("intra", "cross_full"):
+            w = I.PagedDecodeWorkload(tag, n, tuple(lens), page, hq, hkv, d, mode, seed=1009, spare_pages=0)
+            q, kp, vp, table, sl = I.paged_decode_inputs(w, device=dev)
+            nbytes = sum(C.decode_bytes(mode, n, T, 1, hq, hkv, d) for T in lens)
+            o = torch.empty_like(q)
+            ws = torch.empty(sfa.sf_attn_decode_paged_workspace_bytes(batch, n, 8192, hq, hkv, d, mode) + 16,
+                             dtype=torch.uint8, device=dev)
+            call = lambda: sfa.sf_attn_decode_paged(q, kp, vp, table, sl, mode, max_T=8192,  # noqa: E731
+                                                    scale=w.scale, out=o, workspace=ws)
+            record(f"{tag}_{mode}", _rotated_time(torch, [call]), nbytes, 1)
+            del q, kp, vp, table, sl, o, ws
             torch.cuda.empty_cache()
     return out
 
