@@ -41,7 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-constexpr int kWaves = 4;                 // one wave per SIMD: room for the extra accumulators
+constexpr int kWaves = 4;                 // one wave per SIMD per group
 constexpr int kThreads = 64 * kWaves;
 constexpr int BT = 64;                    // rows per staged tile
 constexpr int ST = 2;                     // LDS stages
@@ -230,10 +230,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: query-stationary
+// dQ: query-stationary. Two groups share a CU (two waves per SIMD, so one
+// group's waits overlap the other's work) where the registers allow it: the
+// windowed mask's extra state would spill, so MODE 2 keeps one group per CU.
 // ---------------------------------------------------------------------------
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(BwdParams p) {
   using TL = BTile<D>;
   constexpr int KD = D / 16, DB = D / 32;
   constexpr int NCH = 2 * TL::CH;                       // K then V chunks per tile
