@@ -130,6 +130,93 @@ template <> __device__ __forceinline__ void gather16<64>(u32x2 (&x)[8], const ui
       : "memory");
 }
 
+// Two row operands from LDS (a from pa, b from pb): 16-byte pieces at
+// d = 16 kk (+ 8 hh, folded into the addresses), D / 16 of each, in one asm
+// block that waits for its results, so that the compiler adds no wait for
+// the buffer->LDS loads in flight.
+template <int D> __device__ __forceinline__ void lds_rows2(bf16x8 (&a)[D / 16], bf16x8 (&b)[D / 16], uint32_t pa,
+                                                           uint32_t pb);
+template <> __device__ __forceinline__ void lds_rows2<128>(bf16x8 (&a)[8], bf16x8 (&b)[8], uint32_t pa,
+                                                             uint32_t pb) {
+  u32x4 x[16];
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:0\n\t"
+      "ds_read_b128 %1, %16 offset:32\n\t"
+      "ds_read_b128 %2, %16 offset:64\n\t"
+      "ds_read_b128 %3, %16 offset:96\n\t"
+      "ds_read_b128 %4, %16 offset:128\n\t"
+      "ds_read_b128 %5, %16 offset:160\n\t"
+      "ds_read_b128 %6, %16 offset:192\n\t"
+      "ds_read_b128 %7, %16 offset:224\n\t"
+      "ds_read_b128 %8, %17 offset:0\n\t"
+      "ds_read_b128 %9, %17 offset:32\n\t"
+      "ds_read_b128 %10, %17 offset:64\n\t"
+      "ds_read_b128 %11, %17 offset:96\n\t"
+      "ds_read_b128 %12, %17 offset:128\n\t"
+      "ds_read_b128 %13, %17 offset:160\n\t"
+      "ds_read_b128 %14, %17 offset:192\n\t"
+      "ds_read_b128 %15, %17 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
+      : "v"(pa), "v"(pb)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_memcpy(&a[i], &x[i], 16);
+    __builtin_memcpy(&b[i], &x[8 + i], 16);
+  }
+}
+template <> __device__ __forceinline__ void lds_rows2<64>(bf16x8 (&a)[4], bf16x8 (&b)[4], uint32_t pa,
+                                                             uint32_t pb) {
+  u32x4 x[8];
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:0\n\t"
+      "ds_read_b128 %1, %8 offset:32\n\t"
+      "ds_read_b128 %2, %8 offset:64\n\t"
+      "ds_read_b128 %3, %8 offset:96\n\t"
+      "ds_read_b128 %4, %9 offset:0\n\t"
+      "ds_read_b128 %5, %9 offset:32\n\t"
+      "ds_read_b128 %6, %9 offset:64\n\t"
+      "ds_read_b128 %7, %9 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(pa), "v"(pb)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_memcpy(&a[i], &x[i], 16);
+    __builtin_memcpy(&b[i], &x[4 + i], 16);
+  }
+}
+
+// lse2 and D of the 16 queries of a lane's accumulator registers: the 4
+// queries of register group g start at tile row r[g]; 32 bytes each from the
+// staged [row][2] floats, in one asm block that waits for its results.
+__device__ __forceinline__ void lds_lsed(float (&l2)[16], float (&dd)[16], const uint32_t (&r)[4]) {
+  u32x4 x[8];
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:0\n\t"
+      "ds_read_b128 %1, %8 offset:16\n\t"
+      "ds_read_b128 %2, %9 offset:0\n\t"
+      "ds_read_b128 %3, %9 offset:16\n\t"
+      "ds_read_b128 %4, %10 offset:0\n\t"
+      "ds_read_b128 %5, %10 offset:16\n\t"
+      "ds_read_b128 %6, %11 offset:0\n\t"
+      "ds_read_b128 %7, %11 offset:16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3])
+      : "memory");
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u32x4& v = x[2 * g + e / 2];
+      l2[4 * g + e] = __uint_as_float(v[2 * (e & 1)]);
+      dd[4 * g + e] = __uint_as_float(v[2 * (e & 1) + 1]);
+    }
+}
+
 // Per-lane pieces of the transposed-read addressing (elements, within a
 // padded tile): lane i of 16-lane group grp sources tile row i/4 of its group's
 // 4 rows at column 16*(grp%2) + 4*(i%4); half vh = grp/2 starts 20 rows
@@ -239,7 +326,8 @@ __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(Bwd
   using TL = BTile<D>;
   constexpr int KD = D / 16, DB = D / 32;
   constexpr int NCH = 2 * TL::CH;                       // K then V chunks per tile
-  constexpr int NCW = (NCH + kWaves - 1) / kWaves;
+  constexpr int NCW = NCH / kWaves;
+  static_assert(NCH % kWaves == 0, "chunks must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) u16 ks[ST][TL::ELEMS];
   __shared__ __attribute__((aligned(16))) u16 vs[ST][TL::ELEMS];
 
@@ -294,31 +382,21 @@ __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(Bwd
   }
 
   // DMA chunks: chunk c < CH is K chunk c, else V chunk c - CH; slot
-  // sl = 64*chunk + lane is row sl / SLOTS, 16-byte slot sl % SLOTS
-  uint32_t coff[NCW];
-#pragma unroll
-  for (int j = 0; j < NCW; ++j) {
-    const int c = wave + j * kWaves;
-    const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + lane;
-    const int row = sl / TL::SLOTS, ch = sl % TL::SLOTS;
-    coff[j] = ch >= D / 8 ? kOobOffset : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
-  }
+  // sl = 64*chunk + lane is row sl / SLOTS, 16-byte slot sl % SLOTS (the
+  // padding slots and rows past the end read zeros). The offsets are
+  // recomputed per tile rather than held in registers.
   auto issue = [&](int kt) {
     const int st = kt % ST;
-    const uint32_t tbase = uint32_t(base_row + kt * BT * pstride) * kv_pos_bytes;
-    const bool ragged = (kt + 1) * BT > p.Lv;
+    const uint32_t tbase = uint32_t(base_row + kt * BT * pstride) * kv_pos_bytes + kv_head_bytes;
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
       const int c = wave + j * kWaves;
-      if (c < NCH) {
-        uint32_t off = tbase + coff[j];
-        if (ragged) {
-          const int row = ((c < TL::CH ? c : c - TL::CH) * 64 + lane) / TL::SLOTS;
-          off += kt * BT + row < p.Lv ? 0u : kOobOffset;
-        }
-        if (c < TL::CH) dma16(krs, &ks[st][c * 512], off);
-        else dma16(vrs, &vs[st][(c - TL::CH) * 512], off);
-      }
+      const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + lane;
+      const int row = sl / TL::SLOTS, ch = sl % TL::SLOTS;
+      const bool ok = ch < D / 8 && kt * BT + row < p.Lv;
+      const uint32_t off = ok ? tbase + uint32_t(row * pstride) * kv_pos_bytes + ch * 16 : kOobOffset;
+      if (c < TL::CH) dma16(krs, &ks[st][c * 512], off);
+      else dma16(vrs, &vs[st][(c - TL::CH) * 512], off);
     }
   };
 
@@ -418,10 +496,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   using TL = BTile<D>;
   constexpr int KD = D / 16, DB = D / 32;
   constexpr int NCH = 2 * TL::CH;                       // Q then dO chunks per tile
-  constexpr int NCW = (NCH + kWaves - 1) / kWaves;
+  constexpr int NCW = NCH / kWaves;                     // chunks per wave (wave 0 also moves lse2/D)
+  static_assert(NCH % kWaves == 0, "chunks must split evenly over the waves");
   constexpr int KB = kWaves * 32;                       // keys per work group
-  __shared__ __attribute__((aligned(16))) u16 qs[ST][TL::ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 ds_[ST][TL::ELEMS];
+  constexpr int SK = 3;                                 // LDS stages: step s + 2 loads while s runs
+  __shared__ __attribute__((aligned(16))) u16 qs[SK][TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 ds_[SK][TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) float ls[SK][2 * 64 * 2];   // [query][lse2, D], 1 KiB per stage
 
   const int pstride = MODE == 0 ? p.pstride : 1;
   const int window = MODE == 2 ? p.window : 0;
@@ -457,6 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lsed, p.lsed_bytes);
   const uint32_t q_pos_bytes = uint32_t(p.hq) * D * 2;
+  const uint32_t lbase_seq = uint32_t(b * p.nseq + sq) * p.hq;   // workspace row of head 0 (times Lv)
 
   // K and V of this lane's key as B operands (K^T, V^T: k = d, n = key)
   bf16x8 kf[KD], vf[KD];
@@ -466,34 +548,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     load_rows<D>(vf, vrs, koff, kvalid, hh);
   }
 
-  uint32_t coff[NCW];
-#pragma unroll
-  for (int j = 0; j < NCW; ++j) {
-    const int c = wave + j * kWaves;
-    const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + lane;
-    const int row = sl / TL::SLOTS, ch = sl % TL::SLOTS;
-    coff[j] = ch >= D / 8 ? kOobOffset : uint32_t(row * pstride) * q_pos_bytes + ch * 16;
-  }
-  // step s: query tile qt_begin + s / G, query head kvh*G + s % G
+  // step s: query tile qt_begin + s / G, query head kvh*G + s % G. Chunk c
+  // of a tile (c < CH: Q, else dO) puts slot sl = 64 (c mod CH) + lane at
+  // row sl / SLOTS, 16-byte slot sl % SLOTS (the padding slots read zeros);
+  // wave w moves chunks w, w + 4, ...; wave 0 also moves the 64 queries'
+  // (lse2, D) pairs, 16 bytes per lane.
   auto issue = [&](int s) {
-    const int st = s % ST;
+    const int st = s % SK;
     const int qt = qt_begin + s / p.G;
     const int h = kvh * p.G + s % p.G;
     const uint32_t tbase = uint32_t(base_row + qt * BT * pstride) * q_pos_bytes + uint32_t(h) * D * 2;
-    const bool ragged = (qt + 1) * BT > p.Lv;
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
       const int c = wave + j * kWaves;
-      if (c < NCH) {
-        uint32_t off = tbase + coff[j];
-        if (ragged) {
-          const int row = ((c < TL::CH ? c : c - TL::CH) * 64 + lane) / TL::SLOTS;
-          off += qt * BT + row < p.Lv ? 0u : kOobOffset;
-        }
-        if (c < TL::CH) dma16(qrs, &qs[st][c * 512], off);
-        else dma16(dors, &ds_[st][(c - TL::CH) * 512], off);
-      }
+      const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + lane;
+      const int row = sl / TL::SLOTS, ch = sl % TL::SLOTS;
+      const bool ok = ch < D / 8 && qt * BT + row < p.Lv;
+      const uint32_t off = ok ? tbase + uint32_t(row * pstride) * q_pos_bytes + ch * 16 : kOobOffset;
+      if (c < TL::CH) dma16(qrs, &qs[st][c * 512], off);
+      else dma16(dors, &ds_[st][(c - TL::CH) * 512], off);
     }
+    if (wave == 0) {
+      const int iq = qt * BT + 2 * lane;
+      const uint32_t off = lane < 32 && iq < p.Lv ? ((lbase_seq + h) * p.Lv + iq) * 8 : kOobOffset;
+      dma16(lrs, &ls[st][0], off);
+    }
+  };
+  // this wave's chunks of the latest issued step may stay in flight
+  auto wait_prev = [&](bool keep) {
+    if (!keep) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCW + 1) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCW) : "memory");
   };
 
   const int rowA = sigma(l32);
@@ -508,14 +593,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   if (nsteps > 0) {
     issue(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (nsteps > 1) issue(1);
+    wait_prev(nsteps > 1);
     asm volatile("s_barrier" ::: "memory");
   }
   for (int s = 0; s < nsteps; ++s) {
-    const int st = s % ST;
+    const int st = s % SK;
     const int qt = qt_begin + s / p.G;
-    const int h = kvh * p.G + s % p.G;
-    if (s + 1 < nsteps) issue(s + 1);
+    // stage (s + 2) % 3 held step s - 1, which every wave has finished
+    if (s + 2 < nsteps) issue(s + 2);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qf0 = qt * BT + qb * 32;        // first query of the block
@@ -526,14 +612,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
       if (!live) continue;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       {
-        const u16* qr = &qs[st][(qb * 32 + rowA) * TL::ROW + 8 * hh];
-        const u16* dr = &ds_[st][(qb * 32 + rowA) * TL::ROW + 8 * hh];
         bf16x8 qa[KD], da[KD];
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          qa[kk] = *reinterpret_cast<const bf16x8*>(qr + kk * 16);
-          da[kk] = *reinterpret_cast<const bf16x8*>(dr + kk * 16);
-        }
+        lds_rows2<D>(qa, da, lds_addr(&qs[st][(qb * 32 + rowA) * TL::ROW + 8 * hh]),
+                     lds_addr(&ds_[st][(qb * 32 + rowA) * TL::ROW + 8 * hh]));
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) {
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], sacc, 0, 0, 0);
@@ -544,23 +625,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
       bf16x8 doT[DB][2], qT[DB][2];
       gather_block<D>(doT, lds_addr(&ds_[st][0]), qb * 32, tb);
       gather_block<D>(qT, lds_addr(&qs[st][0]), qb * 32, tb);
-      // lse2 and D of the 4 queries of each register group: 32 contiguous bytes
+      // lse2 and D of the 4 queries of each register group
       float l2[16], dd[16];
-      const uint32_t lbase = (uint32_t(b * p.nseq + sq) * p.hq + h) * p.Lv;
+      {
+        uint32_t r[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int iq = qf0 + reg_key_offset(g, hh);
-        const uint32_t off = (lbase + iq) * 8 + (iq < p.Lv ? 0u : kOobOffset);
-        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(lrs, int(off), 0, 0);
-        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(lrs, int(off + 16), 0, 0);
-        l2[4 * g + 0] = __uint_as_float(a[0]);
-        dd[4 * g + 0] = __uint_as_float(a[1]);
-        l2[4 * g + 1] = __uint_as_float(a[2]);
-        dd[4 * g + 1] = __uint_as_float(a[3]);
-        l2[4 * g + 2] = __uint_as_float(c[0]);
-        dd[4 * g + 2] = __uint_as_float(c[1]);
-        l2[4 * g + 3] = __uint_as_float(c[2]);
-        dd[4 * g + 3] = __uint_as_float(c[3]);
+        for (int g = 0; g < 4; ++g) r[g] = lds_addr(&ls[st][2 * (qb * 32 + reg_key_offset(g, hh))]);
+        lds_lsed(l2, dd, r);
       }
       // the block is full when every query sees every key of the wave and all queries are valid
       const bool full = qf0 + 31 < p.Lv && k0 + 31 <= qf0 && (window == 0 || qf0 + 31 - k0 < window);
@@ -588,8 +659,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
     }
     if (s + 1 < nsteps) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      asm volatile("s_barrier" ::: "memory");
+      // step s + 1 must have landed; the chunks of step s + 2 may still fly
+      wait_prev(s + 2 < nsteps);
+      asm volatile("s_barrier" ::: "memory");   // every read of step s waited for its results above
     }
   }
 
