@@ -41,6 +41,7 @@ CASES = [
     (4, (500, 1000), 256, 32, 8, 128, "cross_full", 0),
     (4, (1000, 997, 31), 128, 32, 8, 128, "cross_window", 130),
     (3, (40, 90), 32, 32, 2, 64, "cross_full", 0),           # G = 16: 48 rows, the last row block unused
+    (8, (70, 40), 32, 64, 8, 128, "cross_window", 150),      # n = 8, G = 8: 64 rows, d = 128
 ]
 
 
