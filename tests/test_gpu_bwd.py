@@ -114,3 +114,23 @@ def test_full_size(w):
     _close(np64(dq[:, rows]), rq, f"{w.name} dq rows")
     _close(np64(dk[:, keys]), rk, f"{w.name} dk keys")
     _close(np64(dv[:, keys]), rv, f"{w.name} dv keys")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_one_closed_form(d):
+    """Window 1: every query sees only itself, so P = 1 on the diagonal.
+    Then dV of a kv head is the sum of dO over its query heads at the same
+    position, dP - D = dO.v - dO.o = 0 (o = v), so dS, dQ and dK are zero."""
+    n, L, B, hq, hkv = 4, 50, 1, 8, 2
+    say("bwd window 1", d)
+    g = torch.Generator(device="cuda").manual_seed(123)
+    q, k, v, do = (torch.randn(s, generator=g, device="cuda").to(torch.bfloat16)
+                   for s in ((B, n * L, hq, d), (B, n * L, hkv, d), (B, n * L, hkv, d), (B, n * L, hq, d)))
+    o, lse = sfa.sf_attn_fwd(q, k, v, "cross_window", n, window=1, scale=_scale(d), lse=True)
+    dq, dk, dv = sfa.sf_attn_bwd(q, k, v, o, do, lse, "cross_window", n, window=1, scale=_scale(d))
+    torch.cuda.synchronize()
+    assert torch.equal(o, v.repeat_interleave(hq // hkv, dim=2)), "window 1 must return V"
+    want_dv = do.double().view(B, n * L, hkv, hq // hkv, d).sum(dim=3)
+    _close(np64(dv), np64(want_dv), "dv = sum of dO")
+    # dS is the bf16 rounding of p * (dP - D) with dP - D only rounding noise
+    assert float(dq.double().abs().max()) < 2e-2 and float(dk.double().abs().max()) < 2e-2
