@@ -51,6 +51,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=16.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters), then exit")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="only run decode calls for counter runs (batch 1 and 8, cross_full and intra, "
+                         "3 calls each on distinct caches), then exit")
     return ap.parse_args()
 
 
@@ -99,6 +102,21 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}))
+        return
+    if args.profile_decode:
+        for batch in (1, 8):
+            for mode in ("cross_full", "intra"):
+                wd = I.decode_workload(batch, mode)
+                g = torch.Generator(device=dev).manual_seed(3)
+                q = torch.randn((batch, wd.n, wd.hq, wd.d), generator=g, device=dev).to(torch.bfloat16)
+                caches = [tuple(torch.randn((batch, wd.n, wd.T, wd.hkv, wd.d), generator=g, device=dev)
+                                .to(torch.bfloat16) for _ in range(2)) for _ in range(3)]
+                for kc, vc in caches:
+                    sfa.sf_attn_decode(q, kc, vc, wd.T, mode, scale=wd.scale)
+                torch.cuda.synchronize()
+                print(json.dumps({"profile_decode": mode, "batch": batch, "calls": 3}), flush=True)
+                del caches
+                torch.cuda.empty_cache()
         return
 
     w = I.CROSS_32K
