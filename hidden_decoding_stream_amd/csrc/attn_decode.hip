@@ -34,6 +34,12 @@
 //   {8g+4+r} (g = lane/16) so that each lane ends up holding 8 consecutive
 //   keys of one query row: the B-operand layout of O^T = V^T P^T. V^T comes
 //   from the row-major V stage by transposed LDS reads (ds_read_b64_tr_b16).
+// * Grid: units along x, splits along y. The XCDs take consecutive groups in
+//   turn, so every split index spreads over all of them. Under a paged cache
+//   the units are taken longest sequence first (ranked on the device from
+//   seq_lens), so that with one 128 KiB group per CU the short sequences fill
+//   in behind the long ones instead of a long one running alone at the end;
+//   a split wholly past its sequence's keys leaves at once.
 // * The 4 waves of a group merge their (max, sum, O) in LDS. With one split
 //   the group writes the normalised bf16 output; otherwise it writes one fp32
 //   partial per query row and split, and a second kernel merges the splits in
@@ -75,6 +81,8 @@ struct DecParams {
   int32_t window;    // 0: none
   float c;           // scale * log2(e)
   int32_t splits, chunk, keys;
+  int32_t batch;
+  float len_class;           // paged: 64 / (max_T + 1), length -> one of 64 classes
   // paged cache (T above is then the largest valid length, max_T)
   const int32_t* seq_lens;   // [batch]
   const int32_t* table;      // [batch][n][max_pages] page of each (stream, logical page)
@@ -110,6 +118,69 @@ template <int D> __device__ __forceinline__ int swv(int k) {
   else return (k & 2) | ((k >> 1) & 4);
 }
 
+// Key space of batch element b of a paged cache. A sequence brings its own
+// length; one outside [1, max_T] gets no keys (its rows come out NaN). Its
+// first visited token is rounded down to a multiple of the step so that no
+// step straddles two pages (the mask drops the extra tokens).
+struct SeqKeys {
+  int T, t_lo, kps, keys;
+};
+__device__ __forceinline__ SeqKeys paged_keys(const DecParams& p, int b) {
+  SeqKeys s;
+  s.T = p.seq_lens[b];
+  if (s.T < 1 || s.T > p.T) s.T = 0;
+  s.t_lo = 0;
+  if (p.window > 0) {
+    const int oldest = (s.T - 1) * p.n - p.window + 1;
+    if (oldest > 0) s.t_lo = (oldest / p.n) & ~(kStep - 1);
+  }
+  s.kps = (s.T - s.t_lo + kStep - 1) / kStep * kStep;
+  s.keys = (p.intra ? 1 : p.n) * s.kps;
+  return s;
+}
+
+// Paged caches: batch element of the r-th longest sequence. Lengths fall into
+// 64 classes (class 0 the longest; an invalid length counts as 0), ties keep
+// batch order. Units are dispatched in this order, so the longest sequences'
+// groups start first and the short ones fill in behind them (longest
+// processing time first): with one group per CU at a time, a long sequence
+// dispatched last would otherwise run on alone at the end. One wave computes
+// it, with `hist` 64 words of LDS of its own; every result is wave-uniform.
+__device__ __forceinline__ int len_key(const DecParams& p, int T) {
+  if (T < 1 || T > p.T) T = 0;
+  return 63 - min(63, int(float(T) * p.len_class));
+}
+__device__ int paged_rank_to_b(const DecParams& p, int r, int lane, uint32_t* hist) {
+  // one wave's LDS operations complete in order; the asm statements only keep
+  // the compiler from moving the plain accesses across the atomics
+  hist[lane] = 0;
+  asm volatile("" ::: "memory");
+  for (int c = 0; c < p.batch; c += 64)
+    if (c + lane < p.batch) atomicAdd(&hist[len_key(p, p.seq_lens[c + lane])], 1u);
+  asm volatile("" ::: "memory");
+  const int count = int(hist[lane]);
+  int incl = count;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  const int excl = incl - count;
+  const int cls = __ffsll((unsigned long long)__ballot(excl <= r && r < incl)) - 1;
+  int rr = r - __shfl(excl, cls);
+  for (int c = 0; c < p.batch; c += 64) {
+    const bool in = c + lane < p.batch && len_key(p, p.seq_lens[c + lane]) == cls;
+    const unsigned long long mk = __ballot(in);
+    const int cnt = __popcll(mk);
+    if (rr < cnt) {
+      const int below = __popcll(mk & ((1ull << lane) - 1));
+      return c + __ffsll((unsigned long long)__ballot(in && below == rr)) - 1;
+    }
+    rr -= cnt;
+  }
+  return 0;   // not reached for r < batch
+}
+
 template <int D, int RB, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   using SG = Stage<D>;
@@ -134,13 +205,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   __shared__ __attribute__((aligned(16))) u16 st2[NS > 2 ? kStageElems : 8];
   __shared__ __attribute__((aligned(16))) u16 st3[NS > 3 ? kStageElems : 8];
   Merge& mrg = *reinterpret_cast<Merge*>(st0);
+  // paged: the ranked batch element, parked here for the merge instead of
+  // being held in a register through the step loop (the 64-row instance has
+  // none to spare)
+  __shared__ int b_park;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x;
-  const int unit = blockIdx.y;
+  // units run along x: the XCDs take consecutive work groups in turn, so the
+  // groups of one split index spread over all of them. (With the split along
+  // x, split 0 of every unit would land on the same few XCDs, and under mixed
+  // sequence lengths split 0 carries most of the work.)
+  const int unit = blockIdx.x;
+  const int split = blockIdx.y;
 
   int b, kvh, s_unit;
   if (p.intra) {
@@ -152,22 +231,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     kvh = unit % p.hkv;
     b = unit / p.hkv;
   }
-  // Cache length of this batch element and its key index space. A paged
-  // sequence brings its own length; one outside [1, max_T] gets no keys (its
-  // rows come out NaN). Its first visited token is rounded down to a multiple
-  // of the step so that no step straddles two pages (the mask drops the
-  // extra tokens).
+  if constexpr (PAGED) {
+    // longest sequences first; the histogram lives in this wave's slot of
+    // stage 0, which no DMA writes before the prologue below
+    b = __builtin_amdgcn_readfirstlane(
+        paged_rank_to_b(p, b, lane, reinterpret_cast<uint32_t*>(st0 + wave * 2 * SG::TILE)));
+    if (tid == 0) b_park = b;
+  }
+  // Cache length of this batch element and its key index space
   int T = p.T, t_lo = p.t_lo, kps = p.kps, keys = p.keys;
   if constexpr (PAGED) {
-    T = p.seq_lens[b];
-    if (T < 1 || T > p.T) T = 0;
-    t_lo = 0;
-    if (p.window > 0) {
-      const int oldest = (T - 1) * p.n - p.window + 1;
-      if (oldest > 0) t_lo = (oldest / p.n) & ~(kStep - 1);
-    }
-    kps = (T - t_lo + kStep - 1) / kStep * kStep;
-    keys = (p.intra ? 1 : p.n) * kps;
+    const SeqKeys sk = paged_keys(p, b);
+    T = sk.T;
+    t_lo = sk.t_lo;
+    kps = sk.kps;
+    keys = sk.keys;
+    // a split wholly past a shorter sequence's keys has nothing to add: it
+    // leaves at once and the combine does not read its slot (split 0 always
+    // runs, so an invalid length still yields its NaN rows)
+    if (split > 0 && split * p.chunk >= keys) return;
   }
   // query rows of this lane's B-operand columns, one per 16-row block
   bool rvalid[RB];
@@ -185,9 +267,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   const size_t stream_stride = (size_t)p.Tmax * p.hkv * D;      // elements between streams (contiguous cache)
   const u16* kbase;
   const u16* vbase;
+  const int32_t* table_b = p.table;   // paged: this sequence's block table rows
   if constexpr (PAGED) {
     kbase = p.kc + (size_t)kvh * D;
     vbase = p.vc + (size_t)kvh * D;
+    table_b = p.table + (size_t)b * p.n * p.max_pages;
   } else {
     kbase = p.kc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
     vbase = p.vc + (size_t)b * p.n * stream_stride + (size_t)kvh * D;
@@ -234,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
       // page index outside the pool) fall outside the range and read zeros
       const uint32_t lp = fdiv(uint32_t(t0), p.page);
       const int tp0 = int(lp * p.page.d);
-      const int pg = p.table[((size_t)b * p.n + sp) * p.max_pages + lp];
+      const int pg = table_b[(size_t)sp * p.max_pages + lp];
       const bool pg_ok = pg >= 0 && int64_t(pg) < p.num_pages;
       const size_t pbase = size_t(pg_ok ? pg : 0) * p.page_elems;
       kb = kbase + pbase;
@@ -409,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 
   // ---- merge the 4 waves in LDS, one 16-row block at a time ----
+  int b_out = b;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     lsum[rb] += __shfl_xor(lsum[rb], 16);
@@ -419,6 +504,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     // every wave is done with its ring (the merge area aliases stage 0), or
     // with the previous block's merge
     __syncthreads();
+    if constexpr (PAGED) {
+      if (rb == 0) b_out = b_park;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -446,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
       const int r = rb * 16 + row;
       const int rs2 = p.intra ? s_unit : r / p.G;
       const int rh2 = kvh * p.G + (p.intra ? r : r % p.G);
-      const size_t orow = (size_t)(b * p.n + rs2) * p.hq + rh2;
+      const size_t orow = (size_t)(b_out * p.n + rs2) * p.hq + rh2;
       if (p.splits == 1) {
         // every row of a valid sequence admits at least its own key, so lt > 0
         // (an invalid paged length leaves lt = 0: NaN)
@@ -474,13 +562,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int64_
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t orow = int64_t(blockIdx.x) * 4 + wave;
   if (orow >= rows) return;
+  // splits holding a partial: all of them, or under a paged cache those that
+  // reach into this row's sequence (the others left without writing)
+  int ns = p.splits;
+  if (p.seq_lens != nullptr) {
+    const int keys = paged_keys(p, int(orow / (int64_t(p.n) * p.hq))).keys;
+    ns = max(1, min(p.splits, (keys + p.chunk - 1) / p.chunk));
+  }
   const float* ml = p.ws_ml + orow * p.splits * 2;
   float M = -INFINITY;
-  for (int s = lane; s < p.splits; s += 64) M = fmaxf(M, ml[2 * s]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float lt = 0.f;
-  for (int s = lane; s < p.splits; s += 64) {
+  for (int s = lane; s < ns; s += 64) {
     const float ms = ml[2 * s];
     lt += ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[2 * s + 1];
   }
@@ -491,7 +586,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int64_
   const float* po = p.ws_o + orow * p.splits * D + 4 * d4;
   f32x4 acc = f32x4{};
 #pragma unroll 8
-  for (int s = cls; s < p.splits; s += C) {
+  for (int s = cls; s < ns; s += C) {
     const float ms = ml[2 * s];
     const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
     const f32x4 x = *reinterpret_cast<const f32x4*>(po + (size_t)s * D);
@@ -585,6 +680,8 @@ hipError_t launch_attn_decode(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.splits = pl.splits;
   p.chunk = int32_t(pl.chunk);
   p.keys = int32_t(pl.keys);
+  p.batch = int32_t(a.batch);
+  p.len_class = float(64.0 / (double(a.T) + 1.0));
   const bool paged = a.seq_lens != nullptr;
   p.seq_lens = a.seq_lens;
   p.table = a.table;
@@ -592,7 +689,7 @@ hipError_t launch_attn_decode(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.max_pages = a.max_pages;
   p.num_pages = a.num_pages;
   p.page_elems = size_t(a.page) * a.hkv * a.d;
-  const dim3 grid(uint32_t(pl.splits), uint32_t(pl.units));
+  const dim3 grid(uint32_t(pl.units), uint32_t(pl.splits));
   const dim3 cgrid(uint32_t((rows + 3) / 4));
   using Kernel = void (*)(DecParams);
   // [d == 128][row blocks 1, 2, 4][paged]

@@ -112,6 +112,31 @@ def test_page_outside_pool_reads_zeros():
     assert_close(np64(o), _oracle(w, q, zk, zv, fixed, sl), "zero pages")
 
 
+@pytest.mark.parametrize("mode,W", [("cross_full", 0), ("intra", 0), ("cross_window", 90)])
+def test_many_sequences_longest_first(mode, W):
+    """150 sequences (more than one wave's worth of lengths to rank), many of
+    them in the same length class, a few with invalid lengths: the work is
+    dispatched longest first, and every sequence's rows must still land in
+    its own output rows (NaN for the invalid ones)."""
+    gen = torch.Generator().manual_seed(31)
+    lens = tuple(int(x) for x in torch.randint(1, 201, (150,), generator=gen))
+    lens = lens[:40] + (200,) * 12 + (7,) * 12 + lens[64:]     # ties at both ends of the ranking
+    w = I.PagedDecodeWorkload("many", 2, lens, 32, 4, 2, 64, mode, window=W, seed=32)
+    q, kp, vp, table, sl = (t.cuda() for t in I.paged_decode_inputs(w))
+    bad = [5, 77, 149]
+    sl_run = sl.clone()
+    sl_run[bad[0]], sl_run[bad[1]], sl_run[bad[2]] = 0, -2, 201
+    good = [b for b in range(w.batch) if b not in bad]
+    ref = _oracle(w, q, kp, vp, table, sl, rows=good)
+    for splits in (0, 1, 4):
+        say("paged many sequences", mode, "splits", splits)
+        o = sfa.sf_attn_decode_paged(q, kp, vp, table, sl_run, mode, max_T=200, window=W, scale=w.scale,
+                                     num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.isnan(o[bad].float()).all(), splits
+        assert_close(np64(o[good]), ref, f"many {mode} splits={splits}")
+
+
 @pytest.mark.parametrize("mode,W", [("cross_full", 0), ("intra", 0), ("cross_window", 4096)])
 def test_full_size_mixed_lengths(mode, W):
     """Serving batch: 8 sequences of 1..8192 tokens x 4 streams, 32/8 heads,
