@@ -247,9 +247,26 @@ def main():
     if not args.no_decode_sweep:
         line["decode"] = decode_sweep(torch, sfa, C, I, dev)
         line["serving"] = serving_sweep(torch, sfa, C, I, dev)
+    line["attainable"] = attainable_peaks(line)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, C, I, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def attainable_peaks(line):
+    """The chip's attainable peaks measured on this GPU (back-to-back dense
+    bf16 MFMAs; a streaming read of 2 GiB, beyond the Infinity Cache), and the
+    headline prefill and the decode sweep as fractions of them, beside the
+    published peaks that `roofline` uses."""
+    import hidden_decoding_stream_amd.peaks as P
+    mfma = P.mfma_bf16_flops() / 1e12
+    read = P.read_bandwidth() / 1e9
+    out = {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_GBps": round(read, 1),
+           "prefill_cross_full_frac": round(line["roofline"]["achieved"] / mfma, 4)}
+    for key, rec in (line.get("decode") or {}).items():
+        out[f"decode_{key}_frac"] = round(rec["GBps"] / read, 4)
+    print(f"[bench] attainable: {mfma:.0f} TFLOP/s bf16, {read:.0f} GB/s read", file=sys.stderr, flush=True)
+    return out
 
 
 def last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream, reps=10):

@@ -26,9 +26,10 @@
 //   column), P and dS with each register's own query lse / D, then
 //   dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposed reads).
 // Tiles are K-style: rows padded to D+16 elements (the sigma-order 16-byte
-// reads hit distinct bank groups), loaded by buffer->LDS DMA through a
-// 2-stage ring with one bare barrier per tile; transposed reads are asm blocks
-// that wait for their own results (see common.h).
+// reads hit distinct bank groups), loaded by buffer->LDS DMA through a ring
+// (2 stages for dQ, 3 for dK/dV) with one bare barrier per tile; LDS reads
+// are asm blocks that wait for their own results (see common.h), and the
+// dK/dV loop runs its MFMAs inside those blocks (DkdvAsm).
 #include <math.h>
 
 #include "common.h"
@@ -187,34 +188,6 @@ template <> __device__ __forceinline__ void lds_rows2<64>(bf16x8 (&a)[4], bf16x8
     __builtin_memcpy(&a[i], &x[i], 16);
     __builtin_memcpy(&b[i], &x[4 + i], 16);
   }
-}
-
-// lse2 and D of the 16 queries of a lane's accumulator registers: the 4
-// queries of register group g start at tile row r[g]; 32 bytes each from the
-// staged [row][2] floats, in one asm block that waits for its results.
-__device__ __forceinline__ void lds_lsed(float (&l2)[16], float (&dd)[16], const uint32_t (&r)[4]) {
-  u32x4 x[8];
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:0\n\t"
-      "ds_read_b128 %1, %8 offset:16\n\t"
-      "ds_read_b128 %2, %9 offset:0\n\t"
-      "ds_read_b128 %3, %9 offset:16\n\t"
-      "ds_read_b128 %4, %10 offset:0\n\t"
-      "ds_read_b128 %5, %10 offset:16\n\t"
-      "ds_read_b128 %6, %11 offset:0\n\t"
-      "ds_read_b128 %7, %11 offset:16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
-      : "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3])
-      : "memory");
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const u32x4& v = x[2 * g + e / 2];
-      l2[4 * g + e] = __uint_as_float(v[2 * (e & 1)]);
-      dd[4 * g + e] = __uint_as_float(v[2 * (e & 1) + 1]);
-    }
 }
 
 // Per-lane pieces of the transposed-read addressing (elements, within a
@@ -488,6 +461,266 @@ __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(Bwd
     }
 }
 
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// The dK/dV loop in three phases per 32-query block, each one asm block that
+// issues the phase's MFMAs with the LDS reads the next phase needs spread over
+// the first half of them, and waits for those reads only at its end: with one
+// wave per SIMD, nothing else would keep the matrix core busy while a read is
+// outstanding. The MFMAs sit in the same block as the reads because a read
+// left in flight across asm blocks could land in a register the compiler has
+// meanwhile reused. Wait states the compiler cannot see inside asm are
+// explicit: s_nop 2 before MFMAs that read VALU-written registers, and 20
+// after the score MFMAs whose results the VALU reads next.
+//   x:  S = Q K^T, dP = dO V^T (fresh accumulators); reads dO^T (transposed)
+//       and the block's (lse2, D) pairs
+//   y1: dV^T += dO^T P; reads Q^T (transposed)
+//   y2: dK^T += Q^T dS; reads the next block's Q and dO rows
+// Same products in the same accumulation order as builtin MFMAs would give.
+template <int D> struct DkdvAsm;
+template <> struct DkdvAsm<128> {
+  // S = Q K^T and dP = dO V^T (fresh accumulators), with dO^T gathered and the
+  // block's (lse2, D) pairs read
+  static __device__ __forceinline__ void x(f32x16& s, f32x16& p, const bf16x8 (&qa)[8], const bf16x8 (&da)[8],
+                                           const bf16x8 (&kf)[8], const bf16x8 (&vf)[8], uint32_t ae, uint32_t ao,
+                                           const uint32_t (&r)[4], u32x2 (&x)[16], u32x4 (&y)[8]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa0], %[kf0], 0\n\t"
+      "ds_read_b64_tr_b16 %[x0], %[ae] offset:0\n\t"
+      "ds_read_b64_tr_b16 %[x1], %[ae] offset:2304\n\t"
+      "ds_read_b64_tr_b16 %[x2], %[ao] offset:1152\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da0], %[vf0], 0\n\t"
+      "ds_read_b64_tr_b16 %[x3], %[ao] offset:3456\n\t"
+      "ds_read_b64_tr_b16 %[x4], %[ae] offset:64\n\t"
+      "ds_read_b64_tr_b16 %[x5], %[ae] offset:2368\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa1], %[kf1], %[s]\n\t"
+      "ds_read_b64_tr_b16 %[x6], %[ao] offset:1216\n\t"
+      "ds_read_b64_tr_b16 %[x7], %[ao] offset:3520\n\t"
+      "ds_read_b64_tr_b16 %[x8], %[ae] offset:128\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da1], %[vf1], %[p]\n\t"
+      "ds_read_b64_tr_b16 %[x9], %[ae] offset:2432\n\t"
+      "ds_read_b64_tr_b16 %[x10], %[ao] offset:1280\n\t"
+      "ds_read_b64_tr_b16 %[x11], %[ao] offset:3584\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa2], %[kf2], %[s]\n\t"
+      "ds_read_b64_tr_b16 %[x12], %[ae] offset:192\n\t"
+      "ds_read_b64_tr_b16 %[x13], %[ae] offset:2496\n\t"
+      "ds_read_b64_tr_b16 %[x14], %[ao] offset:1344\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da2], %[vf2], %[p]\n\t"
+      "ds_read_b64_tr_b16 %[x15], %[ao] offset:3648\n\t"
+      "ds_read_b128 %[y0], %[r0] offset:0\n\t"
+      "ds_read_b128 %[y1], %[r0] offset:16\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa3], %[kf3], %[s]\n\t"
+      "ds_read_b128 %[y2], %[r1] offset:0\n\t"
+      "ds_read_b128 %[y3], %[r1] offset:16\n\t"
+      "ds_read_b128 %[y4], %[r2] offset:0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da3], %[vf3], %[p]\n\t"
+      "ds_read_b128 %[y5], %[r2] offset:16\n\t"
+      "ds_read_b128 %[y6], %[r3] offset:0\n\t"
+      "ds_read_b128 %[y7], %[r3] offset:16\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa4], %[kf4], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da4], %[vf4], %[p]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa5], %[kf5], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da5], %[vf5], %[p]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa6], %[kf6], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da6], %[vf6], %[p]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa7], %[kf7], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da7], %[vf7], %[p]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 3\n\t"
+      : [s] "=&v"(s), [p] "=&v"(p), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+        [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7]), [x8] "=&v"(x[8]),
+        [x9] "=&v"(x[9]), [x10] "=&v"(x[10]), [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]),
+        [x14] "=&v"(x[14]), [x15] "=&v"(x[15]), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]),
+        [y3] "=&v"(y[3]), [y4] "=&v"(y[4]), [y5] "=&v"(y[5]), [y6] "=&v"(y[6]), [y7] "=&v"(y[7])
+      : [qa0] "v"(qa[0]), [qa1] "v"(qa[1]), [qa2] "v"(qa[2]), [qa3] "v"(qa[3]), [qa4] "v"(qa[4]),
+        [qa5] "v"(qa[5]), [qa6] "v"(qa[6]), [qa7] "v"(qa[7]), [da0] "v"(da[0]), [da1] "v"(da[1]),
+        [da2] "v"(da[2]), [da3] "v"(da[3]), [da4] "v"(da[4]), [da5] "v"(da[5]), [da6] "v"(da[6]),
+        [da7] "v"(da[7]), [kf0] "v"(kf[0]), [kf1] "v"(kf[1]), [kf2] "v"(kf[2]), [kf3] "v"(kf[3]),
+        [kf4] "v"(kf[4]), [kf5] "v"(kf[5]), [kf6] "v"(kf[6]), [kf7] "v"(kf[7]), [vf0] "v"(vf[0]),
+        [vf1] "v"(vf[1]), [vf2] "v"(vf[2]), [vf3] "v"(vf[3]), [vf4] "v"(vf[4]), [vf5] "v"(vf[5]),
+        [vf6] "v"(vf[6]), [vf7] "v"(vf[7]), [ae] "v"(ae), [ao] "v"(ao), [r0] "v"(r[0]), [r1] "v"(r[1]),
+        [r2] "v"(r[2]), [r3] "v"(r[3])
+      : "memory");
+  }
+  // acc[db] += opA[db][j] opB[j] (dV^T += dO^T P), with Q^T gathered
+  static __device__ __forceinline__ void y1(f32x16 (&acc)[4], const bf16x8 (&opA)[4][2], const bf16x8 (&opB)[2],
+                                            uint32_t ae, uint32_t ao, u32x2 (&x)[16]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t00], %[pf0], %[v0]\n\t"
+      "ds_read_b64_tr_b16 %[x0], %[ae] offset:0\n\t"
+      "ds_read_b64_tr_b16 %[x1], %[ae] offset:2304\n\t"
+      "ds_read_b64_tr_b16 %[x2], %[ao] offset:1152\n\t"
+      "ds_read_b64_tr_b16 %[x3], %[ao] offset:3456\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t10], %[pf0], %[v1]\n\t"
+      "ds_read_b64_tr_b16 %[x4], %[ae] offset:64\n\t"
+      "ds_read_b64_tr_b16 %[x5], %[ae] offset:2368\n\t"
+      "ds_read_b64_tr_b16 %[x6], %[ao] offset:1216\n\t"
+      "ds_read_b64_tr_b16 %[x7], %[ao] offset:3520\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v2], %[t20], %[pf0], %[v2]\n\t"
+      "ds_read_b64_tr_b16 %[x8], %[ae] offset:128\n\t"
+      "ds_read_b64_tr_b16 %[x9], %[ae] offset:2432\n\t"
+      "ds_read_b64_tr_b16 %[x10], %[ao] offset:1280\n\t"
+      "ds_read_b64_tr_b16 %[x11], %[ao] offset:3584\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v3], %[t30], %[pf0], %[v3]\n\t"
+      "ds_read_b64_tr_b16 %[x12], %[ae] offset:192\n\t"
+      "ds_read_b64_tr_b16 %[x13], %[ae] offset:2496\n\t"
+      "ds_read_b64_tr_b16 %[x14], %[ao] offset:1344\n\t"
+      "ds_read_b64_tr_b16 %[x15], %[ao] offset:3648\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t01], %[pf1], %[v0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t11], %[pf1], %[v1]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v2], %[t21], %[pf1], %[v2]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v3], %[t31], %[pf1], %[v3]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [v0] "+a"(acc[0]), [v1] "+a"(acc[1]), [v2] "+a"(acc[2]), [v3] "+a"(acc[3]), [x0] "=&v"(x[0]),
+        [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]),
+        [x6] "=&v"(x[6]), [x7] "=&v"(x[7]), [x8] "=&v"(x[8]), [x9] "=&v"(x[9]), [x10] "=&v"(x[10]),
+        [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]), [x14] "=&v"(x[14]), [x15] "=&v"(x[15])
+      : [t00] "v"(opA[0][0]), [t01] "v"(opA[0][1]), [t10] "v"(opA[1][0]), [t11] "v"(opA[1][1]),
+        [t20] "v"(opA[2][0]), [t21] "v"(opA[2][1]), [t30] "v"(opA[3][0]), [t31] "v"(opA[3][1]),
+        [pf0] "v"(opB[0]), [pf1] "v"(opB[1]), [ae] "v"(ae), [ao] "v"(ao)
+      : "memory");
+  }
+  // acc[db] += opA[db][j] opB[j] (dK^T += Q^T dS), with the next block's Q and dO rows read
+  static __device__ __forceinline__ void y2(f32x16 (&acc)[4], const bf16x8 (&opA)[4][2], const bf16x8 (&opB)[2],
+                                            uint32_t pa, uint32_t pb, u32x4 (&y)[16]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t00], %[pf0], %[v0]\n\t"
+      "ds_read_b128 %[y0], %[pa] offset:0\n\t"
+      "ds_read_b128 %[y1], %[pa] offset:32\n\t"
+      "ds_read_b128 %[y2], %[pa] offset:64\n\t"
+      "ds_read_b128 %[y3], %[pa] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t10], %[pf0], %[v1]\n\t"
+      "ds_read_b128 %[y4], %[pa] offset:128\n\t"
+      "ds_read_b128 %[y5], %[pa] offset:160\n\t"
+      "ds_read_b128 %[y6], %[pa] offset:192\n\t"
+      "ds_read_b128 %[y7], %[pa] offset:224\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v2], %[t20], %[pf0], %[v2]\n\t"
+      "ds_read_b128 %[y8], %[pb] offset:0\n\t"
+      "ds_read_b128 %[y9], %[pb] offset:32\n\t"
+      "ds_read_b128 %[y10], %[pb] offset:64\n\t"
+      "ds_read_b128 %[y11], %[pb] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v3], %[t30], %[pf0], %[v3]\n\t"
+      "ds_read_b128 %[y12], %[pb] offset:128\n\t"
+      "ds_read_b128 %[y13], %[pb] offset:160\n\t"
+      "ds_read_b128 %[y14], %[pb] offset:192\n\t"
+      "ds_read_b128 %[y15], %[pb] offset:224\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t01], %[pf1], %[v0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t11], %[pf1], %[v1]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v2], %[t21], %[pf1], %[v2]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v3], %[t31], %[pf1], %[v3]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [v0] "+a"(acc[0]), [v1] "+a"(acc[1]), [v2] "+a"(acc[2]), [v3] "+a"(acc[3]), [y0] "=&v"(y[0]),
+        [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3]), [y4] "=&v"(y[4]), [y5] "=&v"(y[5]),
+        [y6] "=&v"(y[6]), [y7] "=&v"(y[7]), [y8] "=&v"(y[8]), [y9] "=&v"(y[9]), [y10] "=&v"(y[10]),
+        [y11] "=&v"(y[11]), [y12] "=&v"(y[12]), [y13] "=&v"(y[13]), [y14] "=&v"(y[14]), [y15] "=&v"(y[15])
+      : [t00] "v"(opA[0][0]), [t01] "v"(opA[0][1]), [t10] "v"(opA[1][0]), [t11] "v"(opA[1][1]),
+        [t20] "v"(opA[2][0]), [t21] "v"(opA[2][1]), [t30] "v"(opA[3][0]), [t31] "v"(opA[3][1]),
+        [pf0] "v"(opB[0]), [pf1] "v"(opB[1]), [pa] "v"(pa), [pb] "v"(pb)
+      : "memory");
+  }
+};
+template <> struct DkdvAsm<64> {
+  // S = Q K^T and dP = dO V^T (fresh accumulators), with dO^T gathered and the
+  // block's (lse2, D) pairs read
+  static __device__ __forceinline__ void x(f32x16& s, f32x16& p, const bf16x8 (&qa)[4], const bf16x8 (&da)[4],
+                                           const bf16x8 (&kf)[4], const bf16x8 (&vf)[4], uint32_t ae, uint32_t ao,
+                                           const uint32_t (&r)[4], u32x2 (&x)[8], u32x4 (&y)[8]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa0], %[kf0], 0\n\t"
+      "ds_read_b64_tr_b16 %[x0], %[ae] offset:0\n\t"
+      "ds_read_b64_tr_b16 %[x1], %[ae] offset:1280\n\t"
+      "ds_read_b64_tr_b16 %[x2], %[ao] offset:640\n\t"
+      "ds_read_b64_tr_b16 %[x3], %[ao] offset:1920\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da0], %[vf0], 0\n\t"
+      "ds_read_b64_tr_b16 %[x4], %[ae] offset:64\n\t"
+      "ds_read_b64_tr_b16 %[x5], %[ae] offset:1344\n\t"
+      "ds_read_b64_tr_b16 %[x6], %[ao] offset:704\n\t"
+      "ds_read_b64_tr_b16 %[x7], %[ao] offset:1984\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa1], %[kf1], %[s]\n\t"
+      "ds_read_b128 %[y0], %[r0] offset:0\n\t"
+      "ds_read_b128 %[y1], %[r0] offset:16\n\t"
+      "ds_read_b128 %[y2], %[r1] offset:0\n\t"
+      "ds_read_b128 %[y3], %[r1] offset:16\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da1], %[vf1], %[p]\n\t"
+      "ds_read_b128 %[y4], %[r2] offset:0\n\t"
+      "ds_read_b128 %[y5], %[r2] offset:16\n\t"
+      "ds_read_b128 %[y6], %[r3] offset:0\n\t"
+      "ds_read_b128 %[y7], %[r3] offset:16\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa2], %[kf2], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da2], %[vf2], %[p]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[qa3], %[kf3], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[da3], %[vf3], %[p]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 3\n\t"
+      : [s] "=&v"(s), [p] "=&v"(p), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+        [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7]), [y0] "=&v"(y[0]),
+        [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3]), [y4] "=&v"(y[4]), [y5] "=&v"(y[5]),
+        [y6] "=&v"(y[6]), [y7] "=&v"(y[7])
+      : [qa0] "v"(qa[0]), [qa1] "v"(qa[1]), [qa2] "v"(qa[2]), [qa3] "v"(qa[3]), [da0] "v"(da[0]),
+        [da1] "v"(da[1]), [da2] "v"(da[2]), [da3] "v"(da[3]), [kf0] "v"(kf[0]), [kf1] "v"(kf[1]),
+        [kf2] "v"(kf[2]), [kf3] "v"(kf[3]), [vf0] "v"(vf[0]), [vf1] "v"(vf[1]), [vf2] "v"(vf[2]),
+        [vf3] "v"(vf[3]), [ae] "v"(ae), [ao] "v"(ao), [r0] "v"(r[0]), [r1] "v"(r[1]), [r2] "v"(r[2]),
+        [r3] "v"(r[3])
+      : "memory");
+  }
+  // acc[db] += opA[db][j] opB[j] (dV^T += dO^T P), with Q^T gathered
+  static __device__ __forceinline__ void y1(f32x16 (&acc)[2], const bf16x8 (&opA)[2][2], const bf16x8 (&opB)[2],
+                                            uint32_t ae, uint32_t ao, u32x2 (&x)[8]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t00], %[pf0], %[v0]\n\t"
+      "ds_read_b64_tr_b16 %[x0], %[ae] offset:0\n\t"
+      "ds_read_b64_tr_b16 %[x1], %[ae] offset:1280\n\t"
+      "ds_read_b64_tr_b16 %[x2], %[ao] offset:640\n\t"
+      "ds_read_b64_tr_b16 %[x3], %[ao] offset:1920\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t10], %[pf0], %[v1]\n\t"
+      "ds_read_b64_tr_b16 %[x4], %[ae] offset:64\n\t"
+      "ds_read_b64_tr_b16 %[x5], %[ae] offset:1344\n\t"
+      "ds_read_b64_tr_b16 %[x6], %[ao] offset:704\n\t"
+      "ds_read_b64_tr_b16 %[x7], %[ao] offset:1984\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t01], %[pf1], %[v0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t11], %[pf1], %[v1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [v0] "+a"(acc[0]), [v1] "+a"(acc[1]), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]),
+        [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+      : [t00] "v"(opA[0][0]), [t01] "v"(opA[0][1]), [t10] "v"(opA[1][0]), [t11] "v"(opA[1][1]),
+        [pf0] "v"(opB[0]), [pf1] "v"(opB[1]), [ae] "v"(ae), [ao] "v"(ao)
+      : "memory");
+  }
+  // acc[db] += opA[db][j] opB[j] (dK^T += Q^T dS), with the next block's Q and dO rows read
+  static __device__ __forceinline__ void y2(f32x16 (&acc)[2], const bf16x8 (&opA)[2][2], const bf16x8 (&opB)[2],
+                                            uint32_t pa, uint32_t pb, u32x4 (&y)[8]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t00], %[pf0], %[v0]\n\t"
+      "ds_read_b128 %[y0], %[pa] offset:0\n\t"
+      "ds_read_b128 %[y1], %[pa] offset:32\n\t"
+      "ds_read_b128 %[y2], %[pa] offset:64\n\t"
+      "ds_read_b128 %[y3], %[pa] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t10], %[pf0], %[v1]\n\t"
+      "ds_read_b128 %[y4], %[pb] offset:0\n\t"
+      "ds_read_b128 %[y5], %[pb] offset:32\n\t"
+      "ds_read_b128 %[y6], %[pb] offset:64\n\t"
+      "ds_read_b128 %[y7], %[pb] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t01], %[pf1], %[v0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t11], %[pf1], %[v1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [v0] "+a"(acc[0]), [v1] "+a"(acc[1]), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]),
+        [y3] "=&v"(y[3]), [y4] "=&v"(y[4]), [y5] "=&v"(y[5]), [y6] "=&v"(y[6]), [y7] "=&v"(y[7])
+      : [t00] "v"(opA[0][0]), [t01] "v"(opA[0][1]), [t10] "v"(opA[1][0]), [t11] "v"(opA[1][1]),
+        [pf0] "v"(opB[0]), [pf1] "v"(opB[1]), [pa] "v"(pa), [pb] "v"(pb)
+      : "memory");
+  }
+};
+
 // ---------------------------------------------------------------------------
 // dK, dV: key-stationary
 // ---------------------------------------------------------------------------
@@ -597,6 +830,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     wait_prev(nsteps > 1);
     asm volatile("s_barrier" ::: "memory");
   }
+  constexpr uint32_t kStageBytes = TL::ELEMS * 2, kLsBytes = 2 * 64 * 2 * 4;
+  const uint32_t qs0 = lds_addr(&qs[0][0]), ds0 = lds_addr(&ds_[0][0]), ls0 = lds_addr(&ls[0][0]);
+  auto rows_at = [&](uint32_t base, int st, int qb) {
+    return base + st * kStageBytes + uint32_t((qb * 32 + rowA) * TL::ROW + 8 * hh) * 2;
+  };
+  bf16x8 qa[KD], da[KD];
+  if (nsteps > 0) lds_rows2<D>(qa, da, rows_at(qs0, 0, 0), rows_at(ds0, 0, 0));
   for (int s = 0; s < nsteps; ++s) {
     const int st = s % SK;
     const int qt = qt_begin + s / p.G;
@@ -605,33 +845,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qf0 = qt * BT + qb * 32;        // first query of the block
-      const int qfl = min(qf0 + 31, p.Lv - 1);   // last valid one
-      // any admitted pair: a query at or after the first key, within the window of the last
-      // (wave-uniform: lanes past the last key only fill columns that are never stored)
-      const bool live = qf0 < p.Lv && k0 < p.Lv && qfl >= k0 && !(window > 0 && qf0 - (k0 + 31) >= window);
-      if (!live) continue;
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-      {
-        bf16x8 qa[KD], da[KD];
-        lds_rows2<D>(qa, da, lds_addr(&qs[st][(qb * 32 + rowA) * TL::ROW + 8 * hh]),
-                     lds_addr(&ds_[st][(qb * 32 + rowA) * TL::ROW + 8 * hh]));
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vf[kk], pacc, 0, 0, 0);
-        }
-      }
-      // dO^T and Q^T fragments of the block
-      bf16x8 doT[DB][2], qT[DB][2];
-      gather_block<D>(doT, lds_addr(&ds_[st][0]), qb * 32, tb);
-      gather_block<D>(qT, lds_addr(&qs[st][0]), qb * 32, tb);
-      // lse2 and D of the 4 queries of each register group
+      f32x16 sacc, pacc;
+      bf16x8 doT[DB][2];
       float l2[16], dd[16];
       {
+        u32x2 x[D / 8];
+        u32x4 y[8];
+        const uint32_t tile = ds0 + st * kStageBytes;
+        const uint32_t ae = tile + uint32_t(tb.even + qb * 32 * TL::ROW) * 2;
+        const uint32_t ao = tile + uint32_t(tb.odd + qb * 32 * TL::ROW) * 2;
         uint32_t r[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) r[g] = lds_addr(&ls[st][2 * (qb * 32 + reg_key_offset(g, hh))]);
-        lds_lsed(l2, dd, r);
+        for (int g = 0; g < 4; ++g) r[g] = ls0 + st * kLsBytes + 8 * (qb * 32 + reg_key_offset(g, hh));
+        DkdvAsm<D>::x(sacc, pacc, qa, da, kf, vf, ae, ao, r, x, y);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j2 = 0; j2 < 2; ++j2) __builtin_memcpy(&doT[db][j2], &x[(db * 2 + j2) * 2], 16);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u32x4& v = y[2 * g + e / 2];
+            l2[4 * g + e] = __uint_as_float(v[2 * (e & 1)]);
+            dd[4 * g + e] = __uint_as_float(v[2 * (e & 1) + 1]);
+          }
       }
       // the block is full when every query sees every key of the wave and all queries are valid
       const bool full = qf0 + 31 < p.Lv && k0 + 31 <= qf0 && (window == 0 || qf0 + 31 - k0 < window);
@@ -650,20 +888,44 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
           pf[j2][i] = (__bf16)pr;
           dsf[j2][i] = (__bf16)(pr * (pacc[reg] - dd[reg]));
         }
+      bf16x8 qT[DB][2];
+      {
+        u32x2 x[D / 8];
+        const uint32_t tile = qs0 + st * kStageBytes;
+        const uint32_t ae = tile + uint32_t(tb.even + qb * 32 * TL::ROW) * 2;
+        const uint32_t ao = tile + uint32_t(tb.odd + qb * 32 * TL::ROW) * 2;
+        DkdvAsm<D>::y1(dvacc, doT, pf, ae, ao, x);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int j2 = 0; j2 < 2; ++j2) {
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doT[db][j2], pf[j2], dvacc[db], 0, 0, 0);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT[db][j2], dsf[j2], dkacc[db], 0, 0, 0);
+          for (int j2 = 0; j2 < 2; ++j2) __builtin_memcpy(&qT[db][j2], &x[(db * 2 + j2) * 2], 16);
+      }
+      // the next block's rows: (s, 1) from this stage, or (s + 1, 0) from the
+      // next one once it is published (on the last step a harmless read of a
+      // stage no DMA writes)
+      int nst = st, nqb = 1;
+      if (qb == 1) {
+        if (s + 1 < nsteps) {
+          // step s + 1 must have landed; the chunks of step s + 2 may still fly
+          wait_prev(s + 2 < nsteps);
+          asm volatile("s_barrier" ::: "memory");   // every read of this stage has returned above
         }
-    }
-    if (s + 1 < nsteps) {
-      // step s + 1 must have landed; the chunks of step s + 2 may still fly
-      wait_prev(s + 2 < nsteps);
-      asm volatile("s_barrier" ::: "memory");   // every read of step s waited for its results above
+        nst = (s + 1) % SK;
+        nqb = 0;
+      }
+      {
+        u32x4 y[2 * KD];
+        DkdvAsm<D>::y2(dkacc, qT, dsf, rows_at(qs0, nst, nqb), rows_at(ds0, nst, nqb), y);
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          __builtin_memcpy(&qa[kk], &y[kk], 16);
+          __builtin_memcpy(&da[kk], &y[KD + kk], 16);
+        }
+      }
     }
   }
+  // accumulators written by MFMAs are read by the epilogue below
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
 
   if (!kvalid) return;
   const size_t krow = (size_t(base_row + vk * pstride) * p.hkv + kvh) * D;
