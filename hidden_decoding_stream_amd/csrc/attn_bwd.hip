@@ -19,7 +19,10 @@
 //   and dO^T in registers), then P^T = exp2(S^T c - lse2) with the lane's own
 //   lse, dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T, with dS^T taken straight
 //   from the accumulators as the B operand (rows read in the sigma order) and
-//   K^T gathered by transposed LDS reads.
+//   K^T gathered by transposed LDS reads. intra and cross_full run two
+//   groups per CU (253 VGPRs, no spills: the per-lane DMA offsets are
+//   recomputed per tile, and the transposed reads share two base registers);
+//   the windowed mode runs one and its loop in asm phases (DqAsm).
 // * bwd_dkdv_kernel: key-stationary. A wave owns 32 keys (K and V in registers
 //   as B operands); the Q and dO tiles of 64 queries stream through LDS, for
 //   each of the G query heads in turn. S = Q K^T and dP = dO V^T (lane = key
@@ -29,7 +32,8 @@
 // reads hit distinct bank groups), loaded by buffer->LDS DMA through a ring
 // (2 stages for dQ, 3 for dK/dV) with one bare barrier per tile; LDS reads
 // are asm blocks that wait for their own results (see common.h), and the
-// dK/dV loop runs its MFMAs inside those blocks (DkdvAsm).
+// one-wave-per-SIMD loops run their MFMAs inside those blocks (DkdvAsm,
+// DqAsm).
 #include <math.h>
 
 #include "common.h"
@@ -41,6 +45,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;                 // one wave per SIMD per group
 constexpr int kThreads = 64 * kWaves;
@@ -81,54 +86,71 @@ template <int D> struct BTile {
 // 16 transposed reads gathering, for one 32-row block of a padded tile, the
 // A operand X^T (rows d, k = tile rows in the accumulator order of
 // reg_key_offset): output (db*2 + j2)*2 + t holds rows 16h + 4*((2t + j2) ^ h)
-// + e of 32-wide d block db, from base ae[db] (j2 = 0) or ao[db] (j2 = 1)
-// plus an immediate offset of (8t + 4j2) rows. One asm block that waits for
-// its results (a builtin read would wait for every buffer->LDS load in flight).
-template <int D> __device__ __forceinline__ void gather16(u32x2 (&x)[D / 8], const uint32_t (&ae)[D / 32],
-                                                          const uint32_t (&ao)[D / 32]);
-template <> __device__ __forceinline__ void gather16<128>(u32x2 (&x)[16], const uint32_t (&ae)[4],
-                                                          const uint32_t (&ao)[4]) {
+// + e of 32-wide d block db, from base ae (j2 = 0) or ao (j2 = 1) plus an
+// immediate offset of 64 db bytes and (8t + 4j2) rows. One asm block that
+// waits for its results (a builtin read would wait for every buffer->LDS load
+// in flight).
+template <int D> __device__ __forceinline__ void gather16(u32x2 (&x)[D / 8], uint32_t ae, uint32_t ao);
+template <> __device__ __forceinline__ void gather16<128>(u32x2 (&x)[16], uint32_t ae, uint32_t ao) {
   // row offsets (8t + 4j2) * 144 elements * 2 bytes: t0j0 0, t1j0 2304, t0j1 1152, t1j1 3456
   asm volatile(
       "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
       "ds_read_b64_tr_b16 %1, %16 offset:2304\n\t"
-      "ds_read_b64_tr_b16 %2, %20 offset:1152\n\t"
-      "ds_read_b64_tr_b16 %3, %20 offset:3456\n\t"
-      "ds_read_b64_tr_b16 %4, %17 offset:0\n\t"
-      "ds_read_b64_tr_b16 %5, %17 offset:2304\n\t"
-      "ds_read_b64_tr_b16 %6, %21 offset:1152\n\t"
-      "ds_read_b64_tr_b16 %7, %21 offset:3456\n\t"
-      "ds_read_b64_tr_b16 %8, %18 offset:0\n\t"
-      "ds_read_b64_tr_b16 %9, %18 offset:2304\n\t"
-      "ds_read_b64_tr_b16 %10, %22 offset:1152\n\t"
-      "ds_read_b64_tr_b16 %11, %22 offset:3456\n\t"
-      "ds_read_b64_tr_b16 %12, %19 offset:0\n\t"
-      "ds_read_b64_tr_b16 %13, %19 offset:2304\n\t"
-      "ds_read_b64_tr_b16 %14, %23 offset:1152\n\t"
-      "ds_read_b64_tr_b16 %15, %23 offset:3456\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:1152\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:3456\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:2368\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:1216\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:3520\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:2432\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:1280\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:3584\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:192\n\t"
+      "ds_read_b64_tr_b16 %13, %16 offset:2496\n\t"
+      "ds_read_b64_tr_b16 %14, %17 offset:1344\n\t"
+      "ds_read_b64_tr_b16 %15, %17 offset:3648\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
-        "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]),
-        "=&v"(x[15])
-      : "v"(ae[0]), "v"(ae[1]), "v"(ae[2]), "v"(ae[3]), "v"(ao[0]), "v"(ao[1]), "v"(ao[2]), "v"(ao[3])
+        "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
+      : "v"(ae), "v"(ao)
       : "memory");
 }
-template <> __device__ __forceinline__ void gather16<64>(u32x2 (&x)[8], const uint32_t (&ae)[2],
-                                                         const uint32_t (&ao)[2]) {
+template <> __device__ __forceinline__ void gather16<64>(u32x2 (&x)[8], uint32_t ae, uint32_t ao) {
   // row offsets (8t + 4j2) * 80 elements * 2 bytes: t0j0 0, t1j0 1280, t0j1 640, t1j1 1920
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
       "ds_read_b64_tr_b16 %1, %8 offset:1280\n\t"
-      "ds_read_b64_tr_b16 %2, %10 offset:640\n\t"
-      "ds_read_b64_tr_b16 %3, %10 offset:1920\n\t"
-      "ds_read_b64_tr_b16 %4, %9 offset:0\n\t"
-      "ds_read_b64_tr_b16 %5, %9 offset:1280\n\t"
-      "ds_read_b64_tr_b16 %6, %11 offset:640\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:1920\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:640\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:1920\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:1344\n\t"
+      "ds_read_b64_tr_b16 %6, %9 offset:704\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:1984\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
-      : "v"(ae[0]), "v"(ae[1]), "v"(ao[0]), "v"(ao[1])
+      : "v"(ae), "v"(ao)
       : "memory");
+}
+
+// Two 16-wide d slices of two row operands (a from pa, b from pb, 32 bytes
+// apart), in one asm block that waits only for its own results.
+__device__ __forceinline__ void lds_pair2(bf16x8 (&a)[2], bf16x8 (&b)[2], uint32_t pa, uint32_t pb) {
+  u32x4 x[4];
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:0\n\t"
+      "ds_read_b128 %1, %4 offset:32\n\t"
+      "ds_read_b128 %2, %5 offset:0\n\t"
+      "ds_read_b128 %3, %5 offset:32\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(pa), "v"(pb)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    __builtin_memcpy(&a[i], &x[i], 16);
+    __builtin_memcpy(&b[i], &x[2 + i], 16);
+  }
 }
 
 // Two row operands from LDS (a from pa, b from pb): 16-byte pieces at
@@ -212,14 +234,8 @@ template <int D>
 __device__ __forceinline__ void gather_block(bf16x8 (&out)[D / 32][2], uint32_t tile, int r0, const TrBase<D>& tb) {
   constexpr int ROW = BTile<D>::ROW;
   constexpr int DB = D / 32;
-  uint32_t ae[DB], ao[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    ae[db] = tile + uint32_t(tb.even + r0 * ROW + db * 32) * 2;
-    ao[db] = tile + uint32_t(tb.odd + r0 * ROW + db * 32) * 2;
-  }
   u32x2 x[D / 8];
-  gather16<D>(x, ae, ao);
+  gather16<D>(x, tile + uint32_t(tb.even + r0 * ROW) * 2, tile + uint32_t(tb.odd + r0 * ROW) * 2);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -294,6 +310,186 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 // group's waits overlap the other's work) where the registers allow it: the
 // windowed mask's extra state would spill, so MODE 2 keeps one group per CU.
 // ---------------------------------------------------------------------------
+// The dQ loop of the windowed mode (one wave per SIMD) in three phases per
+// 32-key block, each one asm block holding MFMAs and the LDS reads the next
+// phase needs (the scheme of DkdvAsm below):
+//   x1: S^T, dP^T over the first half of d (fresh accumulators); reads the
+//       second half of the K and V rows
+//   x2: the second half; gathers K^T (transposed)
+//   y:  dQ^T += K^T dS^T; reads the first half of the next block's rows
+template <int D> struct DqAsm;
+template <> struct DqAsm<128> {
+  static __device__ __forceinline__ void x1(f32x16& s, f32x16& p, const bf16x8 (&ka)[8], const bf16x8 (&va)[8],
+                                            const bf16x8 (&qf)[8], const bf16x8 (&dof)[8], uint32_t pa, uint32_t pb,
+                                            u32x4 (&y)[8]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka0], %[qf0], 0\n\t"
+      "ds_read_b128 %[y0], %[pa] offset:128\n\t"
+      "ds_read_b128 %[y1], %[pa] offset:160\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va0], %[dof0], 0\n\t"
+      "ds_read_b128 %[y2], %[pa] offset:192\n\t"
+      "ds_read_b128 %[y3], %[pa] offset:224\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka1], %[qf1], %[s]\n\t"
+      "ds_read_b128 %[y4], %[pb] offset:128\n\t"
+      "ds_read_b128 %[y5], %[pb] offset:160\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va1], %[dof1], %[p]\n\t"
+      "ds_read_b128 %[y6], %[pb] offset:192\n\t"
+      "ds_read_b128 %[y7], %[pb] offset:224\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka2], %[qf2], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va2], %[dof2], %[p]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka3], %[qf3], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va3], %[dof3], %[p]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [s] "=&v"(s), [p] "=&v"(p), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3]),
+        [y4] "=&v"(y[4]), [y5] "=&v"(y[5]), [y6] "=&v"(y[6]), [y7] "=&v"(y[7])
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [va0] "v"(va[0]),
+        [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [qf0] "v"(qf[0]), [qf1] "v"(qf[1]),
+        [qf2] "v"(qf[2]), [qf3] "v"(qf[3]), [dof0] "v"(dof[0]), [dof1] "v"(dof[1]), [dof2] "v"(dof[2]),
+        [dof3] "v"(dof[3]), [pa] "v"(pa), [pb] "v"(pb)
+      : "memory");
+  }
+  static __device__ __forceinline__ void x2(f32x16& s, f32x16& p, const bf16x8 (&ka)[8], const bf16x8 (&va)[8],
+                                            const bf16x8 (&qf)[8], const bf16x8 (&dof)[8], uint32_t ae, uint32_t ao,
+                                            u32x2 (&x)[16]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka0], %[qf0], %[s]\n\t"
+      "ds_read_b64_tr_b16 %[x0], %[ae] offset:0\n\t"
+      "ds_read_b64_tr_b16 %[x1], %[ae] offset:2304\n\t"
+      "ds_read_b64_tr_b16 %[x2], %[ao] offset:1152\n\t"
+      "ds_read_b64_tr_b16 %[x3], %[ao] offset:3456\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va0], %[dof0], %[p]\n\t"
+      "ds_read_b64_tr_b16 %[x4], %[ae] offset:64\n\t"
+      "ds_read_b64_tr_b16 %[x5], %[ae] offset:2368\n\t"
+      "ds_read_b64_tr_b16 %[x6], %[ao] offset:1216\n\t"
+      "ds_read_b64_tr_b16 %[x7], %[ao] offset:3520\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka1], %[qf1], %[s]\n\t"
+      "ds_read_b64_tr_b16 %[x8], %[ae] offset:128\n\t"
+      "ds_read_b64_tr_b16 %[x9], %[ae] offset:2432\n\t"
+      "ds_read_b64_tr_b16 %[x10], %[ao] offset:1280\n\t"
+      "ds_read_b64_tr_b16 %[x11], %[ao] offset:3584\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va1], %[dof1], %[p]\n\t"
+      "ds_read_b64_tr_b16 %[x12], %[ae] offset:192\n\t"
+      "ds_read_b64_tr_b16 %[x13], %[ae] offset:2496\n\t"
+      "ds_read_b64_tr_b16 %[x14], %[ao] offset:1344\n\t"
+      "ds_read_b64_tr_b16 %[x15], %[ao] offset:3648\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka2], %[qf2], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va2], %[dof2], %[p]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka3], %[qf3], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va3], %[dof3], %[p]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 3\n\t"
+      : [s] "+v"(s), [p] "+v"(p), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+        [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7]), [x8] "=&v"(x[8]),
+        [x9] "=&v"(x[9]), [x10] "=&v"(x[10]), [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]),
+        [x14] "=&v"(x[14]), [x15] "=&v"(x[15])
+      : [ka0] "v"(ka[4]), [ka1] "v"(ka[5]), [ka2] "v"(ka[6]), [ka3] "v"(ka[7]), [va0] "v"(va[4]),
+        [va1] "v"(va[5]), [va2] "v"(va[6]), [va3] "v"(va[7]), [qf0] "v"(qf[4]), [qf1] "v"(qf[5]),
+        [qf2] "v"(qf[6]), [qf3] "v"(qf[7]), [dof0] "v"(dof[4]), [dof1] "v"(dof[5]), [dof2] "v"(dof[6]),
+        [dof3] "v"(dof[7]), [ae] "v"(ae), [ao] "v"(ao)
+      : "memory");
+  }
+  static __device__ __forceinline__ void y(f32x16 (&acc)[4], const bf16x8 (&kT)[4][2], const bf16x8 (&dsf)[2],
+                                           uint32_t pa, uint32_t pb, u32x4 (&y)[8]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t00], %[ds0], %[v0]\n\t"
+      "ds_read_b128 %[y0], %[pa] offset:0\n\t"
+      "ds_read_b128 %[y1], %[pa] offset:32\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t10], %[ds0], %[v1]\n\t"
+      "ds_read_b128 %[y2], %[pa] offset:64\n\t"
+      "ds_read_b128 %[y3], %[pa] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v2], %[t20], %[ds0], %[v2]\n\t"
+      "ds_read_b128 %[y4], %[pb] offset:0\n\t"
+      "ds_read_b128 %[y5], %[pb] offset:32\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v3], %[t30], %[ds0], %[v3]\n\t"
+      "ds_read_b128 %[y6], %[pb] offset:64\n\t"
+      "ds_read_b128 %[y7], %[pb] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t01], %[ds1], %[v0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t11], %[ds1], %[v1]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v2], %[t21], %[ds1], %[v2]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v3], %[t31], %[ds1], %[v3]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [v0] "+a"(acc[0]), [v1] "+a"(acc[1]), [v2] "+a"(acc[2]), [v3] "+a"(acc[3]), [y0] "=&v"(y[0]),
+        [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3]), [y4] "=&v"(y[4]), [y5] "=&v"(y[5]),
+        [y6] "=&v"(y[6]), [y7] "=&v"(y[7])
+      : [t00] "v"(kT[0][0]), [t01] "v"(kT[0][1]), [t10] "v"(kT[1][0]), [t11] "v"(kT[1][1]), [t20] "v"(kT[2][0]),
+        [t21] "v"(kT[2][1]), [t30] "v"(kT[3][0]), [t31] "v"(kT[3][1]), [ds0] "v"(dsf[0]), [ds1] "v"(dsf[1]),
+        [pa] "v"(pa), [pb] "v"(pb)
+      : "memory");
+  }
+};
+template <> struct DqAsm<64> {
+  static __device__ __forceinline__ void x1(f32x16& s, f32x16& p, const bf16x8 (&ka)[4], const bf16x8 (&va)[4],
+                                            const bf16x8 (&qf)[4], const bf16x8 (&dof)[4], uint32_t pa, uint32_t pb,
+                                            u32x4 (&y)[4]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka0], %[qf0], 0\n\t"
+      "ds_read_b128 %[y0], %[pa] offset:64\n\t"
+      "ds_read_b128 %[y1], %[pa] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va0], %[dof0], 0\n\t"
+      "ds_read_b128 %[y2], %[pb] offset:64\n\t"
+      "ds_read_b128 %[y3], %[pb] offset:96\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka1], %[qf1], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va1], %[dof1], %[p]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [s] "=&v"(s), [p] "=&v"(p), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [va0] "v"(va[0]), [va1] "v"(va[1]), [qf0] "v"(qf[0]),
+        [qf1] "v"(qf[1]), [dof0] "v"(dof[0]), [dof1] "v"(dof[1]), [pa] "v"(pa), [pb] "v"(pb)
+      : "memory");
+  }
+  static __device__ __forceinline__ void x2(f32x16& s, f32x16& p, const bf16x8 (&ka)[4], const bf16x8 (&va)[4],
+                                            const bf16x8 (&qf)[4], const bf16x8 (&dof)[4], uint32_t ae, uint32_t ao,
+                                            u32x2 (&x)[8]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka0], %[qf0], %[s]\n\t"
+      "ds_read_b64_tr_b16 %[x0], %[ae] offset:0\n\t"
+      "ds_read_b64_tr_b16 %[x1], %[ae] offset:1280\n\t"
+      "ds_read_b64_tr_b16 %[x2], %[ao] offset:640\n\t"
+      "ds_read_b64_tr_b16 %[x3], %[ao] offset:1920\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va0], %[dof0], %[p]\n\t"
+      "ds_read_b64_tr_b16 %[x4], %[ae] offset:64\n\t"
+      "ds_read_b64_tr_b16 %[x5], %[ae] offset:1344\n\t"
+      "ds_read_b64_tr_b16 %[x6], %[ao] offset:704\n\t"
+      "ds_read_b64_tr_b16 %[x7], %[ao] offset:1984\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[ka1], %[qf1], %[s]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[p], %[va1], %[dof1], %[p]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 3\n\t"
+      : [s] "+v"(s), [p] "+v"(p), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+        [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+      : [ka0] "v"(ka[2]), [ka1] "v"(ka[3]), [va0] "v"(va[2]), [va1] "v"(va[3]), [qf0] "v"(qf[2]),
+        [qf1] "v"(qf[3]), [dof0] "v"(dof[2]), [dof1] "v"(dof[3]), [ae] "v"(ae), [ao] "v"(ao)
+      : "memory");
+  }
+  static __device__ __forceinline__ void y(f32x16 (&acc)[2], const bf16x8 (&kT)[2][2], const bf16x8 (&dsf)[2],
+                                           uint32_t pa, uint32_t pb, u32x4 (&y)[4]) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t00], %[ds0], %[v0]\n\t"
+      "ds_read_b128 %[y0], %[pa] offset:0\n\t"
+      "ds_read_b128 %[y1], %[pa] offset:32\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t10], %[ds0], %[v1]\n\t"
+      "ds_read_b128 %[y2], %[pb] offset:0\n\t"
+      "ds_read_b128 %[y3], %[pb] offset:32\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v0], %[t01], %[ds1], %[v0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[v1], %[t11], %[ds1], %[v1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [v0] "+a"(acc[0]), [v1] "+a"(acc[1]), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]),
+        [y3] "=&v"(y[3])
+      : [t00] "v"(kT[0][0]), [t01] "v"(kT[0][1]), [t10] "v"(kT[1][0]), [t11] "v"(kT[1][1]), [ds0] "v"(dsf[0]),
+        [ds1] "v"(dsf[1]), [pa] "v"(pa), [pb] "v"(pb)
+      : "memory");
+  }
+};
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(BwdParams p) {
   using TL = BTile<D>;
@@ -358,16 +554,22 @@ __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(Bwd
   // sl = 64*chunk + lane is row sl / SLOTS, 16-byte slot sl % SLOTS (the
   // padding slots and rows past the end read zeros). The offsets are
   // recomputed per tile rather than held in registers.
+  const uint32_t row_bytes = uint32_t(pstride) * kv_pos_bytes;   // between rows of a virtual sequence
   auto issue = [&](int kt) {
     const int st = kt % ST;
     const uint32_t tbase = uint32_t(base_row + kt * BT * pstride) * kv_pos_bytes + kv_head_bytes;
+    // the lane's slot positions are recomputed on every call rather than held
+    // in registers across the loop (the opaque copy keeps the compiler from
+    // hoisting them)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
       const int c = wave + j * kWaves;
-      const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + lane;
+      const int sl = (c < TL::CH ? c : c - TL::CH) * 64 + ln;
       const int row = sl / TL::SLOTS, ch = sl % TL::SLOTS;
       const bool ok = ch < D / 8 && kt * BT + row < p.Lv;
-      const uint32_t off = ok ? tbase + uint32_t(row * pstride) * kv_pos_bytes + ch * 16 : kOobOffset;
+      const uint32_t off = ok ? tbase + uint32_t(row) * row_bytes + ch * 16 : kOobOffset;
       if (c < TL::CH) dma16(krs, &ks[st][c * 512], off);
       else dma16(vrs, &vs[st][(c - TL::CH) * 512], off);
     }
@@ -384,66 +586,151 @@ __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(Bwd
   issue(kt_begin);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_barrier" ::: "memory");
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int st = kt % ST;
-    const int k0 = kt * BT;
-    if (kt + 1 < kt_end) issue(kt + 1);
-    const bool live = wave_live && k0 <= qhi && !(window > 0 && q0 - (k0 + BT - 1) >= window);
-    if (live) {
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u16* kr = &ks[st][(kb * 32 + rowA) * TL::ROW + 8 * hh];
-        const u16* vr = &vs[st][(kb * 32 + rowA) * TL::ROW + 8 * hh];
-        bf16x8 ka[KD], va[KD];
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          ka[kk] = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
-          va[kk] = *reinterpret_cast<const bf16x8*>(vr + kk * 16);
-        }
-        sacc[kb] = f32x16{};
-        pacc[kb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], sacc[kb], 0, 0, 0);
-          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], dof[kk], pacc[kb], 0, 0, 0);
-        }
-      }
-      // K^T fragments for dQ^T += K^T dS^T
-      bf16x8 kT[2][DB][2];
-      const uint32_t kt_lds = lds_addr(&ks[st][0]);
-      gather_block<D>(kT[0], kt_lds, 0, tb);
-      gather_block<D>(kT[1], kt_lds, 32, tb);
-
+  if constexpr (MODE == 2) {
+    // one wave per SIMD: the phases in asm (DqAsm), every tile processed and
+    // masked (no per-wave skip, so that the prefetch chain stays unbroken)
+    constexpr int H = KD / 2;
+    constexpr uint32_t kStageBytes = TL::ELEMS * 2;
+    const uint32_t ks0 = lds_addr(&ks[0][0]), vs0 = lds_addr(&vs[0][0]);
+    auto rows_at = [&](uint32_t base, int st, int kb) {
+      return base + st * kStageBytes + uint32_t((kb * 32 + rowA) * TL::ROW + 8 * hh) * 2;
+    };
+    const uint32_t lim = uint32_t(window);
+    bf16x8 ka[KD], va[KD];
+    lds_rows2<D>(ka, va, rows_at(ks0, kt_begin % ST, 0), rows_at(vs0, kt_begin % ST, 0));
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const int st = kt % ST;
+      const int k0 = kt * BT;
+      if (kt + 1 < kt_end) issue(kt + 1);
       const bool full = (k0 + BT - 1 <= q0) && (window == 0 || qhi - k0 < window);
-      const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc, pacc;
+        {
+          u32x4 y[KD];
+          DqAsm<D>::x1(sacc, pacc, ka, va, qf, dof, rows_at(ks0, st, kb), rows_at(vs0, st, kb), y);
+#pragma unroll
+          for (int k = 0; k < H; ++k) {
+            __builtin_memcpy(&ka[H + k], &y[k], 16);
+            __builtin_memcpy(&va[H + k], &y[H + k], 16);
+          }
+        }
+        bf16x8 kT[DB][2];
+        {
+          u32x2 x[D / 8];
+          const uint32_t tile = ks0 + st * kStageBytes;
+          const uint32_t ae = tile + uint32_t(tb.even + kb * 32 * TL::ROW) * 2;
+          const uint32_t ao = tile + uint32_t(tb.odd + kb * 32 * TL::ROW) * 2;
+          DqAsm<D>::x2(sacc, pacc, ka, va, qf, dof, ae, ao, x);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j2 = 0; j2 < 2; ++j2) __builtin_memcpy(&kT[db][j2], &x[(db * 2 + j2) * 2], 16);
+        }
         bf16x8 dsf[2];
 #pragma unroll
         for (int j2 = 0; j2 < 2; ++j2) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int reg = j2 * 8 + i;
-            float s = sacc[kb][reg];
+            float s = sacc[reg];
             if (!full) {
               const int key = k0 + kb * 32 + reg_key_offset(reg >> 2, hh) + (reg & 3);
               if (!(uint32_t(vq - key) < lim)) s = -INFINITY;
             }
             const float pr = __builtin_amdgcn_exp2f(fmaf(s, p.c, -lse2));
-            dsf[j2][i] = (__bf16)(pr * (pacc[kb][reg] - dq_d));
+            dsf[j2][i] = (__bf16)(pr * (pacc[reg] - dq_d));
           }
         }
+        // the next block's rows: (kt, 1) from this stage, or (kt + 1, 0) from
+        // the next one once it is published (after the last tile a harmless
+        // read of a stage no DMA writes)
+        int nst = st, nkb = 1;
+        if (kb == 1) {
+          if (kt + 1 < kt_end) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");   // every read of this stage has returned above
+          }
+          nst = (kt + 1) % ST;
+          nkb = 0;
+        }
+        {
+          u32x4 y[KD];
+          DqAsm<D>::y(dqacc, kT, dsf, rows_at(ks0, nst, nkb), rows_at(vs0, nst, nkb), y);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2)
-            dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT[kb][db][j2], dsf[j2], dqacc[db], 0, 0, 0);
+          for (int k = 0; k < H; ++k) {
+            __builtin_memcpy(&ka[k], &y[k], 16);
+            __builtin_memcpy(&va[k], &y[H + k], 16);
+          }
+        }
       }
     }
-    if (kt + 1 < kt_end) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      asm volatile("s_barrier" ::: "memory");   // no fence needed: every read of stage st was consumed above
+    // accumulators written by MFMAs are read by the epilogue below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+  } else {
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const int st = kt % ST;
+      const int k0 = kt * BT;
+      if (kt + 1 < kt_end) issue(kt + 1);
+      const bool live = wave_live && k0 <= qhi && !(window > 0 && q0 - (k0 + BT - 1) >= window);
+      if (live) {
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // K and V rows, two 16-wide d slices at a time, by asm reads that wait
+          // only for themselves (a C++ read here made the compiler wait for the
+          // next tile's DMA first)
+          const uint32_t pk = lds_addr(&ks[st][(kb * 32 + rowA) * TL::ROW + 8 * hh]);
+          const uint32_t pv = lds_addr(&vs[st][(kb * 32 + rowA) * TL::ROW + 8 * hh]);
+          sacc[kb] = f32x16{};
+          pacc[kb] = f32x16{};
+#pragma unroll
+          for (int j = 0; j < KD / 2; ++j) {
+            bf16x8 ka[2], va[2];
+            lds_pair2(ka, va, pk + 64 * j, pv + 64 * j);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t], qf[2 * j + t], sacc[kb], 0, 0, 0);
+              pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], dof[2 * j + t], pacc[kb], 0, 0, 0);
+            }
+          }
+        }
+        // K^T fragments for dQ^T += K^T dS^T
+        bf16x8 kT[2][DB][2];
+        const uint32_t kt_lds = lds_addr(&ks[st][0]);
+        gather_block<D>(kT[0], kt_lds, 0, tb);
+        gather_block<D>(kT[1], kt_lds, 32, tb);
+
+        const bool full = (k0 + BT - 1 <= q0) && (window == 0 || qhi - k0 < window);
+        const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          bf16x8 dsf[2];
+#pragma unroll
+          for (int j2 = 0; j2 < 2; ++j2) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int reg = j2 * 8 + i;
+              float s = sacc[kb][reg];
+              if (!full) {
+                const int key = k0 + kb * 32 + reg_key_offset(reg >> 2, hh) + (reg & 3);
+                if (!(uint32_t(vq - key) < lim)) s = -INFINITY;
+              }
+              const float pr = __builtin_amdgcn_exp2f(fmaf(s, p.c, -lse2));
+              dsf[j2][i] = (__bf16)(pr * (pacc[kb][reg] - dq_d));
+            }
+          }
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j2 = 0; j2 < 2; ++j2)
+              dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT[kb][db][j2], dsf[j2], dqacc[db], 0, 0, 0);
+        }
+      }
+      if (kt + 1 < kt_end) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");   // no fence needed: every read of stage st was consumed above
+      }
     }
   }
 
@@ -462,7 +749,6 @@ __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(Bwd
 }
 
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // The dK/dV loop in three phases per 32-query block, each one asm block that
 // issues the phase's MFMAs with the LDS reads the next phase needs spread over
 // the first half of them, and waits for those reads only at its end: with one
