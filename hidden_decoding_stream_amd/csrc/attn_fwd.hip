@@ -32,14 +32,16 @@
 //   transposed LDS read ds_read_b64_tr_b16, addressed so that each lane
 //   receives exactly the keys its P^T registers hold.
 // * Memory. K and V tiles go from HBM to LDS by buffer->LDS DMA loads (no
-//   staging registers, no LDS write instructions) through a 4-stage ring
-//   worked in pairs of tiles: the first tile of a pair sends out the DMA of
-//   the next pair, and one bare barrier per pair publishes it. Rows past the end of a sequence use an
-//   out-of-range offset and read as zeros, with no branch. K rows are padded
+//   staging registers, no LDS write instructions) through a 4-stage ring,
+//   two tiles ahead, one barrier per tile. Rows past the end of a sequence
+//   use an out-of-range offset and read as zeros, with no branch. K rows are padded
 //   and V pieces swizzled so that the operand reads are free of bank
 //   conflicts.
 // * Occupancy. A work group is 8 waves (two per SIMD), each owning 32
 //   queries of one query head; one group per CU (138 KiB of LDS at d=128).
+//   The two waves of a SIMD run their MFMA and softmax phases in opposite
+//   order (ping-pong), so that the VALU-heavy softmax of one overlaps the
+//   MFMAs of the other.
 // * Online softmax in base 2 with lazy rescaling: the running reference max m
 //   is raised only when a tile's max exceeds it by more than 2^8; until then
 //   exp2(s - m) <= 256 and no O rescale is needed. The result is the same
@@ -50,6 +52,8 @@
 //   blocks run on the same XCD at the same time and share its L2. Within a
 //   range the heaviest (latest) query blocks go first.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -97,79 +101,314 @@ struct FwdParams {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// All V^T fragments of a tile in one asm block of ds_read_b64_tr_b16,
-// which also waits for them: output i = ((db*2 + kb)*2 + j2)*2 + tr reads
-// key row kb*32 + 4*(2*tr + j2) (+ the lane's row within its group) of the
-// 32-wide d block db, from base ae[db] (j2 = 0) or ao[db] (j2 = 1) plus an
-// immediate offset. Through the builtin, the compiler cannot tell which LDS
-// a transposed read touches and waits for every buffer->LDS load in flight
-// before it, which would drain the DMA of the next tiles on every tile.
-template <int D> __device__ __forceinline__ void gather_vt(u32x2 (&x)[D / 4], const uint32_t (&ae)[D / 32],
-                                                          const uint32_t (&ao)[D / 32]);
-template <> __device__ __forceinline__ void gather_vt<128>(u32x2 (&x)[32], const uint32_t (&ae)[4],
-                                                          const uint32_t (&ao)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %32 offset:0\n\t"
-      "ds_read_b64_tr_b16 %1, %32 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %2, %36 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %3, %36 offset:3072\n\t"
-      "ds_read_b64_tr_b16 %4, %32 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %5, %32 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %6, %36 offset:9216\n\t"
-      "ds_read_b64_tr_b16 %7, %36 offset:11264\n\t"
-      "ds_read_b64_tr_b16 %8, %33 offset:0\n\t"
-      "ds_read_b64_tr_b16 %9, %33 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %10, %37 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %11, %37 offset:3072\n\t"
-      "ds_read_b64_tr_b16 %12, %33 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %13, %33 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %14, %37 offset:9216\n\t"
-      "ds_read_b64_tr_b16 %15, %37 offset:11264\n\t"
-      "ds_read_b64_tr_b16 %16, %34 offset:0\n\t"
-      "ds_read_b64_tr_b16 %17, %34 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %18, %38 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %19, %38 offset:3072\n\t"
-      "ds_read_b64_tr_b16 %20, %34 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %21, %34 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %22, %38 offset:9216\n\t"
-      "ds_read_b64_tr_b16 %23, %38 offset:11264\n\t"
-      "ds_read_b64_tr_b16 %24, %35 offset:0\n\t"
-      "ds_read_b64_tr_b16 %25, %35 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %26, %39 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %27, %39 offset:3072\n\t"
-      "ds_read_b64_tr_b16 %28, %35 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %29, %35 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %30, %39 offset:9216\n\t"
-      "ds_read_b64_tr_b16 %31, %39 offset:11264\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]), "=&v"(x[18]), "=&v"(x[19]), "=&v"(x[20]), "=&v"(x[21]), "=&v"(x[22]), "=&v"(x[23]), "=&v"(x[24]), "=&v"(x[25]), "=&v"(x[26]), "=&v"(x[27]), "=&v"(x[28]), "=&v"(x[29]), "=&v"(x[30]), "=&v"(x[31])
-      : "v"(ae[0]), "v"(ae[1]), "v"(ae[2]), "v"(ae[3]), "v"(ao[0]), "v"(ao[1]), "v"(ao[2]), "v"(ao[3])
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The MFMA phase of a tile in asm blocks, each holding MFMAs and the LDS
+// reads of the next block spread over the first half of them, and waiting
+// for those reads only at its end (a read left in flight past its asm block
+// could land in a register the compiler has meanwhile reused). Transposed
+// reads (ds_read_b64_tr_b16) are asm in any case: through the builtin the
+// compiler cannot tell which LDS a read touches and waits for every
+// buffer->LDS load in flight first. Wait states the compiler cannot see
+// inside asm are written out: s_nop 2 before MFMAs that read VALU-written
+// registers, and 20 after the score MFMAs whose results the VALU reads next.
+// V^T chunk layout (8 transposed reads x[0..7]): for d blocks e0, e1 of one
+// 32-key block kb, x[4e + 2j2 + tr] reads key rows kb*32 + 4*(2*tr + j2) (+
+// the lane's row within its group) from base ae[e] (j2 = 0) or ao[e] (j2 = 1)
+// plus an immediate offset; x[2j], x[2j+1] form MFMA operand j.
+template <int D> struct PpAsm;
+template <> struct PpAsm<128> {
+  // P V chunk: O^T of d blocks e0, e1 += V^T P^T over one 32-key block (operands t: e0 j0, e0 j1,
+  // e1 j0, e1 j1; P p0, p1 = j2 0, 1), two accumulators in turn, reading the V^T chunk of the next
+  // (32-key block KB, d pair) at bases a0/b0 (d block e0) and a1/b1 (e1)
+  template <int KB> static __device__ __forceinline__ void pv_mid(f32x16& o0, f32x16& o1, const bf16x8 (&t)[4],
+                                                                  const bf16x8& p0, const bf16x8& p1, uint32_t a0,
+                                                                  uint32_t b0, uint32_t a1, uint32_t b1, u32x2 (&x)[8]) {
+    if constexpr (KB == 0) {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n\t"
+        "ds_read_b64_tr_b16 %[x0], %[a0] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x1], %[a0] offset:2048\n\t"
+        "ds_read_b64_tr_b16 %[x2], %[b0] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x3], %[b0] offset:3072\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t2], %[p0], %[o1]\n\t"
+        "ds_read_b64_tr_b16 %[x4], %[a1] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x5], %[a1] offset:2048\n\t"
+        "ds_read_b64_tr_b16 %[x6], %[b1] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x7], %[b1] offset:3072\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t1], %[p1], %[o0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p1], %[o1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [o0] "+v"(o0), [o1] "+v"(o1), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+          [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+        : [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2]), [t3] "v"(t[3]), [p0] "v"(p0), [p1] "v"(p1), [a0] "v"(a0),
+          [b0] "v"(b0), [a1] "v"(a1), [b1] "v"(b1)
+        : "memory");
+    } else {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n\t"
+        "ds_read_b64_tr_b16 %[x0], %[a0] offset:8192\n\t"
+        "ds_read_b64_tr_b16 %[x1], %[a0] offset:10240\n\t"
+        "ds_read_b64_tr_b16 %[x2], %[b0] offset:9216\n\t"
+        "ds_read_b64_tr_b16 %[x3], %[b0] offset:11264\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t2], %[p0], %[o1]\n\t"
+        "ds_read_b64_tr_b16 %[x4], %[a1] offset:8192\n\t"
+        "ds_read_b64_tr_b16 %[x5], %[a1] offset:10240\n\t"
+        "ds_read_b64_tr_b16 %[x6], %[b1] offset:9216\n\t"
+        "ds_read_b64_tr_b16 %[x7], %[b1] offset:11264\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t1], %[p1], %[o0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p1], %[o1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [o0] "+v"(o0), [o1] "+v"(o1), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+          [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+        : [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2]), [t3] "v"(t[3]), [p0] "v"(p0), [p1] "v"(p1), [a0] "v"(a0),
+          [b0] "v"(b0), [a1] "v"(a1), [b1] "v"(b1)
+        : "memory");
+    }
+  }
+  // the last P V chunk, reading K chunk 0 (kk 0, 1 of both 32-key blocks) for the scores
+  static __device__ __forceinline__ void pv_last(f32x16& o0, f32x16& o1, const bf16x8 (&t)[4], const bf16x8& p0,
+                                                 const bf16x8& p1, uint32_t kb, u32x4 (&y)[4]) {
+    asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n\t"
+      "ds_read_b128 %[y0], %[kb] offset:0\n\t"
+      "ds_read_b128 %[y1], %[kb] offset:32\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t2], %[p0], %[o1]\n\t"
+      "ds_read_b128 %[y2], %[kb] offset:9216\n\t"
+      "ds_read_b128 %[y3], %[kb] offset:9248\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t1], %[p1], %[o0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p1], %[o1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [o0] "+v"(o0), [o1] "+v"(o1), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+      : [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2]), [t3] "v"(t[3]), [p0] "v"(p0), [p1] "v"(p1), [kb] "v"(kb)
       : "memory");
-}
-template <> __device__ __forceinline__ void gather_vt<64>(u32x2 (&x)[16], const uint32_t (&ae)[2],
-                                                          const uint32_t (&ao)[2]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
-      "ds_read_b64_tr_b16 %1, %16 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %2, %18 offset:512\n\t"
-      "ds_read_b64_tr_b16 %3, %18 offset:1536\n\t"
-      "ds_read_b64_tr_b16 %4, %16 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %5, %16 offset:5120\n\t"
-      "ds_read_b64_tr_b16 %6, %18 offset:4608\n\t"
-      "ds_read_b64_tr_b16 %7, %18 offset:5632\n\t"
-      "ds_read_b64_tr_b16 %8, %17 offset:0\n\t"
-      "ds_read_b64_tr_b16 %9, %17 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %10, %19 offset:512\n\t"
-      "ds_read_b64_tr_b16 %11, %19 offset:1536\n\t"
-      "ds_read_b64_tr_b16 %12, %17 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %13, %17 offset:5120\n\t"
-      "ds_read_b64_tr_b16 %14, %19 offset:4608\n\t"
-      "ds_read_b64_tr_b16 %15, %19 offset:5632\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
-      : "v"(ae[0]), "v"(ae[1]), "v"(ao[0]), "v"(ao[1])
+  }
+  // K chunk 0 alone (scores without a P V before them)
+  static __device__ __forceinline__ void k_first(uint32_t kb, u32x4 (&y)[4]) {
+    asm volatile(
+      "ds_read_b128 %[y0], %[kb] offset:0\n\t"
+      "ds_read_b128 %[y1], %[kb] offset:32\n\t"
+      "ds_read_b128 %[y2], %[kb] offset:9216\n\t"
+      "ds_read_b128 %[y3], %[kb] offset:9248\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+      : [kb] "v"(kb)
       : "memory");
-}
+  }
+  // S^T = K Q^T, kk pair C (operands a: kb0 kk, kb0 kk+1, kb1 kk, kb1 kk+1), reading K chunk C+1;
+  // the last pair reads the first V^T chunk of the tile (32-key block 0, d blocks 0 and 1) for the
+  // P V of the next MFMA phase and ends with the wait states for the VALU reading the scores
+  template <int C> static __device__ __forceinline__ void s_step(f32x16& s0, f32x16& s1, const bf16x8 (&a)[4],
+                                                                  const bf16x8& q0, const bf16x8& q1, uint32_t kb,
+                                                                  u32x4 (&y)[4], uint32_t a0, uint32_t b0, uint32_t a1,
+                                                                  uint32_t b1, u32x2 (&x)[8]) {
+    if constexpr (C == 0) {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k0], %[q0], 0\n\t"
+        "ds_read_b128 %[y0], %[kb] offset:64\n\t"
+        "ds_read_b128 %[y1], %[kb] offset:96\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k2], %[q0], 0\n\t"
+        "ds_read_b128 %[y2], %[kb] offset:9280\n\t"
+        "ds_read_b128 %[y3], %[kb] offset:9312\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k1], %[q1], %[s0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k3], %[q1], %[s1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [s0] "=&v"(s0), [s1] "=&v"(s1), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+        : [k0] "v"(a[0]), [k1] "v"(a[1]), [k2] "v"(a[2]), [k3] "v"(a[3]), [q0] "v"(q0), [q1] "v"(q1), [kb] "v"(kb)
+        : "memory");
+    } else if constexpr (C == 1) {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k0], %[q0], %[s0]\n\t"
+        "ds_read_b128 %[y0], %[kb] offset:128\n\t"
+        "ds_read_b128 %[y1], %[kb] offset:160\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k2], %[q0], %[s1]\n\t"
+        "ds_read_b128 %[y2], %[kb] offset:9344\n\t"
+        "ds_read_b128 %[y3], %[kb] offset:9376\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k1], %[q1], %[s0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k3], %[q1], %[s1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [s0] "+v"(s0), [s1] "+v"(s1), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+        : [k0] "v"(a[0]), [k1] "v"(a[1]), [k2] "v"(a[2]), [k3] "v"(a[3]), [q0] "v"(q0), [q1] "v"(q1), [kb] "v"(kb)
+        : "memory");
+    } else if constexpr (C == 2) {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k0], %[q0], %[s0]\n\t"
+        "ds_read_b128 %[y0], %[kb] offset:192\n\t"
+        "ds_read_b128 %[y1], %[kb] offset:224\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k2], %[q0], %[s1]\n\t"
+        "ds_read_b128 %[y2], %[kb] offset:9408\n\t"
+        "ds_read_b128 %[y3], %[kb] offset:9440\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k1], %[q1], %[s0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k3], %[q1], %[s1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [s0] "+v"(s0), [s1] "+v"(s1), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+        : [k0] "v"(a[0]), [k1] "v"(a[1]), [k2] "v"(a[2]), [k3] "v"(a[3]), [q0] "v"(q0), [q1] "v"(q1), [kb] "v"(kb)
+        : "memory");
+    } else {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k0], %[q0], %[s0]\n\t"
+        "ds_read_b64_tr_b16 %[x0], %[a0] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x1], %[a0] offset:2048\n\t"
+        "ds_read_b64_tr_b16 %[x2], %[b0] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x3], %[b0] offset:3072\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k2], %[q0], %[s1]\n\t"
+        "ds_read_b64_tr_b16 %[x4], %[a1] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x5], %[a1] offset:2048\n\t"
+        "ds_read_b64_tr_b16 %[x6], %[b1] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x7], %[b1] offset:3072\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k1], %[q1], %[s0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k3], %[q1], %[s1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 7\n\t"
+        "s_nop 7\n\t"
+        "s_nop 3\n\t"
+        : [s0] "+v"(s0), [s1] "+v"(s1), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+          [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+        : [k0] "v"(a[0]), [k1] "v"(a[1]), [k2] "v"(a[2]), [k3] "v"(a[3]), [q0] "v"(q0), [q1] "v"(q1), [a0] "v"(a0),
+          [b0] "v"(b0), [a1] "v"(a1), [b1] "v"(b1)
+        : "memory");
+    }
+  }
+};
+
+template <> struct PpAsm<64> {
+  // P V chunk: O^T of d blocks e0, e1 += V^T P^T over one 32-key block (operands t: e0 j0, e0 j1,
+  // e1 j0, e1 j1; P p0, p1 = j2 0, 1), two accumulators in turn, reading the V^T chunk of the next
+  // (32-key block KB, d pair) at bases a0/b0 (d block e0) and a1/b1 (e1)
+  template <int KB> static __device__ __forceinline__ void pv_mid(f32x16& o0, f32x16& o1, const bf16x8 (&t)[4],
+                                                                  const bf16x8& p0, const bf16x8& p1, uint32_t a0,
+                                                                  uint32_t b0, uint32_t a1, uint32_t b1, u32x2 (&x)[8]) {
+    if constexpr (KB == 0) {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n\t"
+        "ds_read_b64_tr_b16 %[x0], %[a0] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x1], %[a0] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x2], %[b0] offset:512\n\t"
+        "ds_read_b64_tr_b16 %[x3], %[b0] offset:1536\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t2], %[p0], %[o1]\n\t"
+        "ds_read_b64_tr_b16 %[x4], %[a1] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x5], %[a1] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x6], %[b1] offset:512\n\t"
+        "ds_read_b64_tr_b16 %[x7], %[b1] offset:1536\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t1], %[p1], %[o0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p1], %[o1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [o0] "+v"(o0), [o1] "+v"(o1), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+          [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+        : [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2]), [t3] "v"(t[3]), [p0] "v"(p0), [p1] "v"(p1), [a0] "v"(a0),
+          [b0] "v"(b0), [a1] "v"(a1), [b1] "v"(b1)
+        : "memory");
+    } else {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n\t"
+        "ds_read_b64_tr_b16 %[x0], %[a0] offset:4096\n\t"
+        "ds_read_b64_tr_b16 %[x1], %[a0] offset:5120\n\t"
+        "ds_read_b64_tr_b16 %[x2], %[b0] offset:4608\n\t"
+        "ds_read_b64_tr_b16 %[x3], %[b0] offset:5632\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t2], %[p0], %[o1]\n\t"
+        "ds_read_b64_tr_b16 %[x4], %[a1] offset:4096\n\t"
+        "ds_read_b64_tr_b16 %[x5], %[a1] offset:5120\n\t"
+        "ds_read_b64_tr_b16 %[x6], %[b1] offset:4608\n\t"
+        "ds_read_b64_tr_b16 %[x7], %[b1] offset:5632\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o0], %[t1], %[p1], %[o0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p1], %[o1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [o0] "+v"(o0), [o1] "+v"(o1), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+          [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+        : [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2]), [t3] "v"(t[3]), [p0] "v"(p0), [p1] "v"(p1), [a0] "v"(a0),
+          [b0] "v"(b0), [a1] "v"(a1), [b1] "v"(b1)
+        : "memory");
+    }
+  }
+  // the last P V chunk, reading K chunk 0 (kk 0, 1 of both 32-key blocks) for the scores
+  static __device__ __forceinline__ void pv_last(f32x16& o0, f32x16& o1, const bf16x8 (&t)[4], const bf16x8& p0,
+                                                 const bf16x8& p1, uint32_t kb, u32x4 (&y)[4]) {
+    asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n\t"
+      "ds_read_b128 %[y0], %[kb] offset:0\n\t"
+      "ds_read_b128 %[y1], %[kb] offset:32\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t2], %[p0], %[o1]\n\t"
+      "ds_read_b128 %[y2], %[kb] offset:5120\n\t"
+      "ds_read_b128 %[y3], %[kb] offset:5152\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t1], %[p1], %[o0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p1], %[o1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [o0] "+v"(o0), [o1] "+v"(o1), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+      : [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2]), [t3] "v"(t[3]), [p0] "v"(p0), [p1] "v"(p1), [kb] "v"(kb)
+      : "memory");
+  }
+  // K chunk 0 alone (scores without a P V before them)
+  static __device__ __forceinline__ void k_first(uint32_t kb, u32x4 (&y)[4]) {
+    asm volatile(
+      "ds_read_b128 %[y0], %[kb] offset:0\n\t"
+      "ds_read_b128 %[y1], %[kb] offset:32\n\t"
+      "ds_read_b128 %[y2], %[kb] offset:5120\n\t"
+      "ds_read_b128 %[y3], %[kb] offset:5152\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+      : [kb] "v"(kb)
+      : "memory");
+  }
+  // S^T = K Q^T, kk pair C (operands a: kb0 kk, kb0 kk+1, kb1 kk, kb1 kk+1), reading K chunk C+1;
+  // the last pair reads the first V^T chunk of the tile (32-key block 0, d blocks 0 and 1) for the
+  // P V of the next MFMA phase and ends with the wait states for the VALU reading the scores
+  template <int C> static __device__ __forceinline__ void s_step(f32x16& s0, f32x16& s1, const bf16x8 (&a)[4],
+                                                                  const bf16x8& q0, const bf16x8& q1, uint32_t kb,
+                                                                  u32x4 (&y)[4], uint32_t a0, uint32_t b0, uint32_t a1,
+                                                                  uint32_t b1, u32x2 (&x)[8]) {
+    if constexpr (C == 0) {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k0], %[q0], 0\n\t"
+        "ds_read_b128 %[y0], %[kb] offset:64\n\t"
+        "ds_read_b128 %[y1], %[kb] offset:96\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k2], %[q0], 0\n\t"
+        "ds_read_b128 %[y2], %[kb] offset:5184\n\t"
+        "ds_read_b128 %[y3], %[kb] offset:5216\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k1], %[q1], %[s0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k3], %[q1], %[s1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        : [s0] "=&v"(s0), [s1] "=&v"(s1), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3])
+        : [k0] "v"(a[0]), [k1] "v"(a[1]), [k2] "v"(a[2]), [k3] "v"(a[3]), [q0] "v"(q0), [q1] "v"(q1), [kb] "v"(kb)
+        : "memory");
+    } else {
+      asm volatile(
+        "s_nop 2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k0], %[q0], %[s0]\n\t"
+        "ds_read_b64_tr_b16 %[x0], %[a0] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x1], %[a0] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x2], %[b0] offset:512\n\t"
+        "ds_read_b64_tr_b16 %[x3], %[b0] offset:1536\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k2], %[q0], %[s1]\n\t"
+        "ds_read_b64_tr_b16 %[x4], %[a1] offset:0\n\t"
+        "ds_read_b64_tr_b16 %[x5], %[a1] offset:1024\n\t"
+        "ds_read_b64_tr_b16 %[x6], %[b1] offset:512\n\t"
+        "ds_read_b64_tr_b16 %[x7], %[b1] offset:1536\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s0], %[k1], %[q1], %[s0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[s1], %[k3], %[q1], %[s1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 7\n\t"
+        "s_nop 7\n\t"
+        "s_nop 3\n\t"
+        : [s0] "+v"(s0), [s1] "+v"(s1), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
+          [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7])
+        : [k0] "v"(a[0]), [k1] "v"(a[1]), [k2] "v"(a[2]), [k3] "v"(a[3]), [q0] "v"(q0), [q1] "v"(q1), [a0] "v"(a0),
+          [b0] "v"(b0), [a1] "v"(a1), [b1] "v"(b1)
+        : "memory");
+    }
+  }
+};
+
 
 // Tile layouts in LDS (elements, bf16):
 //  K: BN rows of D + 16 (two 16-byte pad slots per row). A 16-byte operand
@@ -192,16 +431,16 @@ template <int D> __device__ __forceinline__ int vswz(int row) {
   else return (row >> 1) & 1;
 }
 
-// Work group: 8 waves, two per SIMD, each owning 32 queries. K and V tiles
-// of 64 keys go through a 4-stage LDS ring in pairs: while tiles t and t+1
-// are computed, the DMA of tiles t+2 and t+3 is in flight, and one barrier
-// per pair publishes them (half the barriers of one per tile: 2.5% faster at
-// 32k). Per tile a wave runs
-//   S^T = K Q^T (16 MFMAs) -> mask (edge tiles) -> row max -> lazy rescale
-//   -> P = exp2(S - m), row sums, bf16 -> O^T += V^T P^T (16 MFMAs),
-// with the V^T fragments gathered before the softmax so they arrive while it
-// runs. The two waves of a SIMD come from the same work group but drift
-// apart within a tile, so one's softmax overlaps the other's MFMAs.
+// Work group: 8 waves, two per SIMD (waves w and w + 4), each owning 32
+// queries. Per tile a wave runs an MFMA phase (O^T += V^T P^T for the previous
+// tile, 16 MFMAs, then S^T = K Q^T for this tile, 16 MFMAs) and a softmax
+// phase (mask on edge tiles, one reference max for the tile's 64 keys, lazy
+// rescale, P = exp2(S - m) in bf16, row sums). Waves 0-3 run MFMA then
+// softmax in each tile period, waves 4-7 softmax then MFMA, so on every SIMD
+// one wave keeps the matrix core busy while the other runs its softmax. K and
+// V tiles of 64 keys go through a 4-stage LDS ring: the DMA of tile t+2 goes
+// out at the start of period t, and one barrier per period publishes tile
+// t+1.
 // MODE is the mask (0 intra, 1 causal over the expanded sequence, 2 causal
 // and windowed), fixed at compile time so that the masks and the position
 // arithmetic of the other modes fold away. LASTQ: the queries are the last
@@ -280,29 +519,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   // Wave w moves chunks w, w + 8, ... The byte offset of a chunk is a
   // tile-independent part (kept per chunk; padding slots carry the
   // out-of-range offset for good) plus a scalar tile base.
-  uint32_t coff[NCW];
-#pragma unroll
-  for (int j = 0; j < NCW; ++j) {
-    const int c = wave + j * kWaves;
+  auto chunk_off = [&](int c, int ln) {
     int row = 0, ch = 0;
     bool pad = false;
     if (c < TL::KI) {
-      const int sl = c * 64 + lane;
+      const int sl = c * 64 + ln;
       row = sl / TL::KSLOTS;
       ch = sl % TL::KSLOTS;
       pad = ch >= D / 8;
     } else {
-      const int sl = (c - TL::KI) * 64 + lane;
+      const int sl = (c - TL::KI) * 64 + ln;
       row = sl / TL::VSLOTS;
       const int u = sl % TL::VSLOTS;
       ch = (((u >> 2) ^ vswz<D>(row)) << 2) | (u & 3);
     }
-    coff[j] = pad ? kOobOffset : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
-  }
+    return pad ? kOobOffset : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
+  };
+  uint32_t coff[NCW];
+#pragma unroll
+  for (int j = 0; j < NCW; ++j) coff[j] = chunk_off(wave + j * kWaves, lane);
   auto issue_chunks = [&](int kt, int j0, int j1) {
     const int st = kt % ST;
     const uint32_t tbase = uint32_t(base_row + kt * BN * pstride) * kv_pos_bytes;
     const bool ragged = (kt + 1) * BN > p.Lv;   // last tile of a sequence: rows past the end read zeros
+    // the chunk offsets are recomputed here from an opaque copy of the lane
+    // index rather than held in registers through the tile loop
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const int c = wave + j * kWaves;
@@ -340,129 +581,185 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
-  // ---- prologue: tiles kt_begin and kt_begin + 1 in flight, wait for the first ----
+  // ---- prologue: tiles kt_begin and kt_begin + 1 in flight and landed ----
   issue_chunks(kt_begin, 0, NCW);
   if (kt_begin + 1 < kt_end) issue_chunks(kt_begin + 1, 0, NCW);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_barrier" ::: "memory");
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int st = kt % ST;
-    const bool first = ((kt - kt_begin) & 1) == 0;   // first tile of a pair
+  // The Q fragments' loads completed at the wait above, but the compiler does
+  // not read inline asm: passing them through an empty asm makes it place its
+  // own wait for them here, outside the tile loop, instead of before their
+  // uses inside it, where its count would also wait for the DMA in flight.
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) asm volatile("" : "+v"(qf[kk]));
+  const int T = kt_end - kt_begin;
+  const bool grp_b = wave >= kWaves / 2;   // waves w and w + 4 share a SIMD
+  const bool full_share = wave + (NCW - 1) * kWaves < NCH;   // this wave moves NCW chunks per tile (else NCW - 1)
+  auto live = [&](int kt) {
     const int k0 = kt * BN;
-    const bool live = wave_live && k0 <= diag(qhi) && !(window > 0 && diag(q0) - (k0 + BN - 1) >= window);
-    // the pair's first tile sends out the next pair: its stages held the
-    // previous pair, which every wave finished before the last barrier
-    if (first) {
-      if (kt + 2 < kt_end) issue_chunks(kt + 2, 0, NCW);
-      if (kt + 3 < kt_end) issue_chunks(kt + 3, 0, NCW);
+    return wave_live && k0 <= diag(qhi) && !(window > 0 && diag(q0) - (k0 + BN - 1) >= window);
+  };
+  f32x16 sacc[2];
+  bf16x8 pf[4];   // P of the last softmax, [32-key block * 2 + j2]
+
+  u32x2 xv[8];   // the first V^T chunk of the last scored tile, read ahead by its last score block
+  auto vaddr = [&](int stage, uint32_t (&ae)[DB], uint32_t (&ao)[DB]) {
+    const uint32_t vt = lds_addr(&vs[stage][0]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = (db ^ vsw) * 32;
+      ae[db] = vt + uint32_t(vbase_even + col) * 2;
+      ao[db] = vt + uint32_t(vbase_odd + col) * 2;
     }
-    if (live) {
-      // ---- S^T = K Q^T for two 32-key blocks ----
-      f32x16 sacc[2];
-      const u16* kr0 = &ks[st][krow0 * TL::KROW + 8 * hh];
-      bf16x8 ka[2][KD];
+  };
+  // MFMA phase i: O^T += V^T P^T for tile i-1 in chunks of (32-key block,
+  // pair of d blocks), then S^T = K Q^T for tile i in pairs of 16-wide d steps
+  auto mfma_phase = [&](int i) {
+    const bool do_pv = i >= 1 && live(kt_begin + i - 1);
+    const bool do_s = i < T && live(kt_begin + i);
+    const int sts = (kt_begin + i) % ST;
+    const uint32_t kbase = lds_addr(&ks[sts][krow0 * TL::KROW + 8 * hh]);
+    u32x4 y[4];
+    if (do_pv) {
+      uint32_t ae[DB], ao[DB];
+      vaddr((kt_begin + i - 1) % ST, ae, ao);
+      constexpr int NP = DB / 2;
+      auto chunk = [&](auto CC) {
+        constexpr int c = decltype(CC)::value;
+        constexpr int kb = c / NP, pr = c % NP;
+        bf16x8 t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) __builtin_memcpy(&t[j], &xv[2 * j], 16);
+        if constexpr (c + 1 < 2 * NP) {
+          constexpr int kbn = (c + 1) / NP, prn = (c + 1) % NP;
+          PpAsm<D>::template pv_mid<kbn>(oacc[2 * pr], oacc[2 * pr + 1], t, pf[2 * kb], pf[2 * kb + 1], ae[2 * prn],
+                                         ao[2 * prn], ae[2 * prn + 1], ao[2 * prn + 1], xv);
+        } else {
+          PpAsm<D>::pv_last(oacc[2 * pr], oacc[2 * pr + 1], t, pf[2 * kb], pf[2 * kb + 1], kbase, y);
+        }
+      };
+      chunk(std::integral_constant<int, 0>{});
+      chunk(std::integral_constant<int, 1>{});
+      if constexpr (D == 128) {
+        chunk(std::integral_constant<int, 2>{});
+        chunk(std::integral_constant<int, 3>{});
+      }
+    } else if (do_s) {
+      PpAsm<D>::k_first(kbase, y);
+    }
+    if (do_s) {
+      uint32_t ae[DB], ao[DB];
+      vaddr(sts, ae, ao);
+      auto step = [&](auto C) {
+        constexpr int c = decltype(C)::value;
+        bf16x8 a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) __builtin_memcpy(&a[j], &y[j], 16);
+        PpAsm<D>::template s_step<c>(sacc[0], sacc[1], a, qf[2 * c], qf[2 * c + 1], kbase, y, ae[0], ao[0], ae[1],
+                                     ao[1], xv);
+      };
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      if constexpr (D == 128) {
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+      }
+    }
+  };
+
+  // softmax phase i: mask, one reference max for the 64 keys of the tile
+  // (lazy rescale), P = exp2(S - m) in bf16, row sums
+  auto softmax_phase = [&](int i) {
+    const int kt = kt_begin + i;
+    if (!live(kt)) return;
+    const int k0 = kt * BN;
+    const bool full = (k0 + BN - 1 <= diag(q0)) && (window == 0 || diag(qhi) - k0 < window);
+    if (!full) {
+      const int vq = diag(q0 + l32);
+      const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) ka[kb][kk] = *reinterpret_cast<const bf16x8*>(kr0 + kb * 32 * TL::KROW + kk * 16);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][kk], qf[kk], sacc[kb], 0, 0, 0);
-      }
-      // ---- V^T fragments by transposed LDS reads, issued while the matrix
-      // cores still work on S^T (the mask below is the first use of it) ----
-      bf16x8 va[DB][2][2];
-      {
-        const uint32_t vt = lds_addr(&vs[st][0]);
-        uint32_t ae[DB], ao[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = ((db ^ vsw) - db) * 32 + db * 32;
-          ae[db] = vt + uint32_t(vbase_even + col) * 2;
-          ao[db] = vt + uint32_t(vbase_odd + col) * 2;
-        }
-        u32x2 x[D / 4];
-        gather_vt<D>(x, ae, ao);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j2 = 0; j2 < 2; ++j2) __builtin_memcpy(&va[db][kb][j2], &x[((db * 2 + kb) * 2 + j2) * 2], 16);
-      }
-
-      const bool full = (k0 + BN - 1 <= diag(q0)) && (window == 0 || diag(qhi) - k0 < window);
-      if (!full) {
-        const int vq = diag(q0 + l32);
-        const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = k0 + kb * 32 + reg_key_offset(g, hh) + r;
-              // 0 <= vq - key < lim, one unsigned compare (lim 2^31: causal only)
-              const bool ok = uint32_t(vq - key) < lim;
-              sacc[kb][4 * g + r] = ok ? sacc[kb][4 * g + r] : -INFINITY;
-            }
-      }
-
-      // ---- online softmax (base 2, lazy rescale) and O^T += V^T P^T, one
-      // 32-key block at a time: block 0's VALU work needs only sacc[0], so it
-      // runs while the matrix cores finish block 1's scores, and block 1's
-      // runs while they work on block 0's P V. A raised reference max
-      // rescales O (and l) before the block's P V. ----
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float mx = sacc[kb][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        const float cand = pair_max(mx) * p.c;
-        const bool need = cand > m + kRescaleLog2;
-        if (__any(need)) {
-          const float alpha = need ? __builtin_amdgcn_exp2f(m - cand) : 1.f;
-          m = need ? cand : m;
-          lsum *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        }
-        const float mu = m == -INFINITY ? 0.f : m;
-        bf16x8 pf[2];
-        float ls = 0.f;
-#pragma unroll
-        for (int j2 = 0; j2 < 2; ++j2) {
-          bf16x8 pv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j2 * 8 + i], p.c, -mu));
-            ls += e;
-            pv[i] = (__bf16)e;
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + kb * 32 + reg_key_offset(g, hh) + r;
+            const bool ok = uint32_t(vq - key) < lim;
+            sacc[kb][4 * g + r] = ok ? sacc[kb][4 * g + r] : -INFINITY;
           }
-          pf[j2] = pv;
-        }
-        lsum += ls;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb][j2], pf[j2], oacc[db], 0, 0, 0);
-      }
     }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[0][j]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[1][j]);
+    const float cand = pair_max(mx) * p.c;
+    const bool need = cand > m + kRescaleLog2;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - cand) : 1.f;
+      m = need ? cand : m;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float mu = m == -INFINITY ? 0.f : m;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        bf16x8 pv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j2 * 8 + j], p.c, -mu));
+          ls += e;
+          pv[j] = (__bf16)e;
+        }
+        pf[kb * 2 + j2] = pv;
+      }
+    lsum += ls;
+  };
 
-    if (!first && kt + 1 < kt_end) {
-      // the end of a pair: the next pair must have landed, then one barrier
-      // publishes it (a bare one: every LDS read of this pair has been
-      // consumed by an MFMA above, and there is no DMA left in flight)
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Period pp: group A (waves 0-3) runs the MFMA phase of tile pp then the
+  // softmax of tile pp; group B (waves 4-7) the softmax of tile pp-1 then the
+  // MFMA phase of tile pp. On each SIMD one wave multiplies while the other
+  // runs its softmax. The DMA of tile pp+2 goes out at the start of the
+  // period into the stage tile pp-2 held, which both groups finished reading
+  // in period pp-1.
+  auto period_end = [&](int pp) {
+    if (pp + 1 < T) {
+      // tile pp+1 must have landed; the chunks of tile pp+2 may still fly
+      if (pp + 2 < T) {
+        if (full_share) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCW - 1) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       asm volatile("s_barrier" ::: "memory");
     }
+  };
+  // one loop per group (the same barriers in both): a single loop with both
+  // orders would carry each group's state through the other's path
+  if (!grp_b) {
+#pragma nounroll
+    for (int pp = 0; pp <= T; ++pp) {
+      if (pp + 2 < T) issue_chunks(kt_begin + pp + 2, 0, NCW);
+      mfma_phase(pp);
+      if (pp < T) softmax_phase(pp);
+      period_end(pp);
+    }
+  } else {
+#pragma nounroll
+    for (int pp = 0; pp <= T; ++pp) {
+      if (pp + 2 < T) issue_chunks(kt_begin + pp + 2, 0, NCW);
+      if (pp >= 1) softmax_phase(pp - 1);
+      mfma_phase(pp);
+      period_end(pp);
+    }
   }
+  // the last P V MFMAs' results are read by the VALU below
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
 
   // ---- epilogue: O = O^T / l, bf16; optional natural-log LSE ----
   if (!wave_live) return;
