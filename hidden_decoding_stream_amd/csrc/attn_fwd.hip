@@ -542,8 +542,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
     const int st = kt % ST;
     const uint32_t tbase = uint32_t(base_row + kt * BN * pstride) * kv_pos_bytes;
     const bool ragged = (kt + 1) * BN > p.Lv;   // last tile of a sequence: rows past the end read zeros
-    // the chunk offsets are recomputed here from an opaque copy of the lane
-    // index rather than held in registers through the tile loop
+    // per chunk: its precomputed offset plus this tile's base; only the
+    // ragged last tile of a sequence needs a per-row check
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const int c = wave + j * kWaves;
