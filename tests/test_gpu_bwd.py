@@ -59,6 +59,9 @@ CASES = [
     (1, 130, 1, 2, 2, 64, "cross_full", 0),         # n = 1: ordinary causal attention
     (4, 1, 1, 4, 2, 64, "cross_full", 0),           # one token
     (2, 90, 1, 8, 8, 64, "cross_window", 1000),     # window >= S
+    (4, 33, 1, 16, 2, 64, "cross_full", 0),         # G = 8
+    (3, 50, 1, 6, 2, 128, "intra", 0),              # G = 3
+    (2, 65, 1, 12, 2, 128, "cross_window", 50),     # G = 6
 ]
 
 

@@ -38,6 +38,8 @@ SMALL = [
     (1, 6, 45, 50, 16, 2, 64, "cross_window", 40),       # 48 rows
     (1, 4, 60, 64, 64, 2, 128, "intra", 0),              # G = 32 under intra
     (1, 2, 60, 64, 64, 1, 64, "intra", 0),               # G = 64 under intra
+    (2, 4, 200, 210, 12, 4, 128, "cross_full", 0),       # G = 3: 12 rows
+    (1, 4, 150, 150, 6, 1, 64, "intra", 0),              # G = 6 under intra
 ]
 
 

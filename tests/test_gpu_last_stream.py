@@ -42,6 +42,8 @@ CASES = [
     (4, 1, 1, 4, 2, 64, "cross_full", 0),              # one token
     (2, 700, 1, 4, 1, 64, "cross_window", 1),          # self only
     (4, 129, 1, 8, 2, 128, "cross_window", 6),         # window shorter than a token's streams
+    (4, 77, 1, 6, 2, 128, "cross_full", 0),            # G = 3
+    (2, 129, 1, 12, 2, 64, "intra", 0),                # G = 6
 ]
 
 

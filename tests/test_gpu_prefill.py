@@ -56,6 +56,9 @@ CASES = [
     (4, 17, 1, 16, 2, 128, "cross_full", 0),          # G = 8: two head groups
     (4, 1, 1, 4, 2, 64, "cross_full", 0),              # one token
     (2, 700, 1, 4, 1, 64, "cross_window", 1),          # self only
+    (4, 77, 1, 6, 2, 128, "cross_full", 0),           # G = 3: one head per group, three groups
+    (2, 129, 1, 12, 2, 64, "cross_window", 100),       # G = 6: head groups of 2
+    (2, 70, 1, 32, 2, 128, "intra", 0),               # G = 16: two groups of 8 heads
 ]
 
 
