@@ -156,9 +156,7 @@ def main():
 
         a0, a1 = mark("ilv")
         if a0: a0.record(stream)
-        sfa.sf_interleave(qs, n, out=Q)
-        sfa.sf_interleave(ks, n, out=K)
-        sfa.sf_interleave(vs, n, out=V)
+        sfa.sf_interleave_multi([qs, ks, vs], n, outs=[Q, K, V])
         if a1: a1.record(stream)
         e0, e1 = mark("cross")
         if e0: e0.record(stream)
@@ -168,8 +166,7 @@ def main():
         if i0: i0.record(stream)
         sfa.sf_attn_fwd(Q, K, V, "intra", n, scale=scale, out=Oi)
         if i1: i1.record(stream)
-        sfa.sf_interleave(K, n, inverse=True, out=kc.view(n, B, L, hkv, d))
-        sfa.sf_interleave(V, n, inverse=True, out=vc.view(n, B, L, hkv, d))
+        sfa.sf_interleave_multi([K, V], n, inverse=True, outs=[kc.view(n, B, L, hkv, d), vc.view(n, B, L, hkv, d)])
         d0, d1 = mark("dec")
         if d0: d0.record(stream)
         sfa.sf_attn_decode(q_new, kc.view(B, n, L, hkv, d), vc.view(B, n, L, hkv, d), L, "cross_full",

@@ -18,6 +18,7 @@ from .sfattn import (  # noqa: F401
     sf_attn_fwd_last_stream,
     sf_expand_embed,
     sf_interleave,
+    sf_interleave_multi,
     sf_last_error,
     sf_rope,
 )

@@ -105,6 +105,42 @@ sf_status sf_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_
                        "sf_interleave launch");
 }
 
+sf_status sf_interleave_multi(const void* const* srcs, void* const* dsts, const int64_t* row_bytes, int32_t count,
+                              int32_t n, int64_t L, int64_t batch, int32_t inverse, hipStream_t stream) {
+  if (count < 1) return fail(SF_ERR_INVALID, "count must be >= 1 (got %d)", count);
+  if (count > sfa::kMaxInterleave)
+    return fail(SF_ERR_UNSUPPORTED, "at most %d tensors per call (got %d)", sfa::kMaxInterleave, count);
+  if (!srcs || !dsts || !row_bytes) return fail(SF_ERR_INVALID, "null srcs, dsts or row_bytes array");
+  if (n < 1) return fail(SF_ERR_INVALID, "n must be >= 1 (got %d)", n);
+  if (L < 0 || batch < 0) return fail(SF_ERR_INVALID, "L and batch must be >= 0");
+  if (inverse != 0 && inverse != 1) return fail(SF_ERR_INVALID, "inverse must be 0 or 1");
+  for (int t = 0; t < count; ++t)
+    if (row_bytes[t] < 1) return fail(SF_ERR_INVALID, "row_bytes[%d] must be >= 1", t);
+  if (L == 0 || batch == 0) return ok();
+  int64_t bytes[sfa::kMaxInterleave];
+  for (int t = 0; t < count; ++t) {
+    if (!srcs[t] || !dsts[t]) return fail(SF_ERR_INVALID, "null src or dst of tensor %d", t);
+    bytes[t] = row_bytes[t];
+    if (!mul_ok(bytes[t], n) || !mul_ok(bytes[t], L) || !mul_ok(bytes[t], batch))
+      return fail(SF_ERR_INVALID, "size of tensor %d overflows int64", t);
+  }
+  // every destination is disjoint from every source and from the other destinations
+  for (int t = 0; t < count; ++t)
+    for (int u = 0; u < count; ++u) {
+      if (overlaps(dsts[t], bytes[t], srcs[u], bytes[u]))
+        return fail(SF_ERR_INVALID, "dst of tensor %d overlaps src of tensor %d", t, u);
+      if (u != t && overlaps(dsts[t], bytes[t], dsts[u], bytes[u]))
+        return fail(SF_ERR_INVALID, "dsts of tensors %d and %d overlap", t, u);
+    }
+  const int vb = sfa::interleave_vector_bytes(srcs, dsts, row_bytes, count);
+  for (int t = 0; t < count; ++t)
+    if (uint64_t(bytes[t]) / uint64_t(vb) >= (uint64_t(1) << 32))
+      return fail(SF_ERR_UNSUPPORTED, "tensor %d: %lld bytes exceed 2^32 vectors of %d bytes", t,
+                  (long long)bytes[t], vb);
+  return device_status(sfa::launch_interleave_multi(srcs, dsts, row_bytes, count, n, L, batch, inverse, stream),
+                       "sf_interleave_multi launch");
+}
+
 sf_status sf_expand_embed(const int32_t* ids, const void* tables, void* out, int64_t batch, int32_t n, int64_t L,
                           int64_t vocab, int64_t row_bytes, hipStream_t stream) {
   if (n < 1) return fail(SF_ERR_INVALID, "n must be >= 1 (got %d)", n);

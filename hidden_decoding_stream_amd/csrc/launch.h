@@ -11,6 +11,14 @@ namespace sfa {
 
 hipError_t launch_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_t batch,
                              int64_t row_bytes, int inverse, hipStream_t stream);
+// Up to kMaxInterleave tensors of the same (n, L, batch) in one launch.
+constexpr int kMaxInterleave = 4;
+hipError_t launch_interleave_multi(const void* const* src, void* const* dst, const int64_t* row_bytes,
+                                   int32_t count, int32_t n, int64_t L, int64_t batch, int inverse,
+                                   hipStream_t stream);
+// Bytes per vector the launch above uses: the widest of 16, 8, 4, 2, 1 that
+// divides every pointer and row size.
+int interleave_vector_bytes(const void* const* src, void* const* dst, const int64_t* row_bytes, int32_t count);
 
 hipError_t launch_expand_embed(const int32_t* ids, const void* tables, void* out, int64_t batch, int32_t n,
                                int64_t L, int64_t vocab, int64_t row_bytes, int vb, hipStream_t stream);

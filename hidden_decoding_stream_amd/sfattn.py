@@ -49,6 +49,9 @@ def lib() -> ctypes.CDLL:
     L.sf_interleave.restype = c.c_int
     L.sf_interleave.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int64, c.c_int64, c.c_int64,
                                 c.c_int32, c.c_void_p]
+    L.sf_interleave_multi.restype = c.c_int
+    L.sf_interleave_multi.argtypes = [c.POINTER(c.c_void_p), c.POINTER(c.c_void_p), c.POINTER(c.c_int64),
+                                      c.c_int32, c.c_int32, c.c_int64, c.c_int64, c.c_int32, c.c_void_p]
     L.sf_attn_fwd.restype = c.c_int
     L.sf_attn_fwd.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                               c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_int32, c.c_int32,
@@ -124,10 +127,8 @@ def sf_last_error() -> str:
     return lib().sf_last_error().decode(errors="replace")
 
 
-def sf_interleave(src: torch.Tensor, n: int, inverse: bool = False, out: torch.Tensor | None = None,
-                  stream=None) -> torch.Tensor:
-    """Forward: src [n][B][L][...] -> [B][n*L][...]; inverse: [B][n*L][...] -> [n][B][L][...].
-    Any dtype; a bit-exact copy."""
+def _interleave_shape(src: torch.Tensor, n: int, inverse: bool):
+    """(B, L, output shape, row bytes) of an interleave of src."""
     if not inverse:
         if src.dim() < 3 or src.shape[0] != n:
             raise ValueError("forward interleave expects src of shape [n][B][L][...]")
@@ -139,14 +140,49 @@ def sf_interleave(src: torch.Tensor, n: int, inverse: bool = False, out: torch.T
         B, S = src.shape[:2]
         L = S // n
         out_shape = (n, B, L) + tuple(src.shape[2:])
-    if out is None:
-        out = torch.empty(out_shape, dtype=src.dtype, device=src.device)
-    elif tuple(out.shape) != out_shape or out.dtype != src.dtype:
-        raise ValueError(f"out must be {out_shape} {src.dtype}")
     row_bytes = src.element_size() * int(math.prod(out_shape[3:] if inverse else src.shape[3:]))
+    return B, L, out_shape, row_bytes
+
+
+def _interleave_out(src: torch.Tensor, out_shape, out: torch.Tensor | None) -> torch.Tensor:
+    if out is None:
+        return torch.empty(out_shape, dtype=src.dtype, device=src.device)
+    if tuple(out.shape) != tuple(out_shape) or out.dtype != src.dtype:
+        raise ValueError(f"out must be {tuple(out_shape)} {src.dtype}")
+    return out
+
+
+def sf_interleave(src: torch.Tensor, n: int, inverse: bool = False, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Forward: src [n][B][L][...] -> [B][n*L][...]; inverse: [B][n*L][...] -> [n][B][L][...].
+    Any dtype; a bit-exact copy."""
+    B, L, out_shape, row_bytes = _interleave_shape(src, n, inverse)
+    out = _interleave_out(src, out_shape, out)
     _check(lib().sf_interleave(_dev(src, "src"), _dev(out, "out"), n, L, B, row_bytes, int(inverse),
                                _stream(stream)))
     return out
+
+
+def sf_interleave_multi(srcs, n: int, inverse: bool = False, outs=None, stream=None) -> list:
+    """sf_interleave of 1 to 4 tensors with the same n, B and L (rows may
+    differ in size and dtype) in one launch; returns the outputs in order."""
+    srcs = list(srcs)
+    if not 1 <= len(srcs) <= 4:
+        raise ValueError("sf_interleave_multi takes 1 to 4 tensors")
+    outs = [None] * len(srcs) if outs is None else list(outs)
+    if len(outs) != len(srcs):
+        raise ValueError("outs must match srcs")
+    shapes = [_interleave_shape(x, n, inverse) for x in srcs]
+    if len({(B, L) for B, L, _, _ in shapes}) != 1:
+        raise ValueError("all tensors must share batch and L")
+    B, L = shapes[0][:2]
+    outs = [_interleave_out(x, sh[2], o) for x, sh, o in zip(srcs, shapes, outs)]
+    cnt = len(srcs)
+    src_p = (ctypes.c_void_p * cnt)(*[_dev(x, "src") for x in srcs])
+    dst_p = (ctypes.c_void_p * cnt)(*[_dev(o, "out") for o in outs])
+    rows = (ctypes.c_int64 * cnt)(*[sh[3] for sh in shapes])
+    _check(lib().sf_interleave_multi(src_p, dst_p, rows, cnt, n, L, B, int(inverse), _stream(stream)))
+    return outs
 
 
 def sf_expand_embed(ids: torch.Tensor, tables: torch.Tensor, out: torch.Tensor | None = None, stream=None):

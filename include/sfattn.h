@@ -86,6 +86,21 @@ const char* sf_last_error(void);
 sf_status sf_interleave(const void* src, void* dst, int32_t n, int64_t L, int64_t batch,
                         int64_t row_bytes, int32_t inverse, hipStream_t stream);
 
+/* sf_interleave of `count` tensors of the same n, L and batch in one launch,
+ * e.g. Q, K and V of the expansion above (rows of different sizes: hq and
+ * hkv heads), or K and V on their way into the per-stream cache. Tensor t is
+ * moved exactly as sf_interleave(srcs[t], dsts[t], n, L, batch,
+ * row_bytes[t], inverse) would move it; one launch saves the separate
+ * launches and ramps of the smaller tensors.
+ *   srcs, dsts, row_bytes : HOST arrays of `count` entries; the pointers in
+ *                           them are device pointers.
+ *   count : 1 .. 4 (SF_ERR_INVALID below 1, SF_ERR_UNSUPPORTED above 4).
+ * No destination may overlap any source or another destination
+ * (SF_ERR_INVALID). The vector width is the widest that divides every pointer
+ * and row size; each tensor must stay below 2^32 such vectors. */
+sf_status sf_interleave_multi(const void* const* srcs, void* const* dsts, const int64_t* row_bytes, int32_t count,
+                              int32_t n, int64_t L, int64_t batch, int32_t inverse, hipStream_t stream);
+
 /* Expansion of the input: with n copies of the vocabulary embedding, stream
  * k's representation of token i (row ids[b][i] of table k) is placed at
  * expanded position i*n + k ([HD-tahou] 隐式序列缩放的技术细节, step 1, there

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"sf_interleave", "sf_expand_embed", "sf_rope", "sf_attn_fwd", "sf_attn_fwd_last_stream",
+    assert {"sf_interleave", "sf_interleave_multi", "sf_expand_embed", "sf_rope", "sf_attn_fwd", "sf_attn_fwd_last_stream",
             "sf_attn_bwd", "sf_attn_bwd_workspace_bytes", "sf_attn_decode", "sf_attn_decode_workspace_bytes",
             "sf_attn_decode_paged", "sf_attn_decode_paged_workspace_bytes",
             "sf_abi_version", "sf_last_error"} <= set(names)
@@ -104,6 +104,43 @@ def test_interleave_rejects(kw, status):
 def test_interleave_empty_is_noop():
     assert ilv(Lt=0, src=None, dst=None) == B.SF_OK
     assert ilv(batch=0) == B.SF_OK
+
+
+def ilvm(srcs=(0x10000, 0x40000000, 0x80000000), dsts=(0x100000000, 0x140000000, 0x180000000),
+         rows=(256, 64, 64), count=None, n=4, Lt=16, batch=2, inverse=0, arrays=True):
+    c = len(srcs) if count is None else count
+    k = max(1, len(srcs))
+    sp = (ctypes.c_void_p * k)(*srcs) if arrays else None
+    dp = (ctypes.c_void_p * k)(*dsts) if arrays else None
+    rp = (ctypes.c_int64 * k)(*rows) if arrays else None
+    return L.sf_interleave_multi(sp, dp, rp, c, n, Lt, batch, inverse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(count=0), B.SF_ERR_INVALID),
+    (dict(srcs=(1 << 16,) * 5, dsts=tuple((i + 1) << 32 for i in range(5)), rows=(64,) * 5),
+     B.SF_ERR_UNSUPPORTED),                                               # more than 4 tensors
+    (dict(arrays=False), B.SF_ERR_INVALID),
+    (dict(n=0), B.SF_ERR_INVALID),
+    (dict(Lt=-1), B.SF_ERR_INVALID),
+    (dict(inverse=2), B.SF_ERR_INVALID),
+    (dict(rows=(256, 0, 64)), B.SF_ERR_INVALID),
+    (dict(srcs=(0x10000, 0, 0x80000000)), B.SF_ERR_INVALID),
+    (dict(dsts=(0x100000000, 0x40000000 + 64, 0x180000000)), B.SF_ERR_INVALID),   # dst 1 inside src 1
+    (dict(dsts=(0x100000000, 0x80000000 + 64, 0x180000000)), B.SF_ERR_INVALID),   # dst 1 inside src 2
+    (dict(dsts=(0x100000000, 0x100000000 + 64, 0x180000000)), B.SF_ERR_INVALID),  # two dsts overlap
+    (dict(rows=(256, 1 << 40, 64), Lt=1 << 30), B.SF_ERR_INVALID),                # overflow
+    (dict(rows=(256, 1 << 30, 64), Lt=1 << 4, n=64, batch=64,
+          dsts=(1 << 50, 1 << 51, 1 << 52)), B.SF_ERR_UNSUPPORTED),                # 2^32 vectors
+])
+def test_interleave_multi_rejects(kw, status):
+    assert ilvm(**kw) == status
+    assert sfa.sf_last_error() != ""
+
+
+def test_interleave_multi_empty_is_noop():
+    assert ilvm(Lt=0, srcs=(0, 0, 0), dsts=(0, 0, 0)) == B.SF_OK
+    assert ilvm(batch=0) == B.SF_OK
 
 
 def dec(q=P, kc=P2, vc=P3, o=P4, batch=1, n=4, T=16, Tmax=16, hq=32, hkv=8, d=128, mode=1, window=0,

@@ -76,3 +76,43 @@ def test_full_size_qkv(w):
     back = sfa.sf_interleave(sfa.sf_interleave(k, w.n), w.n, inverse=True)
     torch.cuda.synchronize()
     assert torch.equal(back, k)
+
+
+@pytest.mark.parametrize("n,L,B,rows", [
+    # (elements per row, dtype) of each tensor
+    (4, 37, 2, [(8 * 64, torch.bfloat16), (2 * 64, torch.bfloat16), (2 * 64, torch.bfloat16)]),  # Q, K, V
+    (3, 129, 1, [(7, torch.int16), (32, torch.bfloat16)]),        # 14-byte rows: 2-byte vectors for both
+    (2, 50, 3, [(3, torch.uint8), (5, torch.int32), (1, torch.int16), (16, torch.bfloat16)]),   # four tensors
+    (4, 1000, 1, [(1000, torch.bfloat16)]),                      # one tensor, many blocks
+])
+def test_multi_matches_single_and_oracle(n, L, B, rows):
+    """One launch over several tensors moves each exactly as sf_interleave
+    does, forward and back, with the vector width all of them allow."""
+    say("interleave multi", n, L, B, [r for r, _ in rows])
+    g = torch.Generator().manual_seed(11)
+    srcs = [torch.randint(-100, 100, (n, B, L, r), generator=g).to(dt) for r, dt in rows]
+    outs = sfa.sf_interleave_multi([x.cuda() for x in srcs], n)
+    torch.cuda.synchronize()
+    for x, y in zip(srcs, outs):
+        assert np.array_equal(_bits(y), orc.interleave(_bits(x)))
+        assert torch.equal(y, sfa.sf_interleave(x.cuda(), n))
+    backs = sfa.sf_interleave_multi(outs, n, inverse=True)
+    torch.cuda.synchronize()
+    for x, z in zip(srcs, backs):
+        assert np.array_equal(_bits(z), _bits(x))
+
+
+def test_multi_full_size_qkv():
+    """The 32k step's Q, K and V in one launch, and K, V back into the
+    per-stream layout in another: bitwise equal to one call per tensor."""
+    say("interleave multi full size")
+    w = I.CROSS_32K
+    qs, ks, vs = I.stream_qkv(w.n, w.L, w.batch, w.hq, w.hkv, w.d, seed=5, device="cuda")
+    Q, K, V = sfa.sf_interleave_multi([qs, ks, vs], w.n)
+    torch.cuda.synchronize()
+    assert torch.equal(Q, sfa.sf_interleave(qs, w.n))
+    assert torch.equal(K, sfa.sf_interleave(ks, w.n))
+    assert torch.equal(V, sfa.sf_interleave(vs, w.n))
+    kc, vc = sfa.sf_interleave_multi([K, V], w.n, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, ks) and torch.equal(vc, vs)
