@@ -96,3 +96,63 @@ def test_two_streams_at_once():
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o)
     assert torch.equal(od, ref_d)
+
+
+def test_graph_replay_whole_step():
+    """The whole hot path as one captured graph: Q, K, V interleaved in one
+    launch, cross_full and intra prefill, K and V de-interleaved in one launch
+    into the per-stream cache, and the decode of the last token's n streams
+    from it. Every replay on refilled inputs equals the eager step bit for
+    bit."""
+    n, L, B, hq, hkv, d = 4, 200, 1, 8, 2, 128
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(12)
+    qs = torch.empty((n, B, L, hq, d), dtype=torch.bfloat16, device=dev)
+    ks = torch.empty((n, B, L, hkv, d), dtype=torch.bfloat16, device=dev)
+    vs = torch.empty_like(ks)
+    Q = torch.empty((B, n * L, hq, d), dtype=torch.bfloat16, device=dev)
+    K = torch.empty((B, n * L, hkv, d), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    Oc, Oi = torch.empty_like(Q), torch.empty_like(Q)
+    kc = torch.empty((n, B, L, hkv, d), dtype=torch.bfloat16, device=dev)   # == [B][n][L][hkv][d] at B = 1
+    vc = torch.empty_like(kc)
+    q_new = torch.empty((B, n, hq, d), dtype=torch.bfloat16, device=dev)
+    od = torch.empty_like(q_new)
+    ws = torch.zeros(sfa.sf_attn_decode_workspace_bytes(B, n, L, hq, hkv, d, "cross_full") + 16,
+                     dtype=torch.uint8, device=dev)
+    s = _scale(d)
+
+    def refill():
+        for t in (qs, ks, vs):
+            _fill(t, g)
+
+    def step():
+        sfa.sf_interleave_multi([qs, ks, vs], n, outs=[Q, K, V])
+        sfa.sf_attn_fwd(Q, K, V, "cross_full", n, scale=s, out=Oc)
+        sfa.sf_attn_fwd(Q, K, V, "intra", n, scale=s, out=Oi)
+        sfa.sf_interleave_multi([K, V], n, inverse=True, outs=[kc, vc])
+        q_new.copy_(qs[:, 0, L - 1].unsqueeze(0))
+        sfa.sf_attn_decode(q_new, kc.view(B, n, L, hkv, d), vc.view(B, n, L, hkv, d), L, "cross_full",
+                           scale=s, out=od, workspace=ws)
+
+    refill()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    outs = (Q, K, V, Oc, Oi, kc, vc, od)
+    for replay in range(3):
+        say("whole-step graph replay", replay)
+        refill()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        step()
+        torch.cuda.synchronize()
+        for a, b in zip(got, outs):
+            assert torch.equal(a, b), replay
+        assert torch.equal(kc, ks) and torch.equal(vc, vs)
