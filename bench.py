@@ -14,9 +14,11 @@ One step is one pass of the whole hot path over the 32k workload
 The reported value is the useful attention throughput of the step: the flops of
 the admitted (query, key) pairs of steps 2, 3 and 5 divided by the step time.
 The line also carries the roofline of the dominant kernel (the cross_full
-prefill, timed with HIP events around its own launches), a decode bandwidth
-sweep (batch 1, 8, 64; intra and cross_full) and the CPU oracle timed on a
-bounded sample of the same workload.
+prefill, timed with HIP events around its own launches, with the hardware
+MFMA-busy share from the committed counter summary), every prefill workload
+timed on its own (tiny, intra 16k, cross_window 16k, cross_full and intra
+32k), a decode bandwidth sweep (batch 1, 8, 64; intra and cross_full) and the
+CPU oracle timed on a bounded sample of the same workload.
 
 Inputs are synthetic (seeded N(0,1), rounded to bf16) and resident in HBM
 before timing starts. Only one GPU is used.
@@ -38,7 +40,11 @@ METRIC = "SF-attention useful TFLOP/s + MFMA% at n=4 nL=32k; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 PROFILE_PMC = ROOT / "profiles" / "attn_fwd_cross_full_32k_pmc.txt"
+PROFILE_MFMA = ROOT / "profiles" / "attn_fwd_prefill_mfma_busy.txt"
 FWD_SOURCE = ROOT / "hidden_decoding_stream_amd" / "csrc" / "attn_fwd.hip"
+# launches per workload in --profile-prefill (counter runs read them in this order)
+PROFILE_PREFILL_ORDER = ("intra_16k", "cross_window_16k", "cross_full_32k", "intra_32k")
+PROFILE_PREFILL_REPS = 3
 
 
 def parse_args():
@@ -54,11 +60,32 @@ def parse_args():
     ap.add_argument("--profile-decode", action="store_true",
                     help="only run decode calls for counter runs (batch 1 and 8, cross_full and intra, "
                          "3 calls each on distinct caches), then exit")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="only run the four full-size prefill workloads for counter runs "
+                         f"({', '.join(PROFILE_PREFILL_ORDER)}; {PROFILE_PREFILL_REPS} launches each, "
+                         "in that order), then exit")
     return ap.parse_args()
 
 
 def source_sha(path: pathlib.Path) -> str:
     return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+
+
+def stored_mfma_busy():
+    """Hardware MFMA-busy share per prefill workload (SQ_VALU_MFMA_BUSY_CYCLES
+    over GRBM_GUI_ACTIVE x 1024 SIMDs), from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else {}."""
+    if not PROFILE_MFMA.exists():
+        return {}
+    text = PROFILE_MFMA.read_text()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m_sha or m_sha.group(1) != source_sha(FWD_SOURCE):
+        return {}
+    out = {}
+    for name, busy, clk in re.findall(r"^mfma_busy\[(\w+)\]:\s*([0-9.]+)\s+effective_clock_ghz:\s*([0-9.]+)",
+                                      text, flags=re.M):
+        out[name] = {"mfma_busy": float(busy), "clock_ghz": float(clk)}
+    return out
 
 
 def stored_traffic():
@@ -117,6 +144,20 @@ def main():
                 print(json.dumps({"profile_decode": mode, "batch": batch, "calls": 3}), flush=True)
                 del caches
                 torch.cuda.empty_cache()
+        return
+
+    if args.profile_prefill:
+        by_name = {x.name: x for x in I.PREFILL_WORKLOADS}
+        for name in PROFILE_PREFILL_ORDER:
+            wp = by_name[name]
+            q, k, v = I.workload_qkv(wp, device=dev)
+            o = torch.empty_like(q)
+            for _ in range(PROFILE_PREFILL_REPS):
+                sfa.sf_attn_fwd(q, k, v, wp.mode, wp.n, window=wp.window, scale=wp.scale, out=o)
+            torch.cuda.synchronize()
+            print(json.dumps({"profile_prefill": name, "launches": PROFILE_PREFILL_REPS}), flush=True)
+            del q, k, v, o
+            torch.cuda.empty_cache()
         return
 
     w = I.CROSS_32K
@@ -190,6 +231,7 @@ def main():
     cross_ms, intra_ms, ilv_ms, dec_ms = avg_ms("cross"), avg_ms("intra"), avg_ms("ilv"), avg_ms("dec")
     achieved = flops_cross / (cross_ms * 1e-3) / 1e12
     traffic = stored_traffic()
+    hw = stored_mfma_busy()
     print(f"[bench] step {ms_per_step:.3f} ms; cross_full {cross_ms:.3f} ms ({achieved:.1f} TFLOP/s), "
           f"intra {intra_ms:.3f} ms, interleave x3 {ilv_ms:.3f} ms, decode {dec_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
@@ -225,6 +267,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
+            "mfma_busy": (hw.get("cross_full_32k") or {}).get("mfma_busy"),
+            "clock_ghz": (hw.get("cross_full_32k") or {}).get("clock_ghz"),
             "useful_flop_per_launch": flops_cross,
             "avg_launch_ms": round(cross_ms, 4),
         },
@@ -238,6 +282,8 @@ def main():
         "decode_vs_prefill_max_abs": dev_err,
     }
 
+    line["prefill"] = prefill_configs(torch, sfa, C, I, dev, stream, hw,
+                                      {"cross_full_32k": cross_ms, "intra_32k": intra_ms})
     line["last_stream"] = last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream)
     line["front_end"] = front_end_timing(torch, sfa, C, n, L, B, hq, d, dev, stream)
     line["backward"] = backward_timing(torch, sfa, C, Q, K, V, Oc, n, L, B, hq, hkv, d, scale, dev, stream)
@@ -248,6 +294,51 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, C, I, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def prefill_configs(torch, sfa, C, I, dev, stream, hw, step_ms, reps=10):
+    """Every prefill workload on its own: the tiny problem (intra and
+    cross_full, attention on the bf16 rounding of its fp32 draws), intra 16k
+    (batch 2), cross_window 16k (batch 2, W = 4096 positions) and the 32k
+    cross_full and intra passes (their times are the step's own launches).
+    Useful TFLOP/s counts admitted pairs only; `frac` is of 2.5 PFLOP/s dense
+    bf16; `mfma_busy` and `clock_ghz` come from the committed counter summary
+    (null unless it was taken on the current kernel source)."""
+    out = {}
+    for w in I.PREFILL_WORKLOADS:
+        fl = C.prefill_flops(w.mode, w.n, w.L, w.batch, w.hq, w.d, w.window)
+        if w.name in step_ms:
+            ms = step_ms[w.name]
+        else:
+            q, k, v = I.workload_qkv(w, device=dev)
+            if q.dtype != torch.bfloat16:
+                q, k, v = (I.to_bf16(x) for x in (q, k, v))
+            o = torch.empty_like(q)
+            call = lambda: sfa.sf_attn_fwd(q, k, v, w.mode, w.n, window=w.window, scale=w.scale,  # noqa: E731
+                                           out=o)
+            for _ in range(2):
+                call()
+            pairs = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                pairs.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in pairs) / reps
+            del q, k, v, o
+        tf = fl / (ms * 1e-3) / 1e12
+        rec = {"mode": w.mode, "n": w.n, "L": w.L, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "d": w.d,
+               "window": w.window, "ms": round(ms, 4), "useful_flop": fl, "tflops": round(tf, 2),
+               "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        h = hw.get(w.name) or {}
+        rec["mfma_busy"] = h.get("mfma_busy")
+        rec["clock_ghz"] = h.get("clock_ghz")
+        out[w.name] = rec
+        print(f"[bench] prefill {w.name}: {ms:.4f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    return out
 
 
 def attainable_peaks(line):
@@ -481,20 +572,34 @@ def serving_sweep(torch, sfa, C, I, dev, budget=16 << 30):
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(torch, C, I, qs, ks, vs, target_s):
     """The fp64 oracle, as it stands, on evenly spaced query rows of the same
-    32k cross_full workload (all heads). Scaled to useful TFLOP/s with the
-    same pair count the GPU figure uses."""
+    32k cross_full workload (all heads). The rows are split into blocks that
+    a pool of one worker thread per core of this process's affinity mask (at
+    most its OMP_NUM_THREADS share) computes, each with one BLAS thread (NumPy
+    releases the interpreter lock inside its matrix products, exponentials and
+    comparisons). Scaled to useful TFLOP/s with the same pair count the GPU
+    figure uses."""
+    import concurrent.futures
+
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle.sfa as orc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
     w = I.CROSS_32K
     n, L, S = w.n, w.L, w.S
+    # the process's affinity mask, at most its OMP_NUM_THREADS share (16 on a one-GPU box)
+    cores = max(1, min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS") or 16)))
     # the oracle reads the expanded layout; build it on the CPU by its own interleave
     q = orc.interleave(qs.to("cpu", torch.float64).numpy())
     k = orc.interleave(ks.to("cpu", torch.float64).numpy())
@@ -502,23 +607,32 @@ def cpu_baseline(torch, C, I, qs, ks, vs, target_s):
 
     def run(nrows):
         rows = np.unique(np.linspace(0, S - 1, nrows).astype(np.int64))
+        parts = [r for r in np.array_split(rows, 4 * cores) if len(r)]
         t = time.perf_counter()
-        orc.attn_fwd(q, k, v, "cross_full", n, scale=w.scale, rows=rows)
+        with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(cores) as ex:
+            list(ex.map(lambda r: orc.attn_fwd(q, k, v, "cross_full", n, scale=w.scale, rows=r), parts))
         dt = time.perf_counter() - t
         pairs = int(np.sum(rows + 1))          # causal: row p admits p+1 keys
         return rows, dt, 4 * w.d * pairs * w.batch * w.hq
 
-    rows, dt, fl = run(64)
-    nrows = int(min(S, max(64, 64 * target_s / max(dt, 1e-3))))
-    rows, dt, fl = run(nrows)
+    rows, dt, fl = run(16 * cores)
+    for _ in range(2):     # the time is not quite linear in the rows: calibrate twice
+        if dt >= 0.6 * target_s or len(rows) >= S:
+            break
+        rows, dt, fl = run(int(min(S, len(rows) * target_s / max(dt, 1e-3))))
+    blas = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                     if p.get("user_api") == "blas") or "unknown"
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{len(rows)} evenly spaced query rows of the cross_full 32k workload, all {w.hq} heads, "
-                  f"fp64 NumPy, {dt:.1f} s",
+                  f"fp64 NumPy, {cores} worker threads with one BLAS thread each, {dt:.1f} s",
         "seconds": round(dt, 2),
+        "cpu_model": _cpu_model(),
+        "numpy": np.__version__,
+        "blas": blas,
     }
 
 

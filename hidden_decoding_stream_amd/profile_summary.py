@@ -1,0 +1,129 @@
+"""Summaries of rocprofv3 counter runs of the library's kernels (measurement
+tooling; not used by the library itself).
+
+    python -m hidden_decoding_stream_amd.profile_summary prefill DIR [DIR ...]
+
+Each DIR holds the CSV output of one `rocprofv3 --pmc ... --kernel-trace
+--output-format csv` run of `bench.py --profile-prefill`, which launches the
+four full-size prefill workloads three times each, in a fixed order. The
+attn_fwd_kernel dispatches are assigned to the workloads in dispatch order.
+For each workload it prints the counters averaged over its launches and what
+follows from them:
+
+  mfma_busy        SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs):
+                   the share of SIMD cycles the matrix core was busy
+  effective clock  GRBM_GUI_ACTIVE / kernel duration
+  cu_busy          SQ_BUSY_CU_CYCLES x 4 / (GRBM_GUI_ACTIVE x 256 CUs): the
+                   share of CU cycles with a wave resident (1 - ramp and tail)
+  executed flops   SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, against the useful
+                   (admitted-pair) flops
+  valu_busy        SQ_ACTIVE_INST_VALU x 4 / (GRBM_GUI_ACTIVE x 1024): VALU
+                   issue cycles per SIMD cycle (the counter is per wave, in
+                   quad-cycles)
+  coexec           SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES: the
+                   share of MFMA-busy cycles in which a VALU op also issued
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import pathlib
+import sys
+
+from . import counts as C
+from . import inputs as I
+
+PKG = pathlib.Path(__file__).resolve().parent
+ORDER = ("intra_16k", "cross_window_16k", "cross_full_32k", "intra_32k")
+REPS = 3
+SIMDS = 1024
+CUS = 256
+
+
+def _sha16(path: pathlib.Path) -> str:
+    return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+
+
+def _read_dir(d: pathlib.Path):
+    """{dispatch id: {"name", "ns", counters...}} from one run's CSV files."""
+    rows = {}
+    for f in sorted(d.rglob("*counter_collection.csv")):
+        for r in csv.DictReader(open(f)):
+            did = int(r["Dispatch_Id"])
+            rec = rows.setdefault(did, {"name": r["Kernel_Name"]})
+            rec[r["Counter_Name"]] = rec.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                rec["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    for f in sorted(d.rglob("*kernel_trace.csv")):
+        for r in csv.DictReader(open(f)):
+            did = int(r["Dispatch_Id"])
+            if did in rows:
+                rows[did]["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return rows
+
+
+def prefill(dirs) -> str:
+    by_name = {w.name: w for w in I.PREFILL_WORKLOADS}
+    per = {name: {} for name in ORDER}
+    counters_seen = []
+    for d in dirs:
+        rows = _read_dir(pathlib.Path(d))
+        fwd = [rows[k] for k in sorted(rows) if rows[k]["name"].startswith("attn_fwd_kernel")]
+        if len(fwd) != len(ORDER) * REPS:
+            raise SystemExit(f"{d}: expected {len(ORDER) * REPS} attn_fwd_kernel dispatches, found {len(fwd)}")
+        for i, name in enumerate(ORDER):
+            for rec in fwd[i * REPS:(i + 1) * REPS]:
+                for key, val in rec.items():
+                    if key == "name":
+                        per[name]["kernel"] = val
+                        continue
+                    per[name].setdefault(key, []).append(val)
+        for key in fwd[0]:
+            if key not in ("name", "ns") and key not in counters_seen:
+                counters_seen.append(key)
+    out = []
+    sha = _sha16(PKG / "csrc" / "attn_fwd.hip")
+    for name in ORDER:
+        w = by_name[name]
+        rec = per[name]
+        avg = {k: sum(v) / len(v) for k, v in rec.items() if k != "kernel"}
+        useful = C.prefill_flops(w.mode, w.n, w.L, w.batch, w.hq, w.d, w.window)
+        out.append(f"{name}: {rec['kernel']}  (n={w.n} L={w.L} batch={w.batch} hq={w.hq} hkv={w.hkv} d={w.d}"
+                   f"{' W=' + str(w.window) if w.window else ''})")
+        ns = avg.get("ns")
+        gui = avg.get("GRBM_GUI_ACTIVE")
+        if ns:
+            out.append(f"  duration under counters, mean of {REPS}: {ns / 1e3:.1f} us "
+                       f"({useful / ns / 1e3:.1f} useful TFLOP/s)")
+        for key in counters_seen:
+            if key in avg:
+                out.append(f"  {key}: {avg[key]:.6g}")
+        if gui:
+            clk = gui / ns if ns else float("nan")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                busy = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS)
+                out.append(f"mfma_busy[{name}]: {busy:.2f} effective_clock_ghz: {clk:.3f}")
+            if "SQ_BUSY_CU_CYCLES" in avg:
+                out.append(f"  cu_busy: {100.0 * 4 * avg['SQ_BUSY_CU_CYCLES'] / (gui * CUS):.2f} %")
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                out.append(f"  valu_busy: {100.0 * 4 * avg['SQ_ACTIVE_INST_VALU'] / (gui * SIMDS):.2f} %")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+            ex = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            out.append(f"  executed bf16 MFMA flops: {ex:.4e} (useful {useful:.4e}, useful/executed "
+                       f"{useful / ex:.4f})")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            out.append(f"  coexec: {100.0 * avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.2f} "
+                       "% of MFMA-busy cycles")
+        out.append("")
+    out.append(f"kernel_source_sha256_16: {sha}")
+    return "\n".join(out)
+
+
+def main(argv):
+    if len(argv) < 2 or argv[0] != "prefill":
+        raise SystemExit(__doc__)
+    print(prefill(argv[1:]))
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -119,6 +119,16 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _expect(t: torch.Tensor, name: str, shape, device: torch.device) -> None:
+    """A caller-supplied tensor must have exactly the shape the call writes or
+    reads, on the same device as the call's inputs: the library sees only raw
+    pointers, so a short tensor would be read or written out of bounds."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def sf_abi_version() -> int:
     return int(lib().sf_abi_version())
 
@@ -147,8 +157,9 @@ def _interleave_shape(src: torch.Tensor, n: int, inverse: bool):
 def _interleave_out(src: torch.Tensor, out_shape, out: torch.Tensor | None) -> torch.Tensor:
     if out is None:
         return torch.empty(out_shape, dtype=src.dtype, device=src.device)
-    if tuple(out.shape) != tuple(out_shape) or out.dtype != src.dtype:
-        raise ValueError(f"out must be {tuple(out_shape)} {src.dtype}")
+    if out.dtype != src.dtype:
+        raise ValueError(f"out must be {src.dtype}")
+    _expect(out, "out", out_shape, src.device)
     return out
 
 
@@ -196,8 +207,11 @@ def sf_expand_embed(ids: torch.Tensor, tables: torch.Tensor, out: torch.Tensor |
     row = tables[0, 0].numel() * tables.element_size()
     if out is None:
         out = torch.empty((B, n * L) + tuple(tables.shape[2:]), dtype=tables.dtype, device=tables.device)
-    if out.numel() * out.element_size() != B * n * L * row:
-        raise ValueError("out has the wrong size")
+    if ids.device != tables.device:
+        raise ValueError("ids and tables must be on the same device")
+    if out.dtype != tables.dtype:
+        raise ValueError(f"out must be {tables.dtype}")
+    _expect(out, "out", (B, n * L) + tuple(tables.shape[2:]), tables.device)
     _check(lib().sf_expand_embed(_dev(ids, "ids"), _dev(tables, "tables"), _dev(out, "out"), B, n, L, vocab, row,
                                  _stream(stream)))
     return out
@@ -222,13 +236,18 @@ def sf_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode, n: int,
         raise ValueError("sequence length must be a multiple of n")
     if k.shape != (B, S, hkv, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B][S][hkv][d] matching q")
+    _expect(k, "k", (B, S, hkv, d), q.device)
+    _expect(v, "v", (B, S, hkv, d), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
         lse = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _expect(lse, "lse", (B, hq, S), q.device)
     lse_ptr = _dev(lse, "lse", torch.float32) if want_lse else None
     bf = torch.bfloat16
     _check(lib().sf_attn_fwd(_dev(q, "q", bf), _dev(k, "k", bf), _dev(v, "v", bf), _dev(out, "out", bf),
@@ -247,13 +266,18 @@ def sf_attn_fwd_last_stream(q_last: torch.Tensor, k: torch.Tensor, v: torch.Tens
     hkv = k.shape[2]
     if k.shape != (B, n * L, hkv, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B][n*L][hkv][d] matching q_last")
+    _expect(k, "k", (B, n * L, hkv, d), q_last.device)
+    _expect(v, "v", (B, n * L, hkv, d), q_last.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q_last)
+    _expect(out, "out", q_last.shape, q_last.device)
     want_lse = lse is not None and lse is not False
     if lse is True:
         lse = torch.empty((B, hq, L), dtype=torch.float32, device=q_last.device)
+    if want_lse:
+        _expect(lse, "lse", (B, hq, L), q_last.device)
     lse_ptr = _dev(lse, "lse", torch.float32) if want_lse else None
     bf = torch.bfloat16
     _check(lib().sf_attn_fwd_last_stream(_dev(q_last, "q_last", bf), _dev(k, "k", bf), _dev(v, "v", bf),
@@ -272,12 +296,23 @@ def sf_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     hkv = k.shape[2]
     if S % n:
         raise ValueError("sequence length must be a multiple of n")
+    dev = q.device
+    for t, name in ((k, "k"), (v, "v")):
+        _expect(t, name, (B, S, hkv, d), dev)
+    for t, name in ((o, "o"), (dout, "dout")):
+        _expect(t, name, (B, S, hq, d), dev)
+    _expect(lse, "lse", (B, hq, S), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    _expect(dq, "dq", (B, S, hq, d), dev)
+    _expect(dk, "dk", (B, S, hkv, d), dev)
+    _expect(dv, "dv", (B, S, hkv, d), dev)
     need = int(lib().sf_attn_bwd_workspace_bytes(B, n, S // n, hq, hkv, d, _mode(mode), int(window)))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev:
+        raise ValueError(f"workspace must be on {dev}")
     bf = torch.bfloat16
     _check(lib().sf_attn_bwd(_dev(q, "q", bf), _dev(k, "k", bf), _dev(v, "v", bf), _dev(o, "o", bf),
                              _dev(dout, "dout", bf), _dev(lse, "lse", torch.float32), _dev(dq, "dq", bf),
@@ -303,13 +338,19 @@ def sf_attn_decode(q_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     T_max, hkv = k_cache.shape[2], k_cache.shape[3]
     if k_cache.shape != (B, n, T_max, hkv, d) or v_cache.shape != k_cache.shape:
         raise ValueError("caches must be [B][n][T_max][hkv][d] matching q_new")
+    dev = q_new.device
+    _expect(k_cache, "k_cache", (B, n, T_max, hkv, d), dev)
+    _expect(v_cache, "v_cache", (B, n, T_max, hkv, d), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q_new)
+    _expect(out, "out", q_new.shape, dev)
     need = sf_attn_decode_workspace_bytes(B, n, T, hq, hkv, d, mode, window, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_new.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev:
+        raise ValueError(f"workspace must be on {dev}")
     bf = torch.bfloat16
     _check(lib().sf_attn_decode(_dev(q_new, "q_new", bf), _dev(k_cache, "k_cache", bf),
                                 _dev(v_cache, "v_cache", bf), _dev(out, "out", bf), B, n, int(T), T_max,
@@ -344,15 +385,23 @@ def sf_attn_decode_paged(q_new: torch.Tensor, k_pages: torch.Tensor, v_pages: to
     if seq_lens.shape != (B,):
         raise ValueError("seq_lens must be [B]")
     max_pages = block_table.shape[2]
+    dev = q_new.device
+    for t, name in ((k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                    (seq_lens, "seq_lens")):
+        if t.device != dev:
+            raise ValueError(f"{name} must be on {dev}")
     if max_T is None:
         max_T = max_pages * page
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q_new)
+    _expect(out, "out", q_new.shape, dev)
     need = sf_attn_decode_paged_workspace_bytes(B, n, max_T, hq, hkv, d, mode, window, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_new.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev:
+        raise ValueError(f"workspace must be on {dev}")
     bf, i32 = torch.bfloat16, torch.int32
     _check(lib().sf_attn_decode_paged(
         _dev(q_new, "q_new", bf), _dev(k_pages, "k_pages", bf), _dev(v_pages, "v_pages", bf),

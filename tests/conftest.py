@@ -13,3 +13,13 @@ if HERE not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libsfattn")
+    # The boundary tests need libsfattn.so. Build it when it is absent (hipcc
+    # cross-compiles without a GPU); a failed build is reported by the tests
+    # that load the library, as failures.
+    from hidden_decoding_stream_amd import sfattn
+    if not sfattn.LIB_PATH.exists() and not hasattr(config, "workerinput"):
+        try:
+            from hidden_decoding_stream_amd import build
+            build.build()
+        except Exception as e:  # noqa: BLE001
+            print(f"[conftest] building libsfattn.so failed: {e}", file=sys.stderr)

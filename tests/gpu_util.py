@@ -1,10 +1,13 @@
 """Helpers shared by the GPU parity tests (comparison, sampling, probes)."""
 from __future__ import annotations
 
+import concurrent.futures
+import os
 import sys
 
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import oracle.sfa as orc
 
@@ -65,3 +68,51 @@ def oracle_mask_cols(mode, n, L, window, rows, cols, block=1024):
         sub[r0:r0 + block] = M[:, cols]
         cnt[r0:r0 + block] = M.sum(axis=1)
     return sub, cnt
+
+
+def cpu_share() -> int:
+    """Worker threads for oracle runs: the cores of this process's affinity
+    mask, at most its OMP_NUM_THREADS share (16 on a one-GPU machine)."""
+    cap = int(os.environ.get("OMP_NUM_THREADS") or 16)
+    return max(1, min(len(os.sched_getaffinity(0)), cap))
+
+
+def pooled(fn, items, blas_threads: int = 1):
+    """fn over items on cpu_share() threads, each with `blas_threads` BLAS
+    threads (NumPy releases the interpreter lock in its array work)."""
+    with threadpool_limits(blas_threads), concurrent.futures.ThreadPoolExecutor(cpu_share()) as ex:
+        return list(ex.map(fn, items))
+
+
+def oracle_fwd_head(q, k, v, mode, n, window, scale, rows=None, block=512):
+    """The oracle's attention of one head over all (or the given) query rows:
+    q [S][D], k, v [S][D] (float64). Row blocks go to a thread pool; each
+    block is one plain call of the oracle. Returns (o [R][D], lse [R])."""
+    S = q.shape[0]
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    q4, k4, v4 = q[None, :, None], k[None, :, None], v[None, :, None]
+    parts = [rows[i:i + block] for i in range(0, len(rows), block)]
+    res = pooled(lambda r: orc.attn_fwd(q4, k4, v4, mode, n, window=window, scale=scale, rows=r, with_lse=True),
+                 parts)
+    o = np.concatenate([x[0][0, :, 0] for x in res])
+    lse = np.concatenate([x[1][0, 0] for x in res])
+    return o, lse
+
+
+def assert_close_rows(got, ref, what, rel_max=2e-2, rel_mean=2e-3):
+    """Gradient comparison normalised per row: each row r (last axis = d)
+    must have max |err| <= rel_max * max(1, max_d |ref[r]|), and the mean of
+    |err| / max(1, max_d |ref[r]|) over every element must be <= rel_mean.
+    A gradient's size grows with the number of queries (or keys) that reach
+    it, so a bar scaled by the whole tensor's largest row would be loose for
+    every small row."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    norm = np.maximum(1.0, np.abs(ref).max(axis=-1, keepdims=True))
+    rel = np.abs(got - ref) / norm
+    mx, mn = float(rel.max()), float(rel.mean())
+    say(f"{what}: max|err|/rownorm {mx:.3e} mean {mn:.3e} (largest row norm {float(norm.max()):.3e})")
+    assert mx <= rel_max, f"{what}: max row-normalised error {mx} > {rel_max}"
+    assert mn <= rel_mean, f"{what}: mean row-normalised error {mn} > {rel_mean}"

@@ -3,7 +3,8 @@ token (expanded position i*n + n-1) against every stream's keys.
 
 Small problems are compared on every output element with the fp64 oracle;
 masks are probed bit-exactly (zero keys, one-hot values) at full size; the
-full-size workloads are compared on sampled tokens; and the result equals
+full-size workloads are compared on every token of two heads that read
+different kv heads and on sampled tokens of every head; and the result equals
 rows i*n + n-1 of sf_attn_fwd on the same K and V (GPU against GPU).
 """
 import math
@@ -15,7 +16,7 @@ import torch
 import hidden_decoding_stream_amd as sfa
 import hidden_decoding_stream_amd.inputs as I
 import oracle.sfa as orc
-from gpu_util import assert_close, np64, oracle_mask_cols, probe_values, sample_rows, say
+from gpu_util import assert_close, np64, oracle_fwd_head, oracle_mask_cols, probe_values, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -103,12 +104,23 @@ def test_mask_probe_full_size(w):
 
 
 @pytest.mark.parametrize("w", [I.CROSS_32K, I.INTRA_32K, I.WINDOW_16K], ids=lambda w: w.name)
-def test_full_size_sampled_tokens(w):
+def test_full_size(w):
     say("last stream full size", w.name)
     q, k, v = I.workload_qkv(w, device="cuda")
     n = w.n
     ql = _last_rows(q, n)
     o, lse = sfa.sf_attn_fwd_last_stream(ql, k, v, w.mode, n, window=w.window, scale=w.scale, lse=True)
+    # every token of two heads on different kv heads
+    G = w.hq // w.hkv
+    all_rows = np.arange(w.L) * n + (n - 1)
+    for b, h in ((0, 0), (w.batch - 1, w.hq - 1)):
+        kh = h // G
+        say(f"{w.name}: all {w.L} last-stream rows of batch {b} head {h} (kv head {kh})")
+        ref, ref_lse = oracle_fwd_head(np64(q[b, :, h]), np64(k[b, :, kh]), np64(v[b, :, kh]), w.mode, n,
+                                       w.window or None, w.scale, rows=all_rows)
+        assert_close(np64(o[b, :, h]), ref, f"{w.name} b{b} h{h} all tokens")
+        assert np.abs(np64(lse[b, h]) - ref_lse).max() < 1e-3
+    # sampled tokens of every head
     toks = sample_rows(w.L, seed=w.seed, window=w.window // n if w.window else 0)
     rows = toks * n + (n - 1)
     ref, ref_lse = orc.attn_fwd(np64(q), np64(k), np64(v), w.mode, n, window=w.window or None, scale=w.scale,

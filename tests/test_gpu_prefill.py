@@ -2,9 +2,10 @@
 
 Small problems are compared on every output element (several key tiles, ragged
 tails, all three masks, GQA and MHA, d = 64 and 128). The full-size workloads
-run in the exact launch configuration the benchmark times and are compared on
-sampled query rows (all heads, all batch elements), which the oracle computes
-one by one. Masks are checked bit-exactly with probes: constant keys make the
+run in the exact launch configuration the benchmark times. Each is compared on
+every row of two query heads that read different kv heads (the first head of
+the first batch element and the last head of the last), and on sampled query
+rows of every head and batch element. Masks are checked bit-exactly with probes: constant keys make the
 softmax uniform over the allowed set, one-hot values then read out, per query
 row, which probe keys were admitted (exactly) and the lse gives the count.
 """
@@ -17,7 +18,7 @@ import torch
 import hidden_decoding_stream_amd as sfa
 import hidden_decoding_stream_amd.inputs as I
 import oracle.sfa as orc
-from gpu_util import assert_close, np64, oracle_mask_cols, probe_values, sample_rows, say
+from gpu_util import assert_close, np64, oracle_fwd_head, oracle_mask_cols, probe_values, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -131,10 +132,20 @@ def test_mask_probe_full_size(w):
 
 
 @pytest.mark.parametrize("w", [I.INTRA_16K, I.WINDOW_16K, I.CROSS_32K, I.INTRA_32K], ids=lambda w: w.name)
-def test_full_size_sampled_rows(w):
+def test_full_size(w):
     say("prefill full size", w.name)
     q, k, v = I.workload_qkv(w, device="cuda")
     o, lse = _run(q, k, v, w.mode, w.n, window=w.window, lse=True)
+    # every row of two heads on different kv heads (and both batch elements when B = 2)
+    G = w.hq // w.hkv
+    for b, h in ((0, 0), (w.batch - 1, w.hq - 1)):
+        kh = h // G
+        say(f"{w.name}: all {w.S} rows of batch {b} head {h} (kv head {kh})")
+        ref, ref_lse = oracle_fwd_head(np64(q[b, :, h]), np64(k[b, :, kh]), np64(v[b, :, kh]), w.mode, w.n,
+                                       w.window or None, w.scale)
+        assert_close(np64(o[b, :, h]), ref, f"{w.name} b{b} h{h} all rows")
+        assert np.abs(np64(lse[b, h]) - ref_lse).max() < 1e-3
+    # sampled rows of every head and batch element
     rows = sample_rows(w.S, seed=w.seed, window=w.window)
     ref, ref_lse = orc.attn_fwd(np64(q), np64(k), np64(v), w.mode, w.n,
                                 window=w.window or None, scale=w.scale, rows=rows, with_lse=True)
