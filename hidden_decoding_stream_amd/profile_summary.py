@@ -68,7 +68,7 @@ def prefill(dirs) -> str:
     counters_seen = []
     for d in dirs:
         rows = _read_dir(pathlib.Path(d))
-        fwd = [rows[k] for k in sorted(rows) if rows[k]["name"].startswith("attn_fwd_kernel")]
+        fwd = [rows[k] for k in sorted(rows) if "attn_fwd_kernel<" in rows[k]["name"]]
         if len(fwd) != len(ORDER) * REPS:
             raise SystemExit(f"{d}: expected {len(ORDER) * REPS} attn_fwd_kernel dispatches, found {len(fwd)}")
         for i, name in enumerate(ORDER):
