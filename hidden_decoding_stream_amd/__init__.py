@@ -11,6 +11,7 @@ from .sfattn import (  # noqa: F401
     sf_abi_version,
     sf_attn_bwd,
     sf_attn_decode,
+    sf_attn_decode_noalloc,
     sf_attn_decode_paged,
     sf_attn_decode_paged_workspace_bytes,
     sf_attn_decode_workspace_bytes,

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/sfattn.h"
@@ -72,6 +73,70 @@ sf_status check_heads(int32_t n, int32_t hq, int32_t hkv, int32_t d, int32_t mod
   if (!std::isfinite(scale)) return fail(SF_ERR_INVALID, "scale must be finite");
   if (!(scale > 0.0f)) return fail(SF_ERR_UNSUPPORTED, "scale must be > 0 (got %g)", double(scale));
   if (d != 64 && d != 128) return fail(SF_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  return SF_OK;
+}
+
+// Validation shared by sf_attn_decode and sf_attn_decode_noalloc: everything
+// but the workspace. On SF_OK with batch > 0, `plan` holds the launch plan.
+sf_status check_decode(const void* q_new, const void* k_cache, const void* v_cache, const void* o_new,
+                       int64_t batch, int32_t n, int64_t T, int64_t T_max, int32_t hq, int32_t hkv, int32_t d,
+                       int32_t mode, int64_t window, float scale, int32_t num_splits, sfa::DecodePlan& plan) {
+  if (batch < 0) return fail(SF_ERR_INVALID, "batch must be >= 0");
+  if (T < 1) return fail(SF_ERR_INVALID, "T must be >= 1 (got %lld)", (long long)T);
+  if (T_max < T) return fail(SF_ERR_INVALID, "T (%lld) exceeds T_max (%lld)", (long long)T, (long long)T_max);
+  if (num_splits < 0) return fail(SF_ERR_INVALID, "num_splits must be >= 0");
+  sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
+  if (st != SF_OK) return st;
+  const int32_t G = hq / hkv;
+  if (mode == SF_INTRA ? G > 64 : int64_t(n) * G > 64)
+    return fail(SF_ERR_UNSUPPORTED, "%s decode supports at most 64 query rows per kv head (n=%d, G=%d)",
+                mode_name(mode), n, G);
+  if (batch == 0) return ok();
+  if (!q_new || !k_cache || !v_cache || !o_new) return fail(SF_ERR_INVALID, "null q_new, cache or o_new");
+  int64_t ce = batch, qe = batch;
+  if (!mul_ok(ce, n) || !mul_ok(ce, T_max) || !mul_ok(ce, hkv) || !mul_ok(ce, d) || !mul_ok(qe, n) ||
+      !mul_ok(qe, hq) || !mul_ok(qe, d))
+    return fail(SF_ERR_INVALID, "tensor size overflows int64");
+  if (!aligned(q_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o_new, 16))
+    return fail(SF_ERR_UNSUPPORTED, "q_new, caches and o_new must be 16-byte aligned");
+  if (overlaps(o_new, qe * 2, q_new, qe * 2) || overlaps(o_new, qe * 2, k_cache, ce * 2) ||
+      overlaps(o_new, qe * 2, v_cache, ce * 2))
+    return fail(SF_ERR_INVALID, "o_new overlaps an input");
+  if (ce > (int64_t(1) << 40) || T_max * hkv * d * 2 > INT32_MAX)
+    return fail(SF_ERR_UNSUPPORTED, "cache too large (T_max * hkv * d * 2 = %lld bytes per stream, at most 2^31 - 1)",
+                (long long)(T_max * hkv * d * 2));
+  plan = sfa::plan_decode(batch, n, T, hq, hkv, d, mode, window, num_splits);
+  if (plan.units > 65535)
+    return fail(SF_ERR_UNSUPPORTED, "decode supports at most 65535 key ranges (batch*hkv%s = %lld)",
+                mode == SF_INTRA ? "*n" : "", (long long)plan.units);
+  return SF_OK;
+}
+
+// Decode scratch of sf_attn_decode_noalloc: one fixed array in device memory
+// per GPU, held until the process ends. Host code never uses the array's name
+// as an address (on the host it names a stand-in, not device memory): the
+// device address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and kept in `g_scratch`.
+__device__ __align__(256) unsigned char scratch[SF_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+sf_status decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SF_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return device_status(e == hipSuccess ? hipErrorInvalidSymbol : e,
+                                                      "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
   return SF_OK;
 }
 
@@ -303,34 +368,11 @@ sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_c
                          int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,
                          int32_t num_splits, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-  if (batch < 0) return fail(SF_ERR_INVALID, "batch must be >= 0");
-  if (T < 1) return fail(SF_ERR_INVALID, "T must be >= 1 (got %lld)", (long long)T);
-  if (T_max < T) return fail(SF_ERR_INVALID, "T (%lld) exceeds T_max (%lld)", (long long)T, (long long)T_max);
-  if (num_splits < 0) return fail(SF_ERR_INVALID, "num_splits must be >= 0");
-  sf_status st = check_heads(n, hq, hkv, d, mode, window, scale);
-  if (st != SF_OK) return st;
-  const int32_t G = hq / hkv;
-  if (mode == SF_INTRA ? G > 64 : int64_t(n) * G > 64)
-    return fail(SF_ERR_UNSUPPORTED, "%s decode supports at most 64 query rows per kv head (n=%d, G=%d)",
-                mode_name(mode), n, G);
-  if (batch == 0) return ok();
-  if (!q_new || !k_cache || !v_cache || !o_new) return fail(SF_ERR_INVALID, "null q_new, cache or o_new");
-  int64_t ce = batch, qe = batch;
-  if (!mul_ok(ce, n) || !mul_ok(ce, T_max) || !mul_ok(ce, hkv) || !mul_ok(ce, d) || !mul_ok(qe, n) ||
-      !mul_ok(qe, hq) || !mul_ok(qe, d))
-    return fail(SF_ERR_INVALID, "tensor size overflows int64");
-  if (!aligned(q_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o_new, 16))
-    return fail(SF_ERR_UNSUPPORTED, "q_new, caches and o_new must be 16-byte aligned");
-  if (overlaps(o_new, qe * 2, q_new, qe * 2) || overlaps(o_new, qe * 2, k_cache, ce * 2) ||
-      overlaps(o_new, qe * 2, v_cache, ce * 2))
-    return fail(SF_ERR_INVALID, "o_new overlaps an input");
-  if (ce > (int64_t(1) << 40) || T_max * hkv * d * 2 > INT32_MAX)
-    return fail(SF_ERR_UNSUPPORTED, "cache too large (T_max * hkv * d * 2 = %lld bytes per stream, at most 2^31 - 1)",
-                (long long)(T_max * hkv * d * 2));
-  const sfa::DecodePlan plan = sfa::plan_decode(batch, n, T, hq, hkv, d, mode, window, num_splits);
-  if (plan.units > 65535)
-    return fail(SF_ERR_UNSUPPORTED, "decode supports at most 65535 key ranges (batch*hkv%s = %lld)",
-                mode == SF_INTRA ? "*n" : "", (long long)plan.units);
+  sfa::DecodePlan plan;
+  sf_status st = check_decode(q_new, k_cache, v_cache, o_new, batch, n, T, T_max, hq, hkv, d, mode, window, scale,
+                              num_splits, plan);
+  if (st != SF_OK || batch == 0) return st;
+  const int64_t ce = batch * n * T_max * hkv * d, qe = batch * n * hq * d;
   if ((plan.ws_bytes > 0 && !workspace) || workspace_bytes < plan.ws_bytes)
     return fail(SF_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
                 plan.ws_bytes);
@@ -344,6 +386,29 @@ sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_c
   sfa::DecodeArgs a{q_new, k_cache, v_cache, o_new, batch, n, T, T_max, hq, hkv, d, mode,
                     window, scale, num_splits, workspace};
   return device_status(sfa::launch_attn_decode(a, plan, stream), "sf_attn_decode launch");
+}
+
+sf_status sf_attn_decode_noalloc(const void* q_new, const void* k_cache, const void* v_cache, void* o_new,
+                                 int64_t batch, int32_t n, int64_t T, int64_t T_max, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,
+                                 int32_t num_splits, hipStream_t stream) {
+  sfa::DecodePlan plan;
+  sf_status st = check_decode(q_new, k_cache, v_cache, o_new, batch, n, T, T_max, hq, hkv, d, mode, window, scale,
+                              num_splits, plan);
+  if (st != SF_OK || batch == 0) return st;
+  if (plan.ws_bytes > SF_DECODE_SCRATCH_BYTES)
+    return fail(SF_ERR_UNSUPPORTED,
+                "this decode needs %zu bytes of scratch; sf_attn_decode_noalloc holds %zu (use fewer splits, "
+                "or sf_attn_decode with a workspace)",
+                plan.ws_bytes, size_t(SF_DECODE_SCRATCH_BYTES));
+  void* scratch = nullptr;
+  if (plan.ws_bytes > 0) {
+    st = decode_scratch(&scratch);
+    if (st != SF_OK) return st;
+  }
+  sfa::DecodeArgs a{q_new, k_cache, v_cache, o_new, batch, n, T, T_max, hq, hkv, d, mode,
+                    window, scale, num_splits, scratch};
+  return device_status(sfa::launch_attn_decode(a, plan, stream), "sf_attn_decode_noalloc launch");
 }
 
 size_t sf_attn_decode_paged_workspace_bytes(int64_t batch, int32_t n, int64_t max_T, int32_t hq,

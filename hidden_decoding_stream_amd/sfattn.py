@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
                                  c.c_int64, c.c_int32, c.c_int64, c.c_int64, c.c_int32, c.c_int32,
                                  c.c_int32, c.c_int32, c.c_int64, c.c_float, c.c_int32,
                                  c.c_void_p, c.c_size_t, c.c_void_p]
+    L.sf_attn_decode_noalloc.restype = c.c_int
+    L.sf_attn_decode_noalloc.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                         c.c_int64, c.c_int32, c.c_int64, c.c_int64, c.c_int32, c.c_int32,
+                                         c.c_int32, c.c_int32, c.c_int64, c.c_float, c.c_int32, c.c_void_p]
     L.sf_attn_decode_paged_workspace_bytes.restype = c.c_size_t
     L.sf_attn_decode_paged_workspace_bytes.argtypes = L.sf_attn_decode_workspace_bytes.argtypes
     L.sf_attn_decode_paged.restype = c.c_int
@@ -357,6 +361,32 @@ def sf_attn_decode(q_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                 hq, hkv, d, _mode(mode), int(window), float(scale), int(num_splits),
                                 _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
+    return out
+
+
+def sf_attn_decode_noalloc(q_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, T: int, mode,
+                           window: int = 0, scale: float | None = None, num_splits: int = 0,
+                           out: torch.Tensor | None = None, stream=None):
+    """sf_attn_decode with the library's fixed per-GPU scratch instead of a
+    workspace: it allocates nothing when `out` is given. Calls that overlap in
+    time on one GPU race on that scratch."""
+    B, n, hq, d = q_new.shape
+    T_max, hkv = k_cache.shape[2], k_cache.shape[3]
+    if k_cache.shape != (B, n, T_max, hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B][n][T_max][hkv][d] matching q_new")
+    dev = q_new.device
+    _expect(k_cache, "k_cache", (B, n, T_max, hkv, d), dev)
+    _expect(v_cache, "v_cache", (B, n, T_max, hkv, d), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q_new)
+    _expect(out, "out", q_new.shape, dev)
+    bf = torch.bfloat16
+    _check(lib().sf_attn_decode_noalloc(_dev(q_new, "q_new", bf), _dev(k_cache, "k_cache", bf),
+                                        _dev(v_cache, "v_cache", bf), _dev(out, "out", bf), B, n, int(T), T_max,
+                                        hq, hkv, d, _mode(mode), int(window), float(scale), int(num_splits),
+                                        _stream(stream)))
     return out
 
 

@@ -19,7 +19,9 @@
  *     step 1).
  *   - Tensor pointers are DEVICE pointers owned by the caller. The library
  *     never allocates or frees device memory; decode scratch space is passed in
- *     by the caller (see sf_attn_decode_workspace_bytes).
+ *     by the caller (see sf_attn_decode_workspace_bytes), except for
+ *     sf_attn_decode_noalloc, whose scratch is a fixed array in the library's
+ *     own device memory.
  *   - Calls enqueue work on `stream` (0 = the null stream) and return without
  *     synchronising. Results are valid once the stream has been synchronised.
  *   - Arguments are validated on the host before any HIP call. A rejected call
@@ -28,7 +30,9 @@
  *     supported set). A failed launch returns SF_ERR_DEVICE. In every non-OK
  *     case sf_last_error() describes the problem.
  *   - Calls are re-entrant: the only mutable state is the thread-local error
- *     string. Calls that write the same output buffer concurrently race.
+ *     string (and, for sf_attn_decode_noalloc, the per-GPU scratch array and
+ *     the table of its addresses). Calls that write the same output buffer
+ *     concurrently race.
  *   - Empty problems (batch == 0 or L == 0) are valid no-ops.
  */
 #ifndef SFATTN_H
@@ -225,6 +229,29 @@ sf_status sf_attn_decode(const void* q_new, const void* k_cache, const void* v_c
                          int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,
                          int32_t num_splits, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Bytes of decode scratch that sf_attn_decode_noalloc holds per GPU. */
+#define SF_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* sf_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It computes exactly what sf_attn_decode
+ * computes (same kernels and split plan, bitwise equal results), with the
+ * split partials in a fixed device array of SF_DECODE_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends. It calls no
+ * hipMalloc, hipFree or other allocating routine.
+ *   Arguments, supported set and errors as for sf_attn_decode, and
+ *   SF_ERR_UNSUPPORTED when the plan's workspace
+ *   (sf_attn_decode_workspace_bytes with the same arguments) exceeds
+ *   SF_DECODE_SCRATCH_BYTES. Every plan with num_splits = 0 fits; a large
+ *   explicit num_splits may not.
+ *   Every call on one GPU shares that GPU's array, and nothing in it needs
+ *   to start at zero. Calls that overlap in time on one GPU (for example on
+ *   two streams) race on the array and must not be issued. */
+sf_status sf_attn_decode_noalloc(const void* q_new, const void* k_cache, const void* v_cache, void* o_new,
+                                 int64_t batch, int32_t n, int64_t T, int64_t T_max, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t mode, int64_t window, float scale,
+                                 int32_t num_splits, hipStream_t stream);
 
 /* Bytes of device workspace sf_attn_decode_paged needs (0 if the arguments
  * are invalid or the problem is empty); max_T and num_splits as there. */

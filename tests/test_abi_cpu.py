@@ -171,6 +171,31 @@ def test_decode_empty_batch_is_noop():
     assert dec(batch=0) == B.SF_OK
 
 
+def dec_noalloc(q=P, kc=P2, vc=P3, o=P4, batch=1, n=4, T=16, Tmax=16, hq=32, hkv=8, d=128, mode=1, window=0,
+                scale=0.088, splits=0):
+    return L.sf_attn_decode_noalloc(q, kc, vc, o, batch, n, T, Tmax, hq, hkv, d, mode, window, scale, splits, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), B.SF_ERR_INVALID),
+    (dict(T=17), B.SF_ERR_INVALID),
+    (dict(splits=-1), B.SF_ERR_INVALID),
+    (dict(n=17), B.SF_ERR_UNSUPPORTED),
+    (dict(q=None), B.SF_ERR_INVALID),
+    (dict(o=P), B.SF_ERR_INVALID),                     # output overlaps q
+    # 1024 splits of 4 x 8192 positions at batch 4: 68 MB of partials, beyond the 16 MiB scratch
+    (dict(batch=4, T=8192, Tmax=8192, splits=1024), B.SF_ERR_UNSUPPORTED),
+])
+def test_decode_noalloc_rejects(kw, status):
+    assert dec_noalloc(**kw) == status
+
+
+def test_decode_noalloc_names_the_scratch_limit():
+    assert dec_noalloc(batch=4, T=8192, Tmax=8192, splits=1024) == B.SF_ERR_UNSUPPORTED
+    assert "scratch" in sfa.sf_last_error()
+    assert dec_noalloc(batch=0) == B.SF_OK
+
+
 def test_workspace_query():
     ws = sfa.sf_attn_decode_workspace_bytes(1, 4, 8192, 32, 8, 128, "cross_full")
     assert ws > 0 and ws % 256 == 0
