@@ -8,20 +8,27 @@ Each DIR holds the CSV output of one `rocprofv3 --pmc ... --kernel-trace
 four full-size prefill workloads three times each, in a fixed order. The
 attn_fwd_kernel dispatches are assigned to the workloads in dispatch order.
 For each workload it prints the counters averaged over its launches and what
-follows from them:
+follows from them. GRBM_GUI_ACTIVE is reported summed over the chip's 8 XCDs
+(one instance each, counting that XCD's active cycles), so one XCD's active
+cycles are the sum / 8:
 
-  mfma_busy        SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs):
-                   the share of SIMD cycles the matrix core was busy
-  effective clock  GRBM_GUI_ACTIVE / kernel duration
-  cu_busy          SQ_BUSY_CU_CYCLES x 4 / (GRBM_GUI_ACTIVE x 256 CUs): the
-                   share of CU cycles with a wave resident (1 - ramp and tail)
+  mfma_busy        SQ_VALU_MFMA_BUSY_CYCLES / (GUI_ACTIVE/8 x 1024 SIMDs): the
+                   share of SIMD cycles the matrix core was busy
+  effective clock  (GUI_ACTIVE/8) / kernel duration
+  cu_busy          SQ_BUSY_CU_CYCLES / (GUI_ACTIVE/8 x 256 CUs): the share of
+                   CU cycles with a wave resident, 1 - (ramp + tail + gaps
+                   between work groups). The counter is read as cycles: read
+                   as quad-cycles, as its description has it, it would exceed
+                   100% on every kernel here.
   executed flops   SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, against the useful
                    (admitted-pair) flops
-  valu_busy        SQ_ACTIVE_INST_VALU x 4 / (GRBM_GUI_ACTIVE x 1024): VALU
+  valu_busy        SQ_ACTIVE_INST_VALU x 4 / (GUI_ACTIVE/8 x 1024): VALU
                    issue cycles per SIMD cycle (the counter is per wave, in
                    quad-cycles)
   coexec           SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES: the
                    share of MFMA-busy cycles in which a VALU op also issued
+  lds_*            LDS counters per CU cycle (SQ_LDS_IDX_ACTIVE: LDS busy;
+                   SQ_LDS_BANK_CONFLICT: cycles stalled by bank conflicts)
 """
 from __future__ import annotations
 
@@ -38,6 +45,7 @@ ORDER = ("intra_16k", "cross_window_16k", "cross_full_32k", "intra_32k")
 REPS = 3
 SIMDS = 1024
 CUS = 256
+XCDS = 8
 
 
 def _sha16(path: pathlib.Path) -> str:
@@ -99,14 +107,18 @@ def prefill(dirs) -> str:
             if key in avg:
                 out.append(f"  {key}: {avg[key]:.6g}")
         if gui:
-            clk = gui / ns if ns else float("nan")
+            gx = gui / XCDS
+            clk = gx / ns if ns else float("nan")
             if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
-                busy = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS)
+                busy = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gx * SIMDS)
                 out.append(f"mfma_busy[{name}]: {busy:.2f} effective_clock_ghz: {clk:.3f}")
             if "SQ_BUSY_CU_CYCLES" in avg:
-                out.append(f"  cu_busy: {100.0 * 4 * avg['SQ_BUSY_CU_CYCLES'] / (gui * CUS):.2f} %")
+                out.append(f"  cu_busy: {100.0 * avg['SQ_BUSY_CU_CYCLES'] / (gx * CUS):.2f} %")
             if "SQ_ACTIVE_INST_VALU" in avg:
-                out.append(f"  valu_busy: {100.0 * 4 * avg['SQ_ACTIVE_INST_VALU'] / (gui * SIMDS):.2f} %")
+                out.append(f"  valu_busy: {100.0 * 4 * avg['SQ_ACTIVE_INST_VALU'] / (gx * SIMDS):.2f} %")
+            for key, label in (("SQ_LDS_IDX_ACTIVE", "lds_busy"), ("SQ_LDS_BANK_CONFLICT", "lds_bank_conflict")):
+                if key in avg:
+                    out.append(f"  {label}: {100.0 * avg[key] / (gx * CUS):.2f} % of CU cycles")
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
             ex = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
             out.append(f"  executed bf16 MFMA flops: {ex:.4e} (useful {useful:.4e}, useful/executed "
