@@ -58,8 +58,9 @@ def parse_args():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters), then exit")
     ap.add_argument("--profile-decode", action="store_true",
-                    help="only run decode calls for counter runs (batch 1 and 8, cross_full and intra, "
-                         "3 calls each on distinct caches), then exit")
+                    help="only run decode calls for trace and counter runs (batch 1 and 8, cross_full and "
+                         "intra, 3 calls each on distinct caches; then 24 plain reads of the batch-1 "
+                         "cache's bytes on the decode's 256-group grid), then exit")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="only run the four full-size prefill workloads for counter runs "
                          f"({', '.join(PROFILE_PREFILL_ORDER)}; {PROFILE_PREFILL_REPS} launches each, "
@@ -144,6 +145,19 @@ def main():
                 print(json.dumps({"profile_decode": mode, "batch": batch, "calls": 3}), flush=True)
                 del caches
                 torch.cuda.empty_cache()
+        # the floor for the batch-1 stream: one plain read of the same 134,217,728 bytes on the same
+        # 256-group grid, from 8 distinct buffers (1 GiB, beyond the Infinity Cache), 3 rounds
+        import hidden_decoding_stream_amd.peaks as P
+        nbytes = 2 * 4 * 8192 * 8 * 128 * 2
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(8)]
+        sink = torch.empty(256, dtype=torch.int32, device=dev)
+        st = torch.cuda.current_stream().cuda_stream
+        for _ in range(3):
+            for b in bufs:
+                if P.lib().sfp_read(b.data_ptr(), nbytes, sink.data_ptr(), 256, st) != 0:
+                    raise RuntimeError("sfp_read launch failed")
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_read": nbytes, "blocks": 256, "launches": 24}), flush=True)
         return
 
     if args.profile_prefill:

@@ -2,6 +2,7 @@
 tooling; not used by the library itself).
 
     python -m hidden_decoding_stream_amd.profile_summary prefill DIR [DIR ...]
+    python -m hidden_decoding_stream_amd.profile_summary decode DIR
 
 Each DIR holds the CSV output of one `rocprofv3 --pmc ... --kernel-trace
 --output-format csv` run of `bench.py --profile-prefill`, which launches the
@@ -131,10 +132,53 @@ def prefill(dirs) -> str:
     return "\n".join(out)
 
 
+def decode(d) -> str:
+    """The kernel trace of `bench.py --profile-decode`: every dispatch of the
+    library's decode kernels and of the plain read, in order, with its
+    duration and the idle gap since the previous dispatch ended; then per
+    call (split kernel start to combine kernel end, or the split kernel
+    alone) and per kernel averages."""
+    rows = []
+    for f in sorted(pathlib.Path(d).rglob("*kernel_trace.csv")):
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"]
+            short = ("split" if "decode_split_kernel" in name else "combine" if "decode_combine_kernel" in name
+                     else "read" if "read_kernel" in name else None)
+            if short:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short, name,
+                             r.get("Grid_Size") or r.get("Grid_Size_X") or ""))
+    rows.sort()
+    out = ["dispatch  kernel   grid      us     gap_before_us"]
+    prev_end = None
+    calls = []
+    for i, (st, en, short, name, grid) in enumerate(rows):
+        gap = (st - prev_end) / 1e3 if prev_end is not None else float("nan")
+        out.append(f"{i:8d}  {short:7s}  {grid:>8s}  {(en - st) / 1e3:7.2f}  {gap:7.2f}")
+        if short == "split":
+            calls.append([st, en, en - st, 0, 0.0])
+        elif short == "combine" and calls:
+            calls[-1][1] = en
+            calls[-1][3] = en - st
+            calls[-1][4] = gap
+        prev_end = en
+    out.append("")
+    out.append("per call: split us, combine us, gap split->combine us, call span us")
+    for c in calls:
+        out.append(f"  {c[2] / 1e3:7.2f}  {c[3] / 1e3:7.2f}  {c[4]:7.2f}  {(c[1] - c[0]) / 1e3:7.2f}")
+    reads = [(en - st) / 1e3 for st, en, short, _, _ in rows if short == "read"]
+    if reads:
+        out.append(f"plain read of the same bytes, 256 groups: mean {sum(reads) / len(reads):.2f} us, "
+                   f"min {min(reads):.2f} us over {len(reads)} launches")
+    return "\n".join(out)
+
+
 def main(argv):
-    if len(argv) < 2 or argv[0] != "prefill":
+    if len(argv) >= 2 and argv[0] == "prefill":
+        print(prefill(argv[1:]))
+    elif len(argv) == 2 and argv[0] == "decode":
+        print(decode(argv[1]))
+    else:
         raise SystemExit(__doc__)
-    print(prefill(argv[1:]))
 
 
 if __name__ == "__main__":
