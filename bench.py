@@ -26,6 +26,7 @@ before timing starts. Only one GPU is used.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -39,8 +40,7 @@ ROOT = pathlib.Path(__file__).resolve().parent
 METRIC = "SF-attention useful TFLOP/s + MFMA% at n=4 nL=32k; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-PROFILE_PMC = ROOT / "profiles" / "attn_fwd_cross_full_32k_pmc.txt"
-PROFILE_MFMA = ROOT / "profiles" / "attn_fwd_prefill_mfma_busy.txt"
+PROFILE_COUNTERS = ROOT / "profiles" / "attn_fwd_prefill_counters.txt"
 FWD_SOURCE = ROOT / "hidden_decoding_stream_amd" / "csrc" / "attn_fwd.hip"
 # launches per workload in --profile-prefill (counter runs read them in this order)
 PROFILE_PREFILL_ORDER = ("intra_16k", "cross_window_16k", "cross_full_32k", "intra_32k")
@@ -61,6 +61,12 @@ def parse_args():
                     help="only run decode calls for trace and counter runs (batch 1 and 8, cross_full and "
                          "intra, 3 calls each on distinct caches; then 24 plain reads of the batch-1 "
                          "cache's bytes on the decode's 256-group grid), then exit")
+    ap.add_argument("--trace-prefill", action="store_true",
+                    help="only run the four full-size prefill workloads on the trace build of the library "
+                         "(libsfattn_trace.so) and print each launch's timeline statistics, then exit")
+    ap.add_argument("--profile-backward", action="store_true",
+                    help="only run sf_attn_bwd on the 32k workload for counter runs (cross_full then intra, "
+                         "2 calls each after the forward that gives the LSE), then exit")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="only run the four full-size prefill workloads for counter runs "
                          f"({', '.join(PROFILE_PREFILL_ORDER)}; {PROFILE_PREFILL_REPS} launches each, "
@@ -72,15 +78,25 @@ def source_sha(path: pathlib.Path) -> str:
     return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
 
 
-def stored_mfma_busy():
-    """Hardware MFMA-busy share per prefill workload (SQ_VALU_MFMA_BUSY_CYCLES
-    over GRBM_GUI_ACTIVE x 1024 SIMDs), from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else {}."""
-    if not PROFILE_MFMA.exists():
-        return {}
-    text = PROFILE_MFMA.read_text()
+def _stored_counters():
+    """The committed prefill counter summary, if it was taken on the current
+    kernel source; else None."""
+    if not PROFILE_COUNTERS.exists():
+        return None
+    text = PROFILE_COUNTERS.read_text()
     m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     if not m_sha or m_sha.group(1) != source_sha(FWD_SOURCE):
+        return None
+    return text
+
+
+def stored_mfma_busy():
+    """Hardware MFMA-busy share (SQ_VALU_MFMA_BUSY_CYCLES over one XCD's
+    GRBM_GUI_ACTIVE x 1024 SIMDs) and effective clock per prefill workload,
+    from the committed counter summary (only if taken on the current kernel
+    source); else {}."""
+    text = _stored_counters()
+    if text is None:
         return {}
     out = {}
     for name, busy, clk in re.findall(r"^mfma_busy\[(\w+)\]:\s*([0-9.]+)\s+effective_clock_ghz:\s*([0-9.]+)",
@@ -90,16 +106,12 @@ def stored_mfma_busy():
 
 
 def stored_traffic():
-    """HBM traffic of one cross_full 32k prefill launch, from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    if not PROFILE_PMC.exists():
-        return None
-    text = PROFILE_PMC.read_text()
-    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_b or m_sha.group(1) != source_sha(FWD_SOURCE):
-        return None
-    return float(m_b.group(1))
+    """HBM bytes of one cross_full 32k prefill launch (FETCH_SIZE and
+    WRITE_SIZE, calibrated against a plain copy), from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    text = _stored_counters()
+    m = re.search(r"^hbm_bytes\[cross_full_32k\]:\s*([0-9.eE+]+)", text or "", flags=re.M)
+    return float(m.group(1)) if m else None
 
 
 def main():
@@ -109,6 +121,9 @@ def main():
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    if args.trace_prefill:
+        # the measurement build of the library, with the prefill's timeline compiled in
+        os.environ["SFATTN_LIB"] = str(ROOT / "hidden_decoding_stream_amd" / "libsfattn_trace.so")
     import torch
 
     import hidden_decoding_stream_amd as sfa
@@ -160,6 +175,21 @@ def main():
         print(json.dumps({"profile_read": nbytes, "blocks": 256, "launches": 24}), flush=True)
         return
 
+    if args.trace_prefill:
+        trace_prefill(torch, sfa, I, dev)
+        return
+    if args.profile_backward:
+        wb = I.CROSS_32K
+        q, k, v = I.workload_qkv(wb, device=dev)
+        g = torch.Generator(device=dev).manual_seed(1053)
+        dout = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
+        for mode in ("cross_full", "intra"):
+            o, lse = sfa.sf_attn_fwd(q, k, v, mode, wb.n, scale=wb.scale, lse=True)
+            for _ in range(2):
+                sfa.sf_attn_bwd(q, k, v, o, dout, lse, mode, wb.n, scale=wb.scale)
+            torch.cuda.synchronize()
+            print(json.dumps({"profile_backward": mode, "calls": 2}), flush=True)
+        return
     if args.profile_prefill:
         by_name = {x.name: x for x in I.PREFILL_WORKLOADS}
         for name in PROFILE_PREFILL_ORDER:
@@ -308,6 +338,79 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, C, I, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def trace_prefill(torch, sfa, I, dev, reps=3):
+    """Timeline of the prefill's work groups, from the trace build: for each
+    full-size workload, `reps` launches after 2 untimed ones. Per launch, with
+    every item's start, first-tiles-landed, tile-loop end and end (100 MHz
+    s_memrealtime), and the CU (HW_ID) and XCD (XCC_ID) that ran it:
+      busy_share     sum of item durations / (CUs x span)
+      gap_share      idle time between consecutive items on a CU / (CUs x span)
+      tail_share     idle time after a CU's last item / (CUs x span)
+      prologue_share (first tiles landed - start) / busy: Q load and the first two tiles' DMA
+      epilogue_share (end - tile loop end) / busy: normalisation and the output stores
+      fit_us_per_tile, fit_us_fixed: least squares of item duration against its key tiles.
+    Printed as one JSON line per launch."""
+    import numpy as np
+    L = sfa.lib()
+    L.sf_trace_prefill.argtypes = [ctypes.c_void_p]
+    L.sf_trace_prefill.restype = None
+    by_name = {x.name: x for x in I.PREFILL_WORKLOADS}
+    for name in PROFILE_PREFILL_ORDER:
+        w = by_name[name]
+        q, k, v = I.workload_qkv(w, device=dev)
+        o = torch.empty_like(q)
+        call = lambda: sfa.sf_attn_fwd(q, k, v, w.mode, w.n, window=w.window, scale=w.scale, out=o)  # noqa: E731
+        L.sf_trace_prefill(None)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        # work items of the launch (the kernel's own count): query blocks x head groups per unit
+        G = w.hq // w.hkv
+        HG = 1
+        while HG * 2 <= 8 and G % (HG * 2) == 0:
+            HG *= 2
+        nseq, Lv = (w.n, w.L) if w.mode == "intra" else (1, w.S)
+        items = w.batch * nseq * w.hkv * -(-Lv // ((8 // HG) * 32)) * (G // HG)
+        for rep in range(reps):
+            buf = torch.zeros(items * 8, dtype=torch.int64, device=dev)
+            L.sf_trace_prefill(buf.data_ptr())
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            L.sf_trace_prefill(None)
+            tr = buf.view(-1, 8).cpu().numpy()
+            tr = tr[tr[:, 0] != 0]
+            start, landed, loop_end, end, hw, xcc, _, tiles = (tr[:, i].astype(np.int64) for i in range(8))
+            t0, span = start.min(), end.max() - start.min()
+            cu = xcc * 256 + ((hw >> 8) & 0xFF)      # HW_ID bits 8-15: CU, SH and SE of the work group
+            per = {}
+            for i in range(len(tr)):
+                per.setdefault(int(cu[i]), []).append((int(start[i]), int(end[i])))
+            gaps, tails = 0, 0
+            for lst in per.values():
+                lst.sort()
+                gaps += sum(b[0] - a[1] for a, b in zip(lst, lst[1:]))
+                tails += t0 + span - lst[-1][1]
+            busy = int((end - start).sum())
+            cap = len(per) * span
+            fit = np.linalg.lstsq(np.vstack([tiles, np.ones(len(tiles))]).T.astype(np.float64),
+                                  (end - start).astype(np.float64), rcond=None)[0]
+            print(json.dumps({
+                "trace_prefill": name, "launch": rep, "event_ms": round(e0.elapsed_time(e1), 4),
+                "items": int(len(tr)), "cus": len(per), "span_us": span / 100.0,
+                "busy_share": round(busy / cap, 4), "gap_share": round(gaps / cap, 4),
+                "tail_share": round(tails / cap, 4),
+                "prologue_share": round(float((landed - start).sum()) / busy, 4),
+                "epilogue_share": round(float((end - loop_end).sum()) / busy, 4),
+                "prologue_us_mean": round(float((landed - start).mean()) / 100, 2),
+                "epilogue_us_mean": round(float((end - loop_end).mean()) / 100, 2),
+                "fit_us_per_tile": round(fit[0] / 100, 4), "fit_us_fixed": round(fit[1] / 100, 2)}), flush=True)
+        del q, k, v, o
+        torch.cuda.empty_cache()
 
 
 def prefill_configs(torch, sfa, C, I, dev, stream, hw, step_ms, reps=10):

@@ -4,9 +4,11 @@
 
 Compiles the HIP sources under csrc/ to objects in _build/ (at the repository
 root) and links them into hidden_decoding_stream_amd/libsfattn.so (the
-attention library) and hidden_decoding_stream_amd/libsfpeaks.so (attainable-
-peak microbenchmarks, used only for measurement). Always recompiles: it is the
-"does it build" check as well as the build.
+attention library), hidden_decoding_stream_amd/libsfpeaks.so (attainable-
+peak microbenchmarks) and hidden_decoding_stream_amd/libsfattn_trace.so (the
+attention library with the prefill's per-work-group timeline compiled in,
+SFA_PREFILL_TRACE). The last two are used only for measurement. Always
+recompiles: it is the "does it build" check as well as the build.
 """
 from __future__ import annotations
 
@@ -26,6 +28,7 @@ LIB = PKG / "libsfattn.so"
 SOURCES = ["api.hip", "interleave.hip", "frontend.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
 PEAKS_LIB = PKG / "libsfpeaks.so"
 PEAKS_SOURCES = ["peaks.hip"]
+TRACE_LIB = PKG / "libsfattn_trace.so"
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled: the compiler would otherwise form them
@@ -64,6 +67,9 @@ def build(verbose: bool = False, extra_flags=()) -> pathlib.Path:
     for src in SOURCES + PEAKS_SOURCES:
         obj = BUILD / (pathlib.Path(src).stem + ".o")
         cmds.append((obj, [cc, *FLAGS, *extra_flags, "-c", str(CSRC / src), "-o", str(obj)]))
+    trace_obj = BUILD / "attn_fwd_trace.o"
+    cmds.append((trace_obj, [cc, *FLAGS, *extra_flags, "-DSFA_PREFILL_TRACE", "-c", str(CSRC / "attn_fwd.hip"),
+                             "-o", str(trace_obj)]))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         for (_, cmd), r in zip(cmds, ex.map(_run, [c for _, c in cmds])):
             if verbose:
@@ -72,6 +78,8 @@ def build(verbose: bool = False, extra_flags=()) -> pathlib.Path:
     objs = {pathlib.Path(o).stem: o for o, _ in cmds}
     _link(cc, [objs[pathlib.Path(s).stem] for s in SOURCES], LIB)
     _link(cc, [objs[pathlib.Path(s).stem] for s in PEAKS_SOURCES], PEAKS_LIB)
+    _link(cc, [objs["attn_fwd_trace"] if s == "attn_fwd.hip" else objs[pathlib.Path(s).stem] for s in SOURCES],
+          TRACE_LIB)
     return LIB
 
 

@@ -97,7 +97,25 @@ struct FwdParams {
   int32_t per_xcd;   // ceil(total / 8)
   uint32_t q_bytes;  // buffer sizes (<= 2^31) for out-of-range checks
   uint32_t kv_bytes;
+  unsigned long long* trace;   // trace build only (SFA_PREFILL_TRACE): 8 words per work item
 };
+
+// Timeline of a launch, compiled in only for the measurement build of the
+// library (SFA_PREFILL_TRACE, libsfattn_trace.so): thread 0 of each work group
+// writes 8 words at trace[item * 8]: s_memrealtime (100 MHz) when the item
+// starts, when its first two tiles have landed, when its tile loop ends and
+// when it ends; the HW_ID and XCC_ID registers (which CU and XCD ran it); the
+// block index; and the item's key tiles.
+#ifdef SFA_PREFILL_TRACE
+#define SFA_TRACE_AT(slot)                                           \
+  do {                                                               \
+    if (tid == 0 && p.trace) p.trace[size_t(t) * 8 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define SFA_TRACE_AT(slot) \
+  do {                     \
+  } while (0)
+#endif
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -473,6 +491,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   // ---- work item ----
   const int t = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
   if (t >= p.total) return;
+#ifdef SFA_PREFILL_TRACE
+  if (tid == 0 && p.trace) {
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    p.trace[size_t(t) * 8 + 4] = hw;
+    p.trace[size_t(t) * 8 + 5] = xcc;
+    p.trace[size_t(t) * 8 + 6] = blockIdx.x;
+  }
+#endif
+  SFA_TRACE_AT(0);
   const int ipu = p.nqb * p.hgroups;
   const int unit = t / ipu;
   const int rr = t - unit * ipu;
@@ -586,6 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   if (kt_begin + 1 < kt_end) issue_chunks(kt_begin + 1, 0, NCW);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_barrier" ::: "memory");
+  SFA_TRACE_AT(1);
 
   // The Q fragments' loads completed at the wait above, but the compiler does
   // not read inline asm: passing them through an empty asm makes it place its
@@ -760,6 +790,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   }
   // the last P V MFMAs' results are read by the VALU below
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+  SFA_TRACE_AT(2);
+#ifdef SFA_PREFILL_TRACE
+  if (tid == 0 && p.trace) p.trace[size_t(t) * 8 + 7] = uint32_t(T);
+#endif
 
   // ---- epilogue: O = O^T / l, bf16; optional natural-log LSE ----
   if (!wave_live) return;
@@ -781,12 +815,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
     }
   if (p.lse && hh == 0)
     p.lse[((size_t)b * p.hq + h) * p.QS + (prow - (size_t)b * p.QS)] = (m + log2f(lt)) * kLn2;
+  SFA_TRACE_AT(3);
 }
 
 }  // namespace
 
+#ifdef SFA_PREFILL_TRACE
+unsigned long long* g_prefill_trace = nullptr;
+#endif
+
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   FwdParams p;
+#ifdef SFA_PREFILL_TRACE
+  p.trace = g_prefill_trace;
+#else
+  p.trace = nullptr;
+#endif
   p.q = static_cast<const u16*>(a.q);
   p.k = static_cast<const u16*>(a.k);
   p.v = static_cast<const u16*>(a.v);
@@ -850,3 +894,10 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace sfa
+
+#ifdef SFA_PREFILL_TRACE
+// Measurement build only: prefill launches after this call record their
+// timeline into `buf` (device memory of at least 64 bytes per work item;
+// NULL stops recording).
+extern "C" void sf_trace_prefill(void* buf) { sfa::g_prefill_trace = static_cast<unsigned long long*>(buf); }
+#endif

@@ -3,6 +3,7 @@ tooling; not used by the library itself).
 
     python -m hidden_decoding_stream_amd.profile_summary prefill DIR [DIR ...]
     python -m hidden_decoding_stream_amd.profile_summary decode DIR
+    python -m hidden_decoding_stream_amd.profile_summary kernels PATTERN DIR [DIR ...]
 
 Each DIR holds the CSV output of one `rocprofv3 --pmc ... --kernel-trace
 --output-format csv` run of `bench.py --profile-prefill`, which launches the
@@ -30,6 +31,10 @@ cycles are the sum / 8:
                    share of MFMA-busy cycles in which a VALU op also issued
   lds_*            LDS counters per CU cycle (SQ_LDS_IDX_ACTIVE: LDS busy;
                    SQ_LDS_BANK_CONFLICT: cycles stalled by bank conflicts)
+  hbm_bytes        (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0) KiB per launch: the
+                   factors are what the counters read for a 1 GiB device copy
+                   (bench.py --copy-calibration), against the compulsory
+                   bytes (read Q, K, V once; write O once)
 """
 from __future__ import annotations
 
@@ -47,6 +52,9 @@ REPS = 3
 SIMDS = 1024
 CUS = 256
 XCDS = 8
+# HBM counters against a 1 GiB device copy: FETCH_SIZE reads half the bytes, WRITE_SIZE all of them
+FETCH_FACTOR = 2.0
+WRITE_FACTOR = 1.0
 
 
 def _sha16(path: pathlib.Path) -> str:
@@ -63,11 +71,13 @@ def _read_dir(d: pathlib.Path):
             rec[r["Counter_Name"]] = rec.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             if r.get("Start_Timestamp") and r.get("End_Timestamp"):
                 rec["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    counted = bool(rows)
     for f in sorted(d.rglob("*kernel_trace.csv")):
         for r in csv.DictReader(open(f)):
             did = int(r["Dispatch_Id"])
-            if did in rows:
-                rows[did]["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            if did in rows or not counted:
+                rows.setdefault(did, {"name": r["Kernel_Name"]})["ns"] = int(r["End_Timestamp"]) - int(
+                    r["Start_Timestamp"])
     return rows
 
 
@@ -127,6 +137,11 @@ def prefill(dirs) -> str:
         if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
             out.append(f"  coexec: {100.0 * avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.2f} "
                        "% of MFMA-busy cycles")
+        if "FETCH_SIZE" in avg and "WRITE_SIZE" in avg:
+            # KiB per dispatch, scaled by what the counters read for a plain 1 GiB copy
+            total = (avg["FETCH_SIZE"] * FETCH_FACTOR + avg["WRITE_SIZE"] * WRITE_FACTOR) * 1024
+            compulsory = w.batch * w.S * (2 * w.hq + 2 * w.hkv) * w.d * 2   # read Q, K, V; write O
+            out.append(f"hbm_bytes[{name}]: {total:.4e} (compulsory {compulsory:.4e}, ratio {total / compulsory:.2f})")
         out.append("")
     out.append(f"kernel_source_sha256_16: {sha}")
     return "\n".join(out)
@@ -172,11 +187,69 @@ def decode(d) -> str:
     return "\n".join(out)
 
 
+def kernels(pattern: str, dirs) -> str:
+    """Durations and counters of every kernel whose name contains `pattern`
+    (a run with only --kernel-trace gives the durations alone), averaged
+    over its dispatches in the run directories, with the derived lines of
+    prefill(); FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are also given
+    in bytes, scaled by the 1 GiB copy calibration of
+    FETCH_FACTOR and WRITE_FACTOR)."""
+    per = {}
+    for d in dirs:
+        rows = _read_dir(pathlib.Path(d))
+        for k in sorted(rows):
+            rec = rows[k]
+            if pattern not in rec["name"]:
+                continue
+            name = rec["name"].replace("void ", "").replace("sfa::(anonymous namespace)::", "").split("(")[0]
+            agg = per.setdefault(name, {})
+            for key, val in rec.items():
+                if key != "name":
+                    agg.setdefault(key, []).append(val)
+    out = []
+    for name, agg in per.items():
+        avg = {k: sum(v) / len(v) for k, v in agg.items()}
+        ns = avg.get("ns")
+        out.append(f"{name}: {len(agg.get('ns', []))} dispatches" + (f", mean {ns / 1e3:.1f} us" if ns else ""))
+        if "ns" in agg:
+            out.append("  durations (us, in order): " + " ".join(f"{x / 1e3:.1f}" for x in agg["ns"]))
+        for key in sorted(avg):
+            if key != "ns":
+                out.append(f"  {key}: {avg[key]:.6g}")
+        gui = avg.get("GRBM_GUI_ACTIVE")
+        if gui:
+            gx = gui / XCDS
+            if ns:
+                out.append(f"  effective clock: {gx / ns:.3f} GHz")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                out.append(f"  mfma_busy: {100.0 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (gx * SIMDS):.2f} %")
+            if "SQ_BUSY_CU_CYCLES" in avg:
+                out.append(f"  cu_busy: {100.0 * avg['SQ_BUSY_CU_CYCLES'] / (gx * CUS):.2f} %")
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                out.append(f"  valu_busy: {100.0 * 4 * avg['SQ_ACTIVE_INST_VALU'] / (gx * SIMDS):.2f} %")
+            for key, label in (("SQ_LDS_IDX_ACTIVE", "lds_busy"), ("SQ_LDS_BANK_CONFLICT", "lds_bank_conflict")):
+                if key in avg:
+                    out.append(f"  {label}: {100.0 * avg[key] / (gx * CUS):.2f} % of CU cycles")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and avg.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            out.append(f"  coexec: {100.0 * avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.2f} "
+                       "% of MFMA-busy cycles")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+            out.append(f"  executed bf16 MFMA flops: {avg['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4e}")
+        if "FETCH_SIZE" in avg:
+            out.append(f"  HBM read bytes (FETCH_SIZE x 1024 x {FETCH_FACTOR}): {avg['FETCH_SIZE'] * 1024 * FETCH_FACTOR:.4e}")
+        if "WRITE_SIZE" in avg:
+            out.append(f"  HBM write bytes (WRITE_SIZE x 1024 x {WRITE_FACTOR}): {avg['WRITE_SIZE'] * 1024 * WRITE_FACTOR:.4e}")
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "prefill":
         print(prefill(argv[1:]))
     elif len(argv) == 2 and argv[0] == "decode":
         print(decode(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "kernels":
+        print(kernels(argv[1], argv[2:]))
     else:
         raise SystemExit(__doc__)
 
