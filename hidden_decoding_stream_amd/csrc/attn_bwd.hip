@@ -889,7 +889,6 @@ template <> struct DkdvAsm<64> {
 // row reads at 64 j from one base for the even and one for the odd k-steps.
 constexpr int kRowBytes128 = 320;
 constexpr int kTileBytes128 = 64 * kRowBytes128;
-__device__ __forceinline__ int swz128(int quad) { return (quad & 3) ^ ((quad >> 2) & 1); }
 
 // The block as four groups of eight MFMAs. With one wave per SIMD the matrix
 // core only stays busy if the same wave's vector work and LDS reads issue
@@ -1504,7 +1503,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
       const int row = sl / RBU, u = sl % RBU;
       const bool ok = u < 16 && qt * BT + row < p.Lv;
       const uint32_t off =
-          ok ? tbase + uint32_t(row * pstride) * q_pos_bytes + uint32_t(u ^ swz128(row >> 2)) * 16 : kOobOffset;
+          ok ? tbase + uint32_t(row * pstride) * q_pos_bytes + uint32_t(u ^ row_swizzle128(row >> 2)) * 16 : kOobOffset;
       dma16(j < NCW / 2 ? qrs : dors, &tl[st][j < NCW / 2 ? 0 : 1][cc * 512], off);
     }
     if (wave == 0) {
@@ -1524,7 +1523,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
   // chunks 2 j + hh: base re for even j, ro for odd j, each plus 64 (j / 2))
   uint32_t rofe, rofo;
   {
-    const int r = sigma(l32), sw = swz128(r >> 2);
+    const int r = sigma(l32), sw = row_swizzle128(r >> 2);
     const uint32_t rb = uint32_t(r * kRowBytes128 + 16 * (hh ^ (sw & 1)));
     rofe = rb + 32 * (sw >> 1);
     rofo = rb + 32 - 32 * (sw >> 1);
@@ -1539,7 +1538,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i) {
       const int tt = i & 1, jj = i >> 1;
       const int ro = jj ? 12 * vh + 4 + 8 * tt : 20 * vh + 8 * tt;
-      trof[i] = uint32_t((e + ro) * kRowBytes128 + 16 * (c0 ^ swz128(ro >> 2)) + 8 * half);
+      trof[i] = uint32_t((e + ro) * kRowBytes128 + 16 * (c0 ^ row_swizzle128(ro >> 2)) + 8 * half);
     }
   }
   // (lse2, D) pairs: registers 4 g .. 4 g + 3 hold queries reg_key_offset(g, hh) + 0..3,

@@ -93,12 +93,24 @@ __device__ __forceinline__ void tr_read8(u32x2 (&o)[8], const uint32_t (&a)[8]) 
 // register 4g+r of lane half h then holds C row 8g + 4h + r, i.e. tile row
 // 4*kSigmaG[2g+h] + r: rows 16h .. 16h+15 of the block, so the accumulator
 // registers can feed the next MFMA's B operand (k index = 8h + j) directly.
-// The 16 rows that lanes 0-15 (or 16-31) read are distinct modulo 16, which
-// with a padded row of D+16 elements puts them in distinct LDS bank groups.
 __device__ __forceinline__ int sigma(int m) {
   constexpr uint32_t kSigmaG = 0x63417250u;  // m>>2 = 0..7 -> 0 5 2 7 1 4 3 6 (nibbles, lowest first)
   return 4 * int((kSigmaG >> (4 * (m >> 2))) & 7u) + (m & 3);
 }
+// LDS banks on gfx950: 64 banks of 4 bytes. A 16-byte read (ds_read_b128) is
+// served in four passes of 16 lanes: within each half-wave, the lanes whose
+// quad index (lane / 4 mod 8) has the same parity; 8-byte reads (ds_read_b64,
+// ds_read_b64_tr_b16) in two passes of 32 lanes. A pass in which no two lanes
+// hit one bank at different addresses takes one cycle. For rows read in the
+// sigma order, a pass covers 4 aligned row quads (sigma groups {0,7,4,3} or
+// {5,2,1,6}, plus 8 for the second 32 rows), so with rows of d = 128 bf16
+// padded to 320 bytes (rows of one quad then lie 64 bytes apart modulo 256)
+// and the 16-byte chunk index XORed with this value of the row quad, the 4
+// quads of a pass land in distinct 16-byte slots: the two low bits are
+// distinct over each group, and bit 3 (the second 32 rows) is ignored. A
+// transposed read (64 bytes from each row of one aligned quad) only sees the
+// chunks permuted within those 64 bytes.
+__device__ __forceinline__ int row_swizzle128(int quad) { return (quad & 3) ^ ((quad >> 2) & 1); }
 // Offset (within a 32-key block) of the 4 keys held in registers 4g..4g+3 by
 // lane half h: 16h + 4*(((g&1)*2 + (g>>1)) ^ h).
 __device__ __forceinline__ int reg_key_offset(int g, int h) { return 16 * h + 4 * ((((g & 1) * 2 + (g >> 1))) ^ h); }
