@@ -23,17 +23,20 @@
 //   groups per CU (253 VGPRs, no spills: the per-lane DMA offsets are
 //   recomputed per tile, and the transposed reads share two base registers);
 //   the windowed mode runs one and its loop in asm phases (DqAsm).
-// * bwd_dkdv_kernel: key-stationary. A wave owns 32 keys (K and V in registers
-//   as B operands); the Q and dO tiles of 64 queries stream through LDS, for
-//   each of the G query heads in turn. S = Q K^T and dP = dO V^T (lane = key
-//   column), P and dS with each register's own query lse / D, then
-//   dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposed reads).
-// Tiles are K-style: rows padded to D+16 elements (the sigma-order 16-byte
-// reads hit distinct bank groups), loaded by buffer->LDS DMA through a ring
-// (2 stages for dQ, 3 for dK/dV) with one bare barrier per tile; LDS reads
-// are asm blocks that wait for their own results (see common.h), and the
-// one-wave-per-SIMD loops run their MFMAs inside those blocks (DkdvAsm,
-// DqAsm).
+// * bwd_dkdv128_kernel (d = 128) and bwd_dkdv_kernel (d = 64): key-stationary.
+//   A wave owns 32 keys (K and V as B operands); the Q and dO tiles of 64
+//   queries stream through LDS, for each of the G query heads in turn.
+//   S = Q K^T and dP = dO V^T (lane = key column), P and dS with each
+//   register's own query lse / D, then dV^T += dO^T P and dK^T += Q^T dS
+//   (dO^T, Q^T by transposed reads). At d = 128 each 32-query block is one
+//   scheduled asm stream (dkdv_block128) over tiles laid out free of LDS
+//   bank conflicts (row_swizzle128, common.h); at d = 64 the block runs in
+//   three asm phases (DkdvAsm).
+// Tiles go by buffer->LDS DMA through a ring (2 stages for dQ, 3 for dK/dV)
+// with one bare barrier per tile; dQ and the d = 64 dK/dV use K-style rows
+// padded to D+16 elements. LDS reads are asm blocks that wait for their own
+// results (see common.h), and the one-wave-per-SIMD loops run their MFMAs
+// inside those blocks (dkdv_block128, DkdvAsm, DqAsm).
 #include <math.h>
 
 #include "common.h"
@@ -749,7 +752,7 @@ __global__ __launch_bounds__(kThreads, MODE == 2 ? 1 : 2) void bwd_dq_kernel(Bwd
 }
 
 
-// The dK/dV loop in three phases per 32-query block, each one asm block that
+// The d = 64 dK/dV loop in three phases per 32-query block, each one asm block that
 // issues the phase's MFMAs with the LDS reads the next phase needs spread over
 // the first half of them, and waits for those reads only at its end: with one
 // wave per SIMD, nothing else would keep the matrix core busy while a read is
