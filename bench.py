@@ -41,7 +41,9 @@ METRIC = "SF-attention useful TFLOP/s + MFMA% at n=4 nL=32k; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 PROFILE_COUNTERS = ROOT / "profiles" / "attn_fwd_prefill_counters.txt"
-FWD_SOURCE = ROOT / "hidden_decoding_stream_amd" / "csrc" / "attn_fwd.hip"
+# the prefill kernels' sources: the counter summary is used only if taken on these
+FWD_SOURCES = (ROOT / "hidden_decoding_stream_amd" / "csrc" / "attn_fwd.hip",
+               ROOT / "hidden_decoding_stream_amd" / "csrc" / "attn_fwd128_stream.h")
 # launches per workload in --profile-prefill (counter runs read them in this order)
 PROFILE_PREFILL_ORDER = ("intra_16k", "cross_window_16k", "cross_full_32k", "intra_32k")
 PROFILE_PREFILL_REPS = 3
@@ -74,8 +76,11 @@ def parse_args():
     return ap.parse_args()
 
 
-def source_sha(path: pathlib.Path) -> str:
-    return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(path.read_bytes())
+    return h.hexdigest()[:16]
 
 
 def _stored_counters():
@@ -85,7 +90,7 @@ def _stored_counters():
         return None
     text = PROFILE_COUNTERS.read_text()
     m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m_sha or m_sha.group(1) != source_sha(FWD_SOURCE):
+    if not m_sha or m_sha.group(1) != source_sha(FWD_SOURCES):
         return None
     return text
 
@@ -304,7 +309,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "attn_fwd_kernel<128, 1, false> (cross_full) 32k",
+            "kernel": "attn_fwd128_kernel<1> (cross_full) 32k",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -37,11 +37,15 @@
 //   use an out-of-range offset and read as zeros, with no branch. K rows are padded
 //   and V pieces swizzled so that the operand reads are free of bank
 //   conflicts.
-// * Occupancy. A work group is 8 waves (two per SIMD), each owning 32
-//   queries of one query head; one group per CU (138 KiB of LDS at d=128).
-//   The two waves of a SIMD run their MFMA and softmax phases in opposite
-//   order (ping-pong), so that the VALU-heavy softmax of one overlaps the
-//   MFMAs of the other.
+// * Two kernels. attn_fwd128_kernel (d = 128, every position querying) runs
+//   one wave per SIMD with 64 queries each and the whole tile loop as one
+//   scheduled instruction stream; it is described where it is defined. The
+//   rest of this header describes attn_fwd_kernel, which serves d = 64 and
+//   the last-stream queries: a work group is 8 waves (two per SIMD), each
+//   owning 32 queries of one query head; one group per CU (138 KiB of LDS at
+//   d=128). The two waves of a SIMD run their MFMA and softmax phases in
+//   opposite order (ping-pong), so that the VALU-heavy softmax of one
+//   overlaps the MFMAs of the other.
 // * Online softmax in base 2 with lazy rescaling: the running reference max m
 //   is raised only when a tile's max exceeds it by more than 2^8; until then
 //   exp2(s - m) <= 256 and no O rescale is needed. The result is the same
@@ -55,6 +59,7 @@
 
 #include <type_traits>
 
+#include "attn_fwd128_stream.h"
 #include "common.h"
 #include "launch.h"
 
@@ -818,6 +823,272 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
   SFA_TRACE_AT(3);
 }
 
+
+// ---------------------------------------------------------------------------
+// d = 128, every position querying: one wave per SIMD.
+//
+// A work group is 4 waves (one per SIMD), each owning 64 queries (two 32-query
+// blocks QB0, QB1) of one query head, with 512 registers per wave. Per 64-key
+// tile t a wave issues 64 MFMAs in one scheduled instruction stream:
+//   S0(t)  = K(t) Q0^T             (16, scores of QB0)
+//   O1    += V(t-1)^T P1(t-1)^T    (16, QB1's P V of the previous tile)
+//   S1(t)  = K(t) Q1^T             (16)
+//   O0    += V(t)^T P0(t)^T        (16)
+// and in the shadow of each MFMA (32 cycles) up to 7 other instructions: the
+// softmax of QB0 of tile t between S0(t) and O0 += ..., that of QB1 between
+// S1(t) and the next tile's O1 += ..., the V^T reads of tile t (into the
+// registers each finished O1 MFMA frees), the K reads of tile t+1, the
+// barrier and the DMA of tile t+4. K operands are read once per tile for 64
+// queries, half the LDS reads per query of the two-waves-per-SIMD kernel.
+// The whole tile loop is one asm block (the stream, its register plan and
+// the wait states between its instructions are fixed, see the block's
+// layout below), unrolled over the 4 LDS stages so that every LDS offset is
+// an immediate.
+//
+// Register plan (per wave): AGPR a0-63 O0^T, a64-127 O1^T (4 d blocks x 16),
+// a128-159 / a160-191 Q0^T / Q1^T (8 k steps x 4), a192-255 V^T operands of
+// one tile (4 d blocks x 2 key blocks x 2 k steps); VGPR v96-159 K operands of
+// one tile (2 key blocks x 8 k steps), v160-175 / v176-191 P1 / P0 in bf16,
+// v192-223 / v224-255 S1 / S0, v80-95 temporaries.
+//
+// Softmax. The probabilities of a tile are computed against the running
+// reference max m as they stand, p = exp2(c s - m), summed per lane from the
+// bf16 values the P V product uses (v_dot2 with ones). Only when a lane's sum
+// over the tile exceeds 2^8, which any p > 2^8 implies, does the wave take the
+// out-of-line path: it forms the tile's max, raises m where the max exceeds
+// it by more than 2^8 (rescaling O and l there) and recomputes the tile. This
+// is the lazy rescale of the two-waves kernel with its per-tile max taken
+// only when it can matter.
+//
+// Masks: a tile is full (every key allowed for every query of the block),
+// empty, or one of at most three special tiles per query block (the
+// diagonal, and up to two tiles cut by the window's start), whose per-lane
+// 32-bit mask words are formed once per work item. Full tiles cost one
+// scalar compare; the rest go out of line and set masked scores to -inf.
+//
+// Memory: K (rows padded to 288 bytes) and V (64-byte pieces swizzled by
+// row) tiles go from HBM to LDS by DMA through 4 stages of 36 KiB; every wave
+// moves 5 K chunks (waves 2 and 3 one empty chunk each, from a zero-length
+// buffer) and 4 V chunks of 1 KiB per tile, so that the wait for tile t+1
+// before the barrier of tile t is one fixed count. Past the last tile the
+// DMA continues with out-of-range offsets (zeros), and the loop runs one
+// extra, fully masked, tile so that the last tile's QB1 P V runs in the same
+// stream; rows past the end of a sequence load the next rows of the buffer
+// (or zeros past its end), which the causal mask excludes.
+constexpr int kW128 = 4;
+constexpr int kKStage128 = 18432;         // LDS bytes per K stage (64 rows of 288)
+constexpr int kVStage128 = 16384;         // per V stage
+constexpr int kVRegion128 = 4 * kKStage128;   // the 4 V stages follow the 4 K stages
+
+template <int MODE>
+__global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * (kKStage128 + kVStage128)];
+
+  const int pstride = MODE == 0 ? p.pstride : 1;
+  const int window = MODE == 2 ? p.window : 0;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // ---- work item: (batch, stream, kv head, query block, head group) ----
+  const int t = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+  if (t >= p.total) return;
+  const int ipu = p.nqb * p.hgroups;
+  const int unit = t / ipu;
+  const int rr = t - unit * ipu;
+  const int qb = p.nqb - 1 - rr / p.hgroups;
+  const int hg = rr % p.hgroups;
+  const int kvh = unit % p.hkv;
+  const int bs = unit / p.hkv;
+  const int sq = p.sq0 + bs % p.nseq;
+  const int b = bs / p.nseq;
+  const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
+  const int PS = (kW128 / p.HG) * 64;
+  const int wg_q0 = qb * PS;
+  const int q0 = wg_q0 + (wave / p.HG) * 64;
+  const int wg_qlast = min(wg_q0 + PS, p.Lq) - 1;
+  const int kt_begin = window > 0 ? max(0, wg_q0 - window + 1) / BN : 0;
+  const int kt_end = wg_qlast / BN + 1;
+  const int T = kt_end - kt_begin;
+
+  const int base_row = b * p.S + sq;
+  const int qbase_row = b * p.QS + sq * p.q_sq;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
+  const uint32_t kv_pos_bytes = uint32_t(p.hkv) * D * 2;
+  const uint32_t kv_head_bytes = uint32_t(kvh) * D * 2;
+  const uint32_t tstride = uint32_t(BN * pstride) * kv_pos_bytes;   // bytes between tiles
+
+  // ---- Q^T fragments: lane holds Q[q0 + 32 j + l32][kk*16 + 8 hh .. +8] ----
+  typedef __bf16 bf16x64 __attribute__((ext_vector_type(64)));
+  bf16x64 qv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int vq = q0 + 32 * j + l32;
+    const uint32_t off = ((uint32_t(qbase_row + vq * p.q_rs) * p.hq + h) * D + 8 * hh) * 2 +
+                         (vq < p.Lq ? 0u : kOobOffset);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 x = bload16(qrs, off + kk * 32);
+      __builtin_memcpy(reinterpret_cast<char*>(&qv[j]) + kk * 16, &x, 16);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- DMA chunks of this wave: K chunks w + 4j (j < 4) and c4, V chunks
+  // w + 4(j - 5). The 18 K chunks leave waves 2 and 3 a fifth chunk to spare:
+  // they repeat chunks 17 and 16 (same source, same destination, same bytes).
+  const int c4 = wave < 2 ? wave + 16 : 19 - wave;
+  uint32_t cf[9];
+#pragma unroll
+  for (int jx = 0; jx < 9; ++jx) {
+    if (jx < 5) {
+      const int sl = (jx < 4 ? wave + 4 * jx : c4) * 64 + lane;
+      const int row = sl / 18, ch = sl % 18;
+      cf[jx] = ch >= 16 ? kOobOffset : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
+    } else {
+      const int sl = (wave + 4 * (jx - 5)) * 64 + lane;
+      const int row = sl / 16, u = sl % 16;
+      const int ch = (((u >> 2) ^ (row & 3)) << 2) | (u & 3);
+      cf[jx] = uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
+    }
+  }
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  auto tile_base = [&](int kt) { return uint32_t(base_row + kt * BN * pstride) * kv_pos_bytes; };
+  // tiles 0..3 of the loop into stages 0..3 (past the last tile: zeros)
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t tb = tile_base(kt_begin + s);
+#pragma unroll
+    for (int jx = 0; jx < 9; ++jx) {
+      const uint32_t dst = jx < 5 ? s * kKStage128 + (jx < 4 ? wave + 4 * jx : c4) * 1024
+                                  : kVRegion128 + s * kVStage128 + (wave + 4 * (jx - 5)) * 1024;
+      const uint32_t off = (s < T && cf[jx] < kOobOffset) ? cf[jx] + tb : kOobOffset;
+      dma16(jx < 5 ? krs : vrs, &lds[dst], off);
+    }
+  }
+  // the loop's first DMA is tile 4
+#pragma unroll
+  for (int jx = 0; jx < 9; ++jx) cf[jx] = (4 < T && cf[jx] < kOobOffset) ? cf[jx] + tile_base(kt_begin + 4) : kOobOffset;
+
+  // ---- masks: full range and special tiles of each query block ----
+  uint32_t fd[2], fc[2], sp[2][3], mk[2][3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qlo = q0 + 32 * j, qhi = qlo + 31;
+    const int fa_hi = qlo >= BN - 1 ? (qlo - (BN - 1)) / BN : -1;
+    const int fa_lo = window > 0 ? (qhi - window >= 0 ? (qhi - window) / BN + 1 : 0) : 0;
+    fd[j] = uint32_t(fa_lo - kt_begin);
+    fc[j] = uint32_t(max(0, fa_hi - fa_lo + 1));
+    int cand[3] = {qlo / BN, -1, -1};
+    if (window > 0) {
+      // tiles holding keys qlo - window + 1 .. qhi - window (the window's start)
+      const int a = qlo - window + 1, z = qhi - window;
+      if (z >= 0) {
+        const int ta = a >= 0 ? a / BN : 0, tz = z / BN;
+        int n = 1;
+        for (int x = ta; x <= tz && n < 3; ++x)
+          if (x != cand[0]) cand[n++] = x;
+      }
+    }
+    const int vq = qlo + l32;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      sp[j][k] = cand[k] >= kt_begin && cand[k] < kt_end ? uint32_t(cand[k] - kt_begin) : 0xffffffffu;
+      uint32_t w = 0;
+      if (cand[k] >= 0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = cand[k] * BN + kb * 32 + reg_key_offset(g, hh) + r;
+              const bool ok = key <= vq && (window == 0 || vq - key < window);
+              w |= uint32_t(ok) << (kb * 16 + 4 * g + r);
+            }
+      }
+      mk[j][k] = w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    fd[j] = __builtin_amdgcn_readfirstlane(fd[j]);
+    fc[j] = __builtin_amdgcn_readfirstlane(fc[j]);
+  }
+
+  // ---- LDS read bases of stage 0 (the other stages: immediate offsets) ----
+  const int krow0 = sigma(l32);
+  const uint32_t kl = lds0 + uint32_t(krow0 * 288 + 16 * hh);
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vh = grp >> 1, vsw = gi >> 2;
+  const int vbase = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3);
+  uint32_t ve[4], vo[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int col = (db ^ vsw) * 32;
+    ve[db] = lds0 + kVRegion128 + uint32_t(vbase + vh * 20 * D + col) * 2;
+    vo[db] = lds0 + kVRegion128 + uint32_t(vbase + vh * 12 * D + col) * 2;
+  }
+  const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(wave) * 1024);
+  const uint32_t lw4 = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(c4) * 1024 - 16384u);
+  const uint32_t Tn = __builtin_amdgcn_readfirstlane(uint32_t(T));
+
+  // tile 0 landed for every wave
+  asm volatile("s_waitcnt vmcnt(27)\n\ts_barrier" ::: "memory");
+
+  typedef float f32x32 __attribute__((ext_vector_type(32)));
+  f32x32 o0a, o0b, o1a, o1b;
+  float m0 = -1e30f, l0 = 0.f, m1 = -1e30f, l1 = 0.f;
+  asm volatile(
+      SFA_FWD128_PROLOGUE
+      SFA_FWD128_LOOP
+      "s_waitcnt vmcnt(0) lgkmcnt(0)\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      : [o0a] "={a[0:31]}"(o0a), [o0b] "={a[32:63]}"(o0b), [o1a] "={a[64:95]}"(o1a), [o1b] "={a[96:127]}"(o1b),
+        [m0] "+v"(m0), [l0] "+v"(l0), [m1] "+v"(m1), [l1] "+v"(l1), [cf0] "+v"(cf[0]), [cf1] "+v"(cf[1]),
+        [cf2] "+v"(cf[2]), [cf3] "+v"(cf[3]), [cf4] "+v"(cf[4]), [cf5] "+v"(cf[5]), [cf6] "+v"(cf[6]),
+        [cf7] "+v"(cf[7]), [cf8] "+v"(cf[8])
+      : [q0] "{a[128:159]}"(qv[0]), [q1] "{a[160:191]}"(qv[1]), [c] "s"(p.c), [T] "s"(Tn),
+        [tstride] "s"(tstride), [rk] "s"(krs), [rv] "s"(vrs), [lw] "s"(lw), [lw4] "s"(lw4), [fd0] "s"(fd[0]),
+        [fc0] "s"(fc[0]), [fd1] "s"(fd[1]), [fc1] "s"(fc[1]), [sp00] "v"(sp[0][0]), [sp01] "v"(sp[0][1]),
+        [sp02] "v"(sp[0][2]), [sp10] "v"(sp[1][0]), [sp11] "v"(sp[1][1]), [sp12] "v"(sp[1][2]),
+        [mk00] "v"(mk[0][0]), [mk01] "v"(mk[0][1]), [mk02] "v"(mk[0][2]), [mk10] "v"(mk[1][0]),
+        [mk11] "v"(mk[1][1]), [mk12] "v"(mk[1][2]), [kl] "v"(kl), [ve0] "v"(ve[0]), [ve1] "v"(ve[1]),
+        [ve2] "v"(ve[2]), [ve3] "v"(ve[3]), [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3])
+      : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", SFA_FWD128_CLOBBER_V,
+        SFA_FWD128_CLOBBER_A);
+
+  // ---- epilogue: O = O^T / l, bf16; optional natural-log LSE ----
+  const f32x32 oh[2][2] = {{o0a, o0b}, {o1a, o1b}};
+  const float mm[2] = {m0, m1}, ll[2] = {l0, l1};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float lt = pair_sum(ll[j]);
+    const int vq = q0 + 32 * j + l32;
+    if (vq >= p.Lq) continue;
+    const float inv = 1.f / lt;
+    const size_t prow = (size_t)(qbase_row + vq * p.q_rs);
+    u16* orow = p.o + (prow * p.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 ov;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(oh[j][db >> 1][(db & 1) * 16 + 4 * g + r] * inv);
+        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hh) = ov;
+      }
+    if (p.lse && hh == 0)
+      p.lse[((size_t)b * p.hq + h) * p.QS + (prow - (size_t)b * p.QS)] = (mm[j] + log2f(lt)) * kLn2;
+  }
+}
+
 }  // namespace
 
 #ifdef SFA_PREFILL_TRACE
@@ -865,13 +1136,18 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.G = a.hq / a.hkv;
+  // d = 128 with every position querying: the one-wave-per-SIMD kernel
+  // (4 waves of 64 queries); otherwise 8 waves of 32 queries
+  const bool w128 = a.d == 128 && !a.last_stream;
+  const int waves = w128 ? kW128 : kWaves;
+  const int qpw = w128 ? 64 : 32;
   p.HG = 1;
-  while (p.HG * 2 <= kWaves && p.G % (p.HG * 2) == 0) p.HG *= 2;
+  while (p.HG * 2 <= waves && p.G % (p.HG * 2) == 0) p.HG *= 2;
   p.hgroups = p.G / p.HG;
   // A window at least as long as the sequence is full causal attention.
   p.window = (a.mode == 2 && a.window < S) ? int32_t(a.window) : 0;
   p.c = a.scale * kLog2e;
-  const int PS = (kWaves / p.HG) * 32;
+  const int PS = (waves / p.HG) * qpw;
   p.nqb = (p.Lq + PS - 1) / PS;
   const int64_t total = int64_t(a.batch) * p.nseq * p.hkv * p.nqb * p.hgroups;
   p.total = int32_t(total);
@@ -888,6 +1164,11 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
       {attn_fwd_kernel<128, 0, false>, attn_fwd_kernel<128, 1, false>, attn_fwd_kernel<128, 2, false>,
        attn_fwd_kernel<128, 1, true>, attn_fwd_kernel<128, 2, true>}};
   int kind = intra ? 0 : (p.window > 0 ? 2 : 1);
+  if (w128) {
+    static constexpr Kernel k128[3] = {attn_fwd128_kernel<0>, attn_fwd128_kernel<1>, attn_fwd128_kernel<2>};
+    hipLaunchKernelGGL(k128[kind], grid, dim3(64 * kW128), 0, stream, p);
+    return hipGetLastError();
+  }
   if (a.last_stream && !intra) kind += 2;
   hipLaunchKernelGGL(kKernels[a.d == 128][kind], grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();

@@ -8,7 +8,8 @@ tooling; not used by the library itself).
 Each DIR holds the CSV output of one `rocprofv3 --pmc ... --kernel-trace
 --output-format csv` run of `bench.py --profile-prefill`, which launches the
 four full-size prefill workloads three times each, in a fixed order. The
-attn_fwd_kernel dispatches are assigned to the workloads in dispatch order.
+prefill kernel dispatches (attn_fwd128_kernel, attn_fwd_kernel) are assigned to
+the workloads in dispatch order.
 For each workload it prints the counters averaged over its launches and what
 follows from them. GRBM_GUI_ACTIVE is reported summed over the chip's 8 XCDs
 (one instance each, counting that XCD's active cycles), so one XCD's active
@@ -41,6 +42,7 @@ from __future__ import annotations
 import csv
 import hashlib
 import pathlib
+import re
 import sys
 
 from . import counts as C
@@ -57,8 +59,13 @@ FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
 
 
-def _sha16(path: pathlib.Path) -> str:
-    return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+def _sha16(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the given files' bytes, in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(pathlib.Path(path).read_bytes())
+    return h.hexdigest()[:16]
+
 
 
 def _read_dir(d: pathlib.Path):
@@ -87,9 +94,9 @@ def prefill(dirs) -> str:
     counters_seen = []
     for d in dirs:
         rows = _read_dir(pathlib.Path(d))
-        fwd = [rows[k] for k in sorted(rows) if "attn_fwd_kernel<" in rows[k]["name"]]
+        fwd = [rows[k] for k in sorted(rows) if re.search(r"attn_fwd(128)?_kernel<", rows[k]["name"])]
         if len(fwd) != len(ORDER) * REPS:
-            raise SystemExit(f"{d}: expected {len(ORDER) * REPS} attn_fwd_kernel dispatches, found {len(fwd)}")
+            raise SystemExit(f"{d}: expected {len(ORDER) * REPS} prefill dispatches, found {len(fwd)}")
         for i, name in enumerate(ORDER):
             for rec in fwd[i * REPS:(i + 1) * REPS]:
                 for key, val in rec.items():
@@ -101,7 +108,7 @@ def prefill(dirs) -> str:
             if key not in ("name", "ns") and key not in counters_seen:
                 counters_seen.append(key)
     out = []
-    sha = _sha16(PKG / "csrc" / "attn_fwd.hip")
+    sha = _sha16([PKG / "csrc" / "attn_fwd.hip", PKG / "csrc" / "attn_fwd128_stream.h"])
     for name in ORDER:
         w = by_name[name]
         rec = per[name]
