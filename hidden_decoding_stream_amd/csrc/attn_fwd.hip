@@ -866,17 +866,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
 // 32-bit mask words are formed once per work item. Full tiles cost one
 // scalar compare; the rest go out of line and set masked scores to -inf.
 //
-// Memory: K (rows padded to 288 bytes) and V (64-byte pieces swizzled by
-// row) tiles go from HBM to LDS by DMA through 4 stages of 36 KiB; every wave
-// moves 5 K chunks (waves 2 and 3 one empty chunk each, from a zero-length
-// buffer) and 4 V chunks of 1 KiB per tile, so that the wait for tile t+1
-// before the barrier of tile t is one fixed count. Past the last tile the
+// Memory: K (rows of 320 bytes, 16-byte chunks swizzled by row quad) and V
+// (64-byte pieces swizzled by row) tiles go from HBM to LDS by DMA through 4
+// stages of 36 KiB; every wave moves 5 K and 4 V chunks of 1 KiB per tile, so
+// that the wait for tile t+1 before the barrier of tile t is one fixed count. Past the last tile the
 // DMA continues with out-of-range offsets (zeros), and the loop runs one
 // extra, fully masked, tile so that the last tile's QB1 P V runs in the same
 // stream; rows past the end of a sequence load the next rows of the buffer
 // (or zeros past its end), which the causal mask excludes.
 constexpr int kW128 = 4;
-constexpr int kKStage128 = 18432;         // LDS bytes per K stage (64 rows of 288)
+constexpr int kKStage128 = 20480;         // LDS bytes per K stage (64 rows of 320)
 constexpr int kVStage128 = 16384;         // per V stage
 constexpr int kVRegion128 = 4 * kKStage128;   // the 4 V stages follow the 4 K stages
 
@@ -938,17 +937,19 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- DMA chunks of this wave: K chunks w + 4j (j < 4) and c4, V chunks
-  // w + 4(j - 5). The 18 K chunks leave waves 2 and 3 a fifth chunk to spare:
-  // they repeat chunks 17 and 16 (same source, same destination, same bytes).
-  const int c4 = wave < 2 ? wave + 16 : 19 - wave;
+  // ---- DMA chunks of this wave: K chunks w + 4j (j < 5), V chunks w + 4(j - 5) ----
+  // A K row is 20 slots of 16 bytes: slot u < 16 holds data chunk
+  // u ^ row_swizzle128(row / 4) (the K reads below are then free of bank
+  // conflicts), slots 16-19 are padding (zeros).
   uint32_t cf[9];
 #pragma unroll
   for (int jx = 0; jx < 9; ++jx) {
     if (jx < 5) {
-      const int sl = (jx < 4 ? wave + 4 * jx : c4) * 64 + lane;
-      const int row = sl / 18, ch = sl % 18;
-      cf[jx] = ch >= 16 ? kOobOffset : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + ch * 16;
+      const int sl = (wave + 4 * jx) * 64 + lane;
+      const int row = sl / 20, u = sl % 20;
+      cf[jx] = u >= 16 ? kOobOffset
+                       : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes +
+                             (u ^ row_swizzle128(row >> 2)) * 16;
     } else {
       const int sl = (wave + 4 * (jx - 5)) * 64 + lane;
       const int row = sl / 16, u = sl % 16;
@@ -964,7 +965,7 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
     const uint32_t tb = tile_base(kt_begin + s);
 #pragma unroll
     for (int jx = 0; jx < 9; ++jx) {
-      const uint32_t dst = jx < 5 ? s * kKStage128 + (jx < 4 ? wave + 4 * jx : c4) * 1024
+      const uint32_t dst = jx < 5 ? s * kKStage128 + (wave + 4 * jx) * 1024
                                   : kVRegion128 + s * kVStage128 + (wave + 4 * (jx - 5)) * 1024;
       const uint32_t off = (s < T && cf[jx] < kOobOffset) ? cf[jx] + tb : kOobOffset;
       dma16(jx < 5 ? krs : vrs, &lds[dst], off);
@@ -1020,9 +1021,16 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
     fc[j] = __builtin_amdgcn_readfirstlane(fc[j]);
   }
 
-  // ---- LDS read bases of stage 0 (the other stages: immediate offsets) ----
+  // ---- LDS read bases (the stages: immediate offsets; K stages 2, 3 from a
+  // second pair of bases). K operand (kb, kk) of this lane is chunk 2 kk + hh
+  // of row sigma(l32) + 32 kb: slot (2 kk + hh) ^ sw with sw the row's
+  // swizzle, so even and odd kk sit at two per-lane offsets within each
+  // 64-byte piece (the same for both key blocks).
   const int krow0 = sigma(l32);
-  const uint32_t kl = lds0 + uint32_t(krow0 * 288 + 16 * hh);
+  const int ksw = row_swizzle128(krow0 >> 2);
+  const uint32_t krb = lds0 + uint32_t(krow0 * 320 + 16 * (hh ^ (ksw & 1)));
+  const uint32_t ke0 = krb + 32 * (ksw >> 1), ko0 = krb + 32 - 32 * (ksw >> 1);
+  const uint32_t ke1 = ke0 + 2 * kKStage128, ko1 = ko0 + 2 * kKStage128;
   const int grp = lane >> 4, gi = lane & 15;
   const int vh = grp >> 1, vsw = gi >> 2;
   const int vbase = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3);
@@ -1034,7 +1042,6 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
     vo[db] = lds0 + kVRegion128 + uint32_t(vbase + vh * 12 * D + col) * 2;
   }
   const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(wave) * 1024);
-  const uint32_t lw4 = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(c4) * 1024 - 16384u);
   const uint32_t Tn = __builtin_amdgcn_readfirstlane(uint32_t(T));
 
   // tile 0 landed for every wave
@@ -1054,11 +1061,11 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
         [cf2] "+v"(cf[2]), [cf3] "+v"(cf[3]), [cf4] "+v"(cf[4]), [cf5] "+v"(cf[5]), [cf6] "+v"(cf[6]),
         [cf7] "+v"(cf[7]), [cf8] "+v"(cf[8])
       : [q0] "{a[128:159]}"(qv[0]), [q1] "{a[160:191]}"(qv[1]), [c] "s"(p.c), [T] "s"(Tn),
-        [tstride] "s"(tstride), [rk] "s"(krs), [rv] "s"(vrs), [lw] "s"(lw), [lw4] "s"(lw4), [fd0] "s"(fd[0]),
+        [tstride] "s"(tstride), [rk] "s"(krs), [rv] "s"(vrs), [lw] "s"(lw), [fd0] "s"(fd[0]),
         [fc0] "s"(fc[0]), [fd1] "s"(fd[1]), [fc1] "s"(fc[1]), [sp00] "v"(sp[0][0]), [sp01] "v"(sp[0][1]),
         [sp02] "v"(sp[0][2]), [sp10] "v"(sp[1][0]), [sp11] "v"(sp[1][1]), [sp12] "v"(sp[1][2]),
         [mk00] "v"(mk[0][0]), [mk01] "v"(mk[0][1]), [mk02] "v"(mk[0][2]), [mk10] "v"(mk[1][0]),
-        [mk11] "v"(mk[1][1]), [mk12] "v"(mk[1][2]), [kl] "v"(kl), [ve0] "v"(ve[0]), [ve1] "v"(ve[1]),
+        [mk11] "v"(mk[1][1]), [mk12] "v"(mk[1][2]), [ke0] "v"(ke0), [ko0] "v"(ko0), [ke1] "v"(ke1), [ko1] "v"(ko1), [ve0] "v"(ve[0]), [ve1] "v"(ve[1]),
         [ve2] "v"(ve[2]), [ve3] "v"(ve[3]), [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3])
       : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", SFA_FWD128_CLOBBER_V,
         SFA_FWD128_CLOBBER_A);

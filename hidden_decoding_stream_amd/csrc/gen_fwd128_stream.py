@@ -42,8 +42,9 @@ LT = [88, 89]
 T0, T1, T2, T3, T4 = 90, 91, 92, 93, 94
 SI, SX = 84, [85, 86]       # loop counter, mask-check scratch per QB
 SINC, STMP, SRET = 88, 87, 89
+LDS_PER_GAP = int(__import__("os").environ.get("LDS_PER_GAP", "2"))   # LDS reads per MFMA shadow
 
-KST = 18432      # bytes per K stage (64 rows of 288)
+KST = 20480      # bytes per K stage (64 rows of 320: 16 chunks of 16 bytes, swizzled, and 4 pad slots)
 VST = 16384      # bytes per V stage
 V_REGION = 4 * KST
 
@@ -277,6 +278,17 @@ def stream_x_or_y(j, lab_mask, lab_slow, pairs_head, pairs_tail, part, st):
 
 
 # ---------------------------------------------------------------- LDS / DMA
+def kbase(st, kk):
+    """Base register of K operand reads: even / odd k step (the row swizzle moves
+    the two 32-byte halves of a 64-byte piece apart per row), stages 0-1 / 2-3."""
+    return f"%[k{'o' if kk % 2 else 'e'}{st // 2}]"
+
+
+def kofs(st, kb, kk):
+    """Immediate offset of K operand (kb, kk) in stage st (rows of 320 bytes)."""
+    return (st % 2) * KST + 32 * 320 * kb + 64 * (kk // 2)
+
+
 def v_reads(st):
     items = []
     so = st * VST
@@ -289,7 +301,7 @@ def v_reads(st):
         for h in range(2):
             it = Ins(f"ds_read_b64_tr_b16 {ar(reg + 2 * h, 2)}, {base} offset:{so + offs[h]}", "lds",
                      wr=aset(reg + 2 * h, 2), after=16 + u + 2, name=f"V{u}.{h}")
-            it.fixed_deadline = 40
+            it.fixed_deadline = 36
             items.append(it)
     return items
 
@@ -301,7 +313,7 @@ def k_reads(st):
     for mm in range(16):
         kk, kb = divmod(mm, 2)
         reg = K_BASE + 32 * kb + 4 * kk
-        items.append(Ins(f"ds_read_b128 {vr(reg, 4)}, %[kl] offset:{so + 9216 * kb + 32 * kk}", "lds",
+        items.append(Ins(f"ds_read_b128 {vr(reg, 4)}, {kbase(nst, kk)} offset:{kofs(nst, kb, kk)}", "lds",
                          wr=vset(reg, 4), after=32 + mm + 2, name=f"K{mm}"))
     return items
 
@@ -314,7 +326,7 @@ def dma(st):
     for jx in range(9):
         if jx < 5:
             off = st * KST + 4096 * jx
-            lw = "%[lw4]" if jx == 4 else "%[lw]"
+            lw = "%[lw]"
             rs = "%[rk]"
         else:
             off = V_REGION + st * VST + 4096 * (jx - 5)
@@ -407,9 +419,13 @@ def schedule(mf, streams, prio_order, end_items):
             return None
         return it, h
 
+    gap_lds = [0]
+
     def emit(it):
         nonlocal t, mfree
         out.append(it)
+        if it.kind == "lds":
+            gap_lds[0] += 1
         emitted_names.add(it.name)
         if it.kind == "mfma":
             st = max(t, mfree)
@@ -431,6 +447,10 @@ def schedule(mf, streams, prio_order, end_items):
                       and streams[s][heads[s]].deadline <= k]
             if k < len(mf) and not urgent:
                 cands = [c for c in cands if t + 4 * c[3].slots <= mfree]
+            # at most LDS_PER_GAP LDS reads in one MFMA shadow: bursts fill the
+            # CU's LDS command queue and stall issue
+            if not urgent:
+                cands = [c for c in cands if c[3].kind != "lds" or gap_lds[0] < LDS_PER_GAP]
             if not cands:
                 if urgent:
                     # an urgent item waits for a hazard: pad
@@ -465,6 +485,7 @@ def schedule(mf, streams, prio_order, end_items):
         if h > 0:
             emit(nop(h - 1))
         emit(mf[k])
+        gap_lds[0] = 0
         n_mfma += 1
     # drain leftovers (past the last MFMA)
     left = True
@@ -497,9 +518,9 @@ def build_iteration(st, h_split, lab):
     # barrier after all V reads have landed; DMA of tile i+4 into this stage and
     # the K(t+1) reads after it
     vr_ = v_reads(st)
-    bar = Ins("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier", "sync", after=35, slots=2, name="bar")
+    bar = Ins("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier", "sync", after=36, slots=2, name="bar")
     bar.deps = [vr_[-1]]
-    bar.fixed_deadline = 48
+    bar.fixed_deadline = 40
     kr = k_reads(st)
     for it in kr:
         it.deps = [bar]
@@ -605,14 +626,29 @@ def main():
     out.write("\n")
     # the QB1 sum of the (absent) tile before the first: its tail part runs in
     # the first iteration on scores of -inf
+    # Registers start as the state after a tile -1 with no admitted key: O, P1
+    # and the V^T operands 0, the QB1 scores -inf (their exps in the first
+    # tile's stream give 0), the QB1 partial sum 0. Tuples are filled by MFMAs
+    # of constant operands (one issue slot per 16 registers): zeros times
+    # zeros, and bf16 -inf times bf16 ones. The score MFMAs go first, so that
+    # the first VALU reads of S1 / P1 lie more than 12 wait states later.
+    z, ni, one = vr(T0, 4), vr(TEMPS[1][0][0], 4), vr(80, 4)
     pro = [f"s_mov_b32 s{SI}, 0", f"v_mov_b32 v{LT[1]}, 0"]
-    pro += [f"v_accvgpr_write_b32 a{x}, 0" for x in range(128)]
-    pro += [f"v_accvgpr_write_b32 a{V_BASE + x}, 0" for x in range(64)]
-    pro += [f"v_mov_b32 v{S_BASE[1] + e}, {NEG_INF}" for e in range(32)]
-    pro += [f"v_mov_b32 v{P_BASE[1] + x}, 0" for x in range(16)]
+    pro += [f"v_mov_b32 v{T0 + x}, 0" for x in range(4)]
+    pro += [f"v_mov_b32 v{TEMPS[1][0][0] + x}, 0xff80ff80" for x in range(4)]
+    pro += [f"v_mov_b32 v{80 + x}, 0x3f803f80" for x in range(4)]
+    pro += ["s_nop 2"]
+    pro += [f"{MF} {vr(S_BASE[1], 16)}, {ni}, {one}, 0", f"{MF} {vr(S_BASE[1] + 16, 16)}, {ni}, {one}, 0",
+            f"{MF} {vr(P_BASE[1], 16)}, {z}, {z}, 0"]
+    kreads = []
     for mm in range(16):
         kk, kb = divmod(mm, 2)
-        pro.append(f"ds_read_b128 {vr(K_BASE + 32 * kb + 4 * kk, 4)}, %[kl] offset:{9216 * kb + 32 * kk}")
+        kreads.append(f"ds_read_b128 {vr(K_BASE + 32 * kb + 4 * kk, 4)}, {kbase(0, kk)} offset:{kofs(0, kb, kk)}")
+    zero = [f"{MF} {ar(16 * x, 16)}, {z}, {z}, 0" for x in range(8)]
+    zero += [f"{MF} {ar(V_BASE + 16 * x, 16)}, {z}, {z}, 0" for x in range(4)]
+    for x in range(12):
+        pro.append(zero[x])
+        pro += kreads[x * 16 // 12:(x + 1) * 16 // 12]
     out.write("#define SFA_FWD128_PROLOGUE \\\n")
     for ln in pro:
         out.write(f'  "{ln}\\n" \\\n')
