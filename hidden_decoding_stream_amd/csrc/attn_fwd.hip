@@ -102,6 +102,9 @@ struct FwdParams {
   int32_t per_xcd;   // ceil(total / 8)
   uint32_t q_bytes;  // buffer sizes (<= 2^31) for out-of-range checks
   uint32_t kv_bytes;
+  // divisions of the work-item decode (attn_fwd128_kernel): by nqb * hgroups,
+  // hgroups, hkv and nseq
+  FastDiv f_ipu, f_hg, f_hkv, f_nseq;
   unsigned long long* trace;   // trace build only (SFA_PREFILL_TRACE): 8 words per work item
 };
 
@@ -874,6 +877,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
 // extra, fully masked, tile so that the last tile's QB1 P V runs in the same
 // stream; rows past the end of a sequence load the next rows of the buffer
 // (or zeros past its end), which the causal mask excludes.
+// Mask word of a lane whose admitted keys in a 64-key tile are the offsets
+// lo..hi: bit 16 kb + 4 g + r is set when the key of score register 4 g + r
+// of key block kb, offset 32 kb + reg_key_offset(g, hh) + r, is admitted.
+// Those offsets come in runs of 4, so the word is the 64-bit run mask with
+// its nibbles permuted: lane half 0 reads nibbles 0 2 1 3 of each 32-key
+// block, half 1 nibbles 5 7 4 6.
+__device__ __forceinline__ uint32_t tile_mask_word(int lo, int hi, int hh) {
+  lo = max(lo, 0);
+  hi = min(hi, BN - 1);
+  const uint64_t m = hi < lo ? 0ull : (~0ull >> (63 - hi)) & (~0ull << lo);
+  uint32_t w = 0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const uint32_t x = uint32_t(m >> (32 * kb));
+    uint32_t o;
+    if (hh == 0) {
+      o = (x & 0xF00Fu) | ((x >> 4) & 0xF0u) | ((x << 4) & 0xF00u);
+    } else {
+      const uint32_t y = x >> 16;
+      o = ((y >> 4) & 0xFu) | ((y >> 8) & 0xF0u) | ((y & 0xFu) << 8) | ((y << 4) & 0xF000u);
+    }
+    w |= o << (16 * kb);
+  }
+  return w;
+}
+
 constexpr int kW128 = 4;
 constexpr int kKStage128 = 20480;         // LDS bytes per K stage (64 rows of 320)
 constexpr int kVStage128 = 16384;         // per V stage
@@ -894,15 +923,15 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
   // ---- work item: (batch, stream, kv head, query block, head group) ----
   const int t = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
   if (t >= p.total) return;
-  const int ipu = p.nqb * p.hgroups;
-  const int unit = t / ipu;
-  const int rr = t - unit * ipu;
-  const int qb = p.nqb - 1 - rr / p.hgroups;
-  const int hg = rr % p.hgroups;
-  const int kvh = unit % p.hkv;
-  const int bs = unit / p.hkv;
-  const int sq = p.sq0 + bs % p.nseq;
-  const int b = bs / p.nseq;
+  const int unit = int(fdiv(uint32_t(t), p.f_ipu));
+  const int rr = t - unit * int(p.f_ipu.d);
+  const int rq = int(fdiv(uint32_t(rr), p.f_hg));
+  const int qb = p.nqb - 1 - rq;
+  const int hg = rr - rq * p.hgroups;
+  const int bs = int(fdiv(uint32_t(unit), p.f_hkv));
+  const int kvh = unit - bs * p.hkv;
+  const int b = int(fdiv(uint32_t(bs), p.f_nseq));
+  const int sq = p.sq0 + bs - b * p.nseq;
   const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
   const int PS = (kW128 / p.HG) * 64;
   const int wg_q0 = qb * PS;
@@ -935,7 +964,7 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
       __builtin_memcpy(reinterpret_cast<char*>(&qv[j]) + kk * 16, &x, 16);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // (the Q loads complete with the first tile, at the wait before the loop)
 
   // ---- DMA chunks of this wave: K chunks w + 4j (j < 5), V chunks w + 4(j - 5) ----
   // A K row is 20 slots of 16 bytes: slot u < 16 holds data chunk
@@ -999,20 +1028,10 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       sp[j][k] = cand[k] >= kt_begin && cand[k] < kt_end ? uint32_t(cand[k] - kt_begin) : 0xffffffffu;
-      uint32_t w = 0;
-      if (cand[k] >= 0) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = cand[k] * BN + kb * 32 + reg_key_offset(g, hh) + r;
-              const bool ok = key <= vq && (window == 0 || vq - key < window);
-              w |= uint32_t(ok) << (kb * 16 + 4 * g + r);
-            }
-      }
-      mk[j][k] = w;
+      // the lane's admitted keys of the tile, as offsets from its first key
+      const int hi = vq - cand[k] * BN;
+      const int lo = window > 0 ? hi - window + 1 : 0;
+      mk[j][k] = cand[k] >= 0 ? tile_mask_word(lo, hi, hh) : 0u;
     }
   }
 #pragma unroll
@@ -1067,7 +1086,7 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
         [mk00] "v"(mk[0][0]), [mk01] "v"(mk[0][1]), [mk02] "v"(mk[0][2]), [mk10] "v"(mk[1][0]),
         [mk11] "v"(mk[1][1]), [mk12] "v"(mk[1][2]), [ke0] "v"(ke0), [ko0] "v"(ko0), [ke1] "v"(ke1), [ko1] "v"(ko1), [ve0] "v"(ve[0]), [ve1] "v"(ve[1]),
         [ve2] "v"(ve[2]), [ve3] "v"(ve[3]), [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3])
-      : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", SFA_FWD128_CLOBBER_V,
+      : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91", SFA_FWD128_CLOBBER_V,
         SFA_FWD128_CLOBBER_A);
 
   // ---- epilogue: O = O^T / l, bf16; optional natural-log LSE ----
@@ -1159,6 +1178,10 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   const int64_t total = int64_t(a.batch) * p.nseq * p.hkv * p.nqb * p.hgroups;
   p.total = int32_t(total);
   p.per_xcd = int32_t((total + 7) / 8);
+  p.f_ipu = make_fastdiv(uint32_t(p.nqb * p.hgroups));
+  p.f_hg = make_fastdiv(uint32_t(p.hgroups));
+  p.f_hkv = make_fastdiv(uint32_t(p.hkv));
+  p.f_nseq = make_fastdiv(uint32_t(p.nseq));
   p.q_bytes = uint32_t(a.batch * p.QS * a.hq * a.d * 2);
   p.kv_bytes = uint32_t(a.batch * S * a.hkv * a.d * 2);
   const dim3 grid(uint32_t(p.per_xcd) * 8u);

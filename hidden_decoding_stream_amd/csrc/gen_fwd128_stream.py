@@ -42,6 +42,8 @@ LT = [88, 89]
 T0, T1, T2, T3, T4 = 90, 91, 92, 93, 94
 SI, SX = 84, [85, 86]       # loop counter, mask-check scratch per QB
 SINC, STMP, SRET = 88, 87, 89
+SSKIP = 90                  # s[90:91]: lanes whose O needs the rescale
+M_INIT = "0xf149f2ca"       # -1e30f, the reference max before any admitted key
 LDS_PER_GAP = int(__import__("os").environ.get("LDS_PER_GAP", "2"))   # LDS reads per MFMA shadow
 
 KST = 20480      # bytes per K stage (64 rows of 320: 16 chunks of 16 bytes, swizzled, and 4 pad slots)
@@ -221,11 +223,17 @@ def slow_block(j, lab):
     b.append(Ins(f"v_add_f32 v{T1}, 0x41000000, {m}", rd={m}, wr={f"v{T1}"}))
     b.append(Ins(f"v_cmp_gt_f32 vcc, v{T0}, v{T1}", rd={f"v{T0}", f"v{T1}"}, wr={"vcc"}))
     b.append(Ins(f"s_cbranch_vccz {lab}_ret", "salu", rd={"vcc"}))
+    # O needs no rescale where m was still its initial -1e30 (no key admitted
+    # yet, so O is 0): skip it when that holds for every lane raising m
+    b.append(Ins(f"v_mov_b32 v{T4}, {M_INIT}", wr={f"v{T4}"}))
+    b.append(Ins(f"v_cmp_lg_f32 s[{SSKIP}:{SSKIP + 1}], v{T4}, {m}\n\ts_and_b64 s[{SSKIP}:{SSKIP + 1}], "
+                 f"s[{SSKIP}:{SSKIP + 1}], vcc", rd={f"v{T4}", m, "vcc"}))
     b.append(Ins(f"v_sub_f32 v{T2}, {m}, v{T0}", rd={m, f"v{T0}"}, wr={f"v{T2}"}))
     b.append(Ins(f"v_exp_f32 v{T2}, v{T2}", "trans", rd={f"v{T2}"}, wr={f"v{T2}"}, slots=2))
     b.append(Ins(f"v_cndmask_b32 {m}, {m}, v{T0}, vcc", rd={m, f"v{T0}", "vcc"}, wr={m}))
     b.append(Ins(f"v_cndmask_b32 v{T2}, 1.0, v{T2}, vcc", rd={f"v{T2}", "vcc"}, wr={f"v{T2}"}))
     b.append(Ins(f"v_mul_f32 {l}, {l}, v{T2}", rd={l, f"v{T2}"}, wr={l}))
+    b.append(Ins(f"s_cbranch_scc0 {lab}_x", "salu"))
     ob = O_BASE[j]
     for x in range(0, 64, 2):
         b.append(Ins(f"v_accvgpr_read_b32 v{T3}, a{ob + x}", rd={f"a{ob + x}"}, wr={f"v{T3}"}))
@@ -234,6 +242,7 @@ def slow_block(j, lab):
         b.append(Ins(f"v_mul_f32 v{T4}, v{T4}, v{T2}", rd={f"v{T4}", f"v{T2}"}, wr={f"v{T4}"}))
         b.append(Ins(f"v_accvgpr_write_b32 a{ob + x}, v{T3}", rd={f"v{T3}"}, wr={f"a{ob + x}"}))
         b.append(Ins(f"v_accvgpr_write_b32 a{ob + x + 1}, v{T4}", rd={f"v{T4}"}, wr={f"a{ob + x + 1}"}))
+    b.append(Ins(f"{lab}_x:", "label"))
     b += exps(j, range(16), True, LT[j])
     b += ret_dispatch(lab)
     return b
