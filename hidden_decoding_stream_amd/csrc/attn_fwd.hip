@@ -923,6 +923,17 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
   // ---- work item: (batch, stream, kv head, query block, head group) ----
   const int t = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
   if (t >= p.total) return;
+#ifdef SFA_PREFILL_TRACE
+  if (tid == 0 && p.trace) {
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    p.trace[size_t(t) * 8 + 4] = hw;
+    p.trace[size_t(t) * 8 + 5] = xcc;
+    p.trace[size_t(t) * 8 + 6] = blockIdx.x;
+  }
+#endif
+  SFA_TRACE_AT(0);
   const int unit = int(fdiv(uint32_t(t), p.f_ipu));
   const int rr = t - unit * int(p.f_ipu.d);
   const int rq = int(fdiv(uint32_t(rr), p.f_hg));
@@ -1065,6 +1076,7 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
 
   // tile 0 landed for every wave
   asm volatile("s_waitcnt vmcnt(27)\n\ts_barrier" ::: "memory");
+  SFA_TRACE_AT(1);
 
   typedef float f32x32 __attribute__((ext_vector_type(32)));
   f32x32 o0a, o0b, o1a, o1b;
@@ -1072,7 +1084,7 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
   asm volatile(
       SFA_FWD128_PROLOGUE
       SFA_FWD128_LOOP
-      "s_waitcnt vmcnt(0) lgkmcnt(0)\n"
+      "s_waitcnt lgkmcnt(0)\n"
       "s_nop 7\n"
       "s_nop 7\n"
       : [o0a] "={a[0:31]}"(o0a), [o0b] "={a[32:63]}"(o0b), [o1a] "={a[64:95]}"(o1a), [o1b] "={a[96:127]}"(o1b),
@@ -1088,6 +1100,11 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
         [ve2] "v"(ve[2]), [ve3] "v"(ve[3]), [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3])
       : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91", SFA_FWD128_CLOBBER_V,
         SFA_FWD128_CLOBBER_A);
+
+  SFA_TRACE_AT(2);
+#ifdef SFA_PREFILL_TRACE
+  if (tid == 0 && p.trace) p.trace[size_t(t) * 8 + 7] = uint32_t(T);
+#endif
 
   // ---- epilogue: O = O^T / l, bf16; optional natural-log LSE ----
   const f32x32 oh[2][2] = {{o0a, o0b}, {o1a, o1b}};
@@ -1113,6 +1130,11 @@ __global__ __launch_bounds__(64 * kW128, 1) void attn_fwd128_kernel(FwdParams p)
     if (p.lse && hh == 0)
       p.lse[((size_t)b * p.hq + h) * p.QS + (prow - (size_t)b * p.QS)] = (mm[j] + log2f(lt)) * kLn2;
   }
+  // The tile loop ends with DMA of the tiles past the last still in flight
+  // (they write no stage a read still needs); the wave waits for them only
+  // now, behind the epilogue, and before it ends and its LDS is released.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  SFA_TRACE_AT(3);
 }
 
 }  // namespace
