@@ -353,7 +353,7 @@ def trace_prefill(torch, sfa, I, dev, reps=3):
       busy_share     sum of item durations / (CUs x span)
       gap_share      idle time between consecutive items on a CU / (CUs x span)
       tail_share     idle time after a CU's last item / (CUs x span)
-      prologue_share (first tiles landed - start) / busy: Q load and the first two tiles' DMA
+      prologue_share (first tiles landed - start) / busy: Q load and the first tiles' DMA
       epilogue_share (end - tile loop end) / busy: normalisation and the output stores
       fit_us_per_tile, fit_us_fixed: least squares of item duration against its key tiles.
     Printed as one JSON line per launch."""
