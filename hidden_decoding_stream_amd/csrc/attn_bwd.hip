@@ -39,6 +39,7 @@
 // inside those blocks (dkdv_block128, DkdvAsm, DqAsm).
 #include <math.h>
 
+#include "attn_dq128_stream.h"
 #include "common.h"
 #include "launch.h"
 
@@ -1625,6 +1626,189 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// dQ at d = 128, intra and cross_full: one wave per SIMD with 64 queries (two
+// blocks of 32) of one query head, so that every K / V row read from LDS
+// feeds twice as many MFMAs as in bwd_dq_kernel. The work group's 4 waves
+// share the key tiles: HG query heads of one key/value head times 4 / HG
+// blocks of 64 queries. The tile loop is one asm stream (attn_dq128_stream.h,
+// written by gen_dq128_stream.py): per 64-key tile, S^T = K Q^T and
+// dP^T = V dO^T for each 32-key block, dS^T = exp2(S^T c - lse2) (dP^T - D)
+// in place, rounded to bf16, and dQ^T += K^T dS^T one key block behind.
+// Products, their accumulation order and the rounding of dS are those of
+// bwd_dq_kernel. K and V tiles go by DMA through 3 stages (tile t + 2 while
+// t runs), in the rows of 320 bytes of the d = 128 dK/dV tiles (row reads
+// and transposed reads free of bank conflicts). Tiles up to the diagonal of
+// the wave's queries are full; the diagonal one takes the lanes' mask words,
+// later ones (other waves' queries, and the extra tile that closes the
+// stream) are masked whole.
+// ---------------------------------------------------------------------------
+constexpr int kDqStage = 20480;                // bytes per K (or V) stage
+constexpr int kDqVRegion = 3 * kDqStage;       // V stages after the 3 K stages
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq128_kernel(BwdParams p) {
+  constexpr int D = 128;
+  static_assert(kDqStage == kTileBytes128, "the stream's stage offsets assume 20480-byte tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[6 * kDqStage];
+
+  const int pstride = MODE == 0 ? p.pstride : 1;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  // work item: (batch, virtual sequence, kv head, query block, head group), heaviest first
+  const int t = (blockIdx.x & 7) * p.per_xcd_q + (blockIdx.x >> 3);
+  if (t >= p.total_q) return;
+  const int ipu = p.nqb * p.hgroups;
+  const int unit = t / ipu;
+  const int rr = t - unit * ipu;
+  const int qb = p.nqb - 1 - rr / p.hgroups;
+  const int hg = rr % p.hgroups;
+  const int kvh = unit % p.hkv;
+  const int bs = unit / p.hkv;
+  const int sq = bs % p.nseq;
+  const int b = bs / p.nseq;
+  const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
+  const int PS = (kWaves / p.HG) * 64;
+  const int wg_q0 = qb * PS;
+  const int q0 = wg_q0 + (wave / p.HG) * 64;
+  const int wg_qlast = min(wg_q0 + PS, p.Lv) - 1;
+  const int T = wg_qlast / BT + 1;
+  const int base_row = b * p.S + sq;
+
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t dors = make_rsrc(p.dout, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lsed, p.lsed_bytes);
+  const uint32_t kv_pos_bytes = uint32_t(p.hkv) * D * 2;
+  const uint32_t kv_head_bytes = uint32_t(kvh) * D * 2;
+  const uint32_t tstride = uint32_t(BT * pstride) * kv_pos_bytes;   // bytes between tiles
+
+  // Q^T and dO^T (B operands: lane holds row q0 + 32 j + l32, d = 16 kk + 8 hh .. + 8),
+  // and the lane's query lse2 and D
+  typedef __bf16 bf16x64 __attribute__((ext_vector_type(64)));
+  bf16x64 qv[2], dv[2];
+  float lse2[2], dd[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int vq = q0 + 32 * j + l32;
+    const bool ok = vq < p.Lv;
+    const uint32_t off = (uint32_t(base_row + vq * pstride) * p.hq + h) * D * 2 + 16 * hh + (ok ? 0u : kOobOffset);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 x = bload16(qrs, off + kk * 32);
+      __builtin_memcpy(reinterpret_cast<char*>(&qv[j]) + kk * 16, &x, 16);
+      const uint4 y = bload16(dors, off + kk * 32);
+      __builtin_memcpy(reinterpret_cast<char*>(&dv[j]) + kk * 16, &y, 16);
+    }
+    const uint32_t li = ((uint32_t(b * p.nseq + sq) * p.hq + h) * p.Lv + vq) * 8 + (ok ? 0u : kOobOffset);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(lrs, int(li), 0, 0);
+    lse2[j] = __uint_as_float(x[0]);
+    dd[j] = __uint_as_float(x[1]);
+  }
+
+  // DMA chunks of this wave: chunk w + 4 x (x < 5) of the K tile and the same
+  // chunk of the V tile. Slot sl = 64 chunk + lane is 16-byte slot u = sl mod 20
+  // of row sl / 20, holding data chunk u ^ row_swizzle128(row / 4); slots 16-19
+  // are padding (zeros).
+  uint32_t cf[5];
+#pragma unroll
+  for (int x = 0; x < 5; ++x) {
+    const int sl = (wave + 4 * x) * 64 + lane;
+    const int row = sl / 20, u = sl % 20;
+    cf[x] = u >= 16 ? kOobOffset
+                    : uint32_t(row * pstride) * kv_pos_bytes + kv_head_bytes + (u ^ row_swizzle128(row >> 2)) * 16;
+  }
+  auto tile_base = [&](int kt) { return uint32_t(base_row + kt * BT * pstride) * kv_pos_bytes; };
+  // tile 0 into stage 0, zeros into the K tile of stage 2 (the first iteration
+  // reads its K^T as that of a tile -1, whose dS are 0), tile 1 into stage 1
+#pragma unroll
+  for (int x = 0; x < 5; ++x) {
+    const uint32_t o0 = cf[x] < kOobOffset ? cf[x] + tile_base(0) : kOobOffset;
+    dma16(krs, &lds[(wave + 4 * x) * 1024], o0);
+    dma16(vrs, &lds[kDqVRegion + (wave + 4 * x) * 1024], o0);
+  }
+#pragma unroll
+  for (int x = 0; x < 5; ++x) dma16(krs, &lds[2 * kDqStage + (wave + 4 * x) * 1024], kOobOffset);
+#pragma unroll
+  for (int x = 0; x < 5; ++x) {
+    const uint32_t o1 = (1 < T && cf[x] < kOobOffset) ? cf[x] + tile_base(1) : kOobOffset;
+    dma16(krs, &lds[kDqStage + (wave + 4 * x) * 1024], o1);
+    dma16(vrs, &lds[kDqVRegion + kDqStage + (wave + 4 * x) * 1024], o1);
+  }
+  // the loop's first DMA is tile 2
+#pragma unroll
+  for (int x = 0; x < 5; ++x) cf[x] = (2 < T && cf[x] < kOobOffset) ? cf[x] + tile_base(2) : kOobOffset;
+
+  // LDS read bases: rows of a 32-row block in the sigma order (chunks 2 kk + hh:
+  // even kk from ke, odd from ko, plus 64 (kk / 2)); transposed reads for
+  // (t, jj) from t<t><jj>, plus 64 db; stages and key blocks at immediate offsets
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  const int ra = sigma(l32), rsw = row_swizzle128(ra >> 2);
+  const uint32_t rb = lds0 + uint32_t(ra * kRowBytes128 + 16 * (hh ^ (rsw & 1)));
+  const uint32_t ke = rb + 32 * (rsw >> 1), ko = rb + 32 - 32 * (rsw >> 1);
+  const uint32_t ve = ke + kDqVRegion, vo = ko + kDqVRegion;
+  uint32_t tr[4];
+  {
+    const int grp = lane >> 4, gi = lane & 15, vh = grp >> 1, e = gi >> 2;
+    const int c0 = 2 * (grp & 1) + ((gi & 3) >> 1), half = gi & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = i & 1, jj = i >> 1;
+      const int ro = jj ? 12 * vh + 4 + 8 * tt : 20 * vh + 8 * tt;
+      tr[i] = lds0 + uint32_t((e + ro) * kRowBytes128 + 16 * (c0 ^ row_swizzle128(ro >> 2)) + 8 * half);
+    }
+  }
+  const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(wave) * 1024);
+  const uint32_t Tn = __builtin_amdgcn_readfirstlane(uint32_t(T));
+  // the wave's diagonal tile and the lanes' admitted keys in it
+  const uint32_t dtl = __builtin_amdgcn_readfirstlane(uint32_t(q0 / BT));
+  const uint32_t mk0 = tile_mask_word(0, l32, hh), mk1 = tile_mask_word(0, 32 + l32, hh);
+
+  // tile 0 and the zeros landed for every wave (tile 1 may still be in flight)
+  asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+
+  typedef float f32x32 __attribute__((ext_vector_type(32)));
+  f32x32 d0a, d0b, d1a, d1b;
+  asm volatile(
+      SFA_DQ128_PROLOGUE
+      SFA_DQ128_LOOP
+      "s_waitcnt lgkmcnt(0)\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      : [d0a] "={a[0:31]}"(d0a), [d0b] "={a[32:63]}"(d0b), [d1a] "={a[64:95]}"(d1a), [d1b] "={a[96:127]}"(d1b),
+        [cf0] "+v"(cf[0]), [cf1] "+v"(cf[1]), [cf2] "+v"(cf[2]), [cf3] "+v"(cf[3]), [cf4] "+v"(cf[4])
+      : [q0] "{a[128:159]}"(qv[0]), [q1] "{a[160:191]}"(qv[1]), [o0] "{a[192:223]}"(dv[0]),
+        [o1] "{a[224:255]}"(dv[1]), [c] "s"(p.c), [T] "s"(Tn), [tstride] "s"(tstride), [rk] "s"(krs),
+        [rv] "s"(vrs), [lw] "s"(lw), [dtl] "s"(dtl), [l0] "v"(lse2[0]), [l1] "v"(lse2[1]), [d0] "v"(dd[0]),
+        [d1] "v"(dd[1]), [mk0] "v"(mk0), [mk1] "v"(mk1), [ke] "v"(ke), [ko] "v"(ko), [ve] "v"(ve), [vo] "v"(vo),
+        [t00] "v"(tr[0]), [t10] "v"(tr[1]), [t01] "v"(tr[2]), [t11] "v"(tr[3])
+      : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", SFA_DQ128_CLOBBER_V);
+
+  const f32x32 dh[2][2] = {{d0a, d0b}, {d1a, d1b}};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int vq = q0 + 32 * j + l32;
+    if (vq >= p.Lv) continue;
+    u16* orow = p.dq + (size_t(base_row + vq * pstride) * p.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 ov;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(dh[j][db >> 1][(db & 1) * 16 + 4 * g + r] * p.scale);
+        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hh) = ov;
+      }
+  }
+  // the DMA of the tiles past the last is still in flight: wait before the
+  // work group ends and its LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 size_t round_up(size_t x, size_t q) { return (x + q - 1) / q * q; }
 
 }  // namespace
@@ -1663,7 +1847,9 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
   p.window = (a.mode == 2 && a.window < S) ? int32_t(a.window) : 0;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
-  const int PS = (kWaves / p.HG) * 32;
+  // dQ at d = 128 without a window: 64 queries per wave (bwd_dq128_kernel), else 32
+  const bool dq128 = a.d == 128 && !(a.mode == 2 && p.window > 0);
+  const int PS = (kWaves / p.HG) * (dq128 ? 64 : 32);
   p.nqb = (p.Lv + PS - 1) / PS;
   p.nkb = (p.Lv + kWaves * 32 - 1) / (kWaves * 32);
   const int64_t units = int64_t(a.batch) * p.nseq * p.hkv;
@@ -1691,7 +1877,10 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL(bwd_prep_kernel<64>, pgrid, dim3(256), 0, stream, p);
   hipLaunchKernelGGL(kDkdv[di][kind], kgrid, dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(kDq[di][kind], qgrid, dim3(kThreads), 0, stream, p);
+  if (dq128)
+    hipLaunchKernelGGL(kind == 0 ? bwd_dq128_kernel<0> : bwd_dq128_kernel<1>, qgrid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(kDq[di][kind], qgrid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -877,32 +877,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
 // extra, fully masked, tile so that the last tile's QB1 P V runs in the same
 // stream; rows past the end of a sequence load the next rows of the buffer
 // (or zeros past its end), which the causal mask excludes.
-// Mask word of a lane whose admitted keys in a 64-key tile are the offsets
-// lo..hi: bit 16 kb + 4 g + r is set when the key of score register 4 g + r
-// of key block kb, offset 32 kb + reg_key_offset(g, hh) + r, is admitted.
-// Those offsets come in runs of 4, so the word is the 64-bit run mask with
-// its nibbles permuted: lane half 0 reads nibbles 0 2 1 3 of each 32-key
-// block, half 1 nibbles 5 7 4 6.
-__device__ __forceinline__ uint32_t tile_mask_word(int lo, int hi, int hh) {
-  lo = max(lo, 0);
-  hi = min(hi, BN - 1);
-  const uint64_t m = hi < lo ? 0ull : (~0ull >> (63 - hi)) & (~0ull << lo);
-  uint32_t w = 0;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const uint32_t x = uint32_t(m >> (32 * kb));
-    uint32_t o;
-    if (hh == 0) {
-      o = (x & 0xF00Fu) | ((x >> 4) & 0xF0u) | ((x << 4) & 0xF00u);
-    } else {
-      const uint32_t y = x >> 16;
-      o = ((y >> 4) & 0xFu) | ((y >> 8) & 0xF0u) | ((y & 0xFu) << 8) | ((y << 4) & 0xF000u);
-    }
-    w |= o << (16 * kb);
-  }
-  return w;
-}
-
 constexpr int kW128 = 4;
 constexpr int kKStage128 = 20480;         // LDS bytes per K stage (64 rows of 320)
 constexpr int kVStage128 = 16384;         // per V stage

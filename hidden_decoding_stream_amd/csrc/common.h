@@ -97,6 +97,32 @@ __device__ __forceinline__ int sigma(int m) {
   constexpr uint32_t kSigmaG = 0x63417250u;  // m>>2 = 0..7 -> 0 5 2 7 1 4 3 6 (nibbles, lowest first)
   return 4 * int((kSigmaG >> (4 * (m >> 2))) & 7u) + (m & 3);
 }
+// Mask word of a lane whose admitted keys in a 64-key tile are the offsets
+// lo..hi: bit 16 kb + 4 g + r is set when the key of score register 4 g + r
+// of key block kb, offset 32 kb + reg_key_offset(g, hh) + r, is admitted.
+// Those offsets come in runs of 4, so the word is the 64-bit run mask with
+// its nibbles permuted: lane half 0 reads nibbles 0 2 1 3 of each 32-key
+// block, half 1 nibbles 5 7 4 6.
+__device__ __forceinline__ uint32_t tile_mask_word(int lo, int hi, int hh) {
+  lo = max(lo, 0);
+  hi = min(hi, 63);
+  const uint64_t m = hi < lo ? 0ull : (~0ull >> (63 - hi)) & (~0ull << lo);
+  uint32_t w = 0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const uint32_t x = uint32_t(m >> (32 * kb));
+    uint32_t o;
+    if (hh == 0) {
+      o = (x & 0xF00Fu) | ((x >> 4) & 0xF0u) | ((x << 4) & 0xF00u);
+    } else {
+      const uint32_t y = x >> 16;
+      o = ((y >> 4) & 0xFu) | ((y >> 8) & 0xF0u) | ((y & 0xFu) << 8) | ((y << 4) & 0xF000u);
+    }
+    w |= o << (16 * kb);
+  }
+  return w;
+}
+
 // LDS banks on gfx950: 64 banks of 4 bytes. A 16-byte read (ds_read_b128) is
 // served in four passes of 16 lanes: within each half-wave, the lanes whose
 // quad index (lane / 4 mod 8) has the same parity; 8-byte reads (ds_read_b64,
