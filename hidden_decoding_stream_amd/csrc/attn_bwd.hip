@@ -39,6 +39,7 @@
 // inside those blocks (dkdv_block128, DkdvAsm, DqAsm).
 #include <math.h>
 
+#include "attn_dkdv128_stream.h"
 #include "attn_dq128_stream.h"
 #include "common.h"
 #include "launch.h"
@@ -1627,6 +1628,220 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV at d = 128, intra and cross_full: the work items, tile layout and
+// products of bwd_dkdv128_kernel, with the whole step loop as one asm stream
+// (attn_dkdv128_stream.h, written by gen_dkdv128_stream.py), so that no
+// compiled code runs between blocks: the DMA offsets advance by per-step
+// increments, the (lse2, D) pairs of a step come by DMA too (each wave moves
+// 16 queries' pairs, into a KiB of its own), and the masks are per-lane words
+// formed once (the first two query tiles hold the diagonal, a ragged last
+// tile masks the queries past the end; the step after the last, which
+// closes the stream, is masked whole). Rows past the end of a sequence load
+// the next rows of the buffer (or zeros past its end), which those masks
+// exclude.
+// ---------------------------------------------------------------------------
+constexpr int kKvTile = 20480;                 // bytes of a Q (or dO) tile
+constexpr int kKvDRegion = 3 * kKvTile;        // the 3 dO tiles follow the 3 Q tiles
+constexpr int kKvLRegion = 6 * kKvTile;        // then the pairs, 4 KiB per stage
+constexpr int kKvLStage = 4096;
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdParams p) {
+  constexpr int D = 128;
+  constexpr int KB = kWaves * 32;                      // keys per work group
+  static_assert(kKvTile == kTileBytes128, "the stream's offsets assume 20480-byte tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kKvLRegion + 3 * kKvLStage];
+
+  const int pstride = MODE == 0 ? p.pstride : 1;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  // work item: (batch, virtual sequence, kv head, key block), heaviest first
+  const int t = (blockIdx.x & 7) * p.per_xcd_k + (blockIdx.x >> 3);
+  if (t >= p.total_k) return;
+  const int unit = t / p.nkb;
+  const int kbk = t - unit * p.nkb;
+  const int kvh = unit % p.hkv;
+  const int bs = unit / p.hkv;
+  const int sq = bs % p.nseq;
+  const int b = bs / p.nseq;
+  const int base_row = b * p.S + sq;
+  const int wg_k0 = kbk * KB;
+  const int k0 = wg_k0 + wave * 32;
+  const int vk = k0 + l32;
+  const bool kvalid = vk < p.Lv;
+  const int qt_begin = wg_k0 / BT;
+  const int qt_end = (p.Lv - 1) / BT + 1;
+  const int G = p.G;
+  const int T = (qt_end - qt_begin) * G;               // steps: (query tile, head of the group)
+
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t dors = make_rsrc(p.dout, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lsed, p.lsed_bytes);
+  const uint32_t q_pos_bytes = uint32_t(p.hq) * D * 2;
+  const uint32_t lbase_seq = uint32_t(b * p.nseq + sq) * p.hq;
+
+  // K^T and V^T (B operands: lane holds row vk, d = 16 kk + 8 hh .. + 8)
+  typedef __bf16 bf16x64 __attribute__((ext_vector_type(64)));
+  bf16x64 kf, vf;
+  {
+    const uint32_t off = (uint32_t(base_row + vk * pstride) * p.hkv + kvh) * D * 2 + 16 * hh +
+                         (kvalid ? 0u : kOobOffset);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 x = bload16(krs, off + kk * 32);
+      __builtin_memcpy(reinterpret_cast<char*>(&kf) + kk * 16, &x, 16);
+      const uint4 y = bload16(vrs, off + kk * 32);
+      __builtin_memcpy(reinterpret_cast<char*>(&vf) + kk * 16, &y, 16);
+    }
+  }
+
+  // DMA chunks of this wave: chunk w + 4 x (x < 5) of the Q tile and the same
+  // chunk of the dO tile (slot sl = 64 chunk + lane is 16-byte slot u = sl mod 20
+  // of row sl / 20, holding data chunk u ^ row_swizzle128(row / 4); slots 16-19
+  // padding), and the pairs of queries 16 w .. 16 w + 15 (lanes 0-7, 16 bytes each)
+  uint32_t cf[5];
+#pragma unroll
+  for (int x = 0; x < 5; ++x) {
+    const int sl = (wave + 4 * x) * 64 + lane;
+    const int row = sl / 20, u = sl % 20;
+    cf[x] = u >= 16 ? kOobOffset : uint32_t(row * pstride) * q_pos_bytes + (u ^ row_swizzle128(row >> 2)) * 16;
+  }
+  auto step_base = [&](int s) {
+    const int qt = qt_begin + s / G, h = kvh * G + s % G;
+    return uint32_t(base_row + qt * BT * pstride) * q_pos_bytes + uint32_t(h) * D * 2;
+  };
+  auto pair_off = [&](int s) {
+    const int qt = qt_begin + s / G, h = kvh * G + s % G;
+    return lane < 8 && s < T ? ((lbase_seq + h) * uint32_t(p.Lv) + uint32_t(qt * BT + 16 * wave + 2 * lane)) * 8
+                             : kOobOffset;
+  };
+  auto chunk = [&](int x, int s) { return (s < T && cf[x] < kOobOffset) ? cf[x] + step_base(s) : kOobOffset; };
+  // step 0 into stage 0, zeros into the Q and dO tiles of stage 2 (the first
+  // step's transposed reads of a step -1, whose P and dS are 0), step 1 into stage 1
+#pragma unroll
+  for (int x = 0; x < 5; ++x) {
+    dma16(qrs, &lds[(wave + 4 * x) * 1024], chunk(x, 0));
+    dma16(dors, &lds[kKvDRegion + (wave + 4 * x) * 1024], chunk(x, 0));
+  }
+  dma16(lrs, &lds[kKvLRegion + wave * 1024], pair_off(0));
+#pragma unroll
+  for (int x = 0; x < 5; ++x) {
+    dma16(qrs, &lds[2 * kKvTile + (wave + 4 * x) * 1024], kOobOffset);
+    dma16(dors, &lds[kKvDRegion + 2 * kKvTile + (wave + 4 * x) * 1024], kOobOffset);
+  }
+#pragma unroll
+  for (int x = 0; x < 5; ++x) {
+    dma16(qrs, &lds[kKvTile + (wave + 4 * x) * 1024], chunk(x, 1));
+    dma16(dors, &lds[kKvDRegion + kKvTile + (wave + 4 * x) * 1024], chunk(x, 1));
+  }
+  dma16(lrs, &lds[kKvLRegion + kKvLStage + wave * 1024], pair_off(1));
+  // the loop's first DMA is step 2
+#pragma unroll
+  for (int x = 0; x < 5; ++x) cf[x] = chunk(x, 2);
+  uint32_t cl = pair_off(2);
+
+  // LDS read bases (stages, blocks and d slices at immediate offsets): rows of
+  // a 32-row block in the sigma order (even k-steps from qe, odd from qo; dO
+  // from ge / go), transposed reads for (t, jj) from q<t><jj> / d<t><jj>, and
+  // the pairs of registers 0-7 / 8-15 from lp0 / lp1 (the lane half's KiB)
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  uint32_t qe, qo;
+  {
+    const int r = sigma(l32), sw = row_swizzle128(r >> 2);
+    const uint32_t rb = lds0 + uint32_t(r * kRowBytes128 + 16 * (hh ^ (sw & 1)));
+    qe = rb + 32 * (sw >> 1);
+    qo = rb + 32 - 32 * (sw >> 1);
+  }
+  uint32_t tq[4];
+  {
+    const int grp = lane >> 4, gi = lane & 15, vh = grp >> 1, e = gi >> 2;
+    const int c0 = 2 * (grp & 1) + ((gi & 3) >> 1), half = gi & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = i & 1, jj = i >> 1;
+      const int ro = jj ? 12 * vh + 4 + 8 * tt : 20 * vh + 8 * tt;
+      tq[i] = lds0 + uint32_t((e + ro) * kRowBytes128 + 16 * (c0 ^ row_swizzle128(ro >> 2)) + 8 * half);
+    }
+  }
+  const uint32_t lpb = lds0 + kKvLRegion + uint32_t(hh) * 1024;
+  const uint32_t lp0 = lpb + 8 * uint32_t(reg_key_offset(0, hh) - 16 * hh);
+  const uint32_t lp1 = lpb + 8 * uint32_t(reg_key_offset(2, hh) - 16 * hh);
+
+  // mask words: bit r set when register r's query (query tile qt, block qb)
+  // is valid and sees the lane's key
+  auto word = [&](int qt, int qb) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int iq = qt * BT + qb * 32 + reg_key_offset(r >> 2, hh) + (r & 3);
+      w |= uint32_t(iq < p.Lv && iq >= vk) << r;
+    }
+    return w;
+  };
+  const uint32_t w00 = word(qt_begin, 0), w01 = word(qt_begin, 1);
+  const uint32_t w10 = word(qt_begin + 1, 0), w11 = word(qt_begin + 1, 1);
+  const uint32_t wl0 = word(qt_end - 1, 0), wl1 = word(qt_end - 1, 1);
+  const uint32_t tlast = p.Lv % BT ? uint32_t(qt_end - 1 - qt_begin) : 0xffffffffu;
+
+  const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(wave) * 1024);
+  const uint32_t Tn = __builtin_amdgcn_readfirstlane(uint32_t(T));
+  const uint32_t Gn = uint32_t(G);
+  const uint32_t inch = D * 2, incw = uint32_t(BT * pstride) * q_pos_bytes - uint32_t(G - 1) * D * 2;
+  const uint32_t inclh = uint32_t(p.Lv) * 8, inclw = uint32_t(BT) * 8 - uint32_t(G - 1) * uint32_t(p.Lv) * 8;
+
+  // step 0 and the zeros landed for every wave (step 1 may still be in flight)
+  asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
+
+  typedef float f32x32 __attribute__((ext_vector_type(32)));
+  f32x32 dka, dkb, dva, dvb;
+  asm volatile(
+      SFA_DKDV128_PROLOGUE
+      SFA_DKDV128_LOOP
+      "s_waitcnt lgkmcnt(0)\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      : [dka] "={a[0:31]}"(dka), [dkb] "={a[32:63]}"(dkb), [dva] "={a[64:95]}"(dva), [dvb] "={a[96:127]}"(dvb),
+        [cf0] "+v"(cf[0]), [cf1] "+v"(cf[1]), [cf2] "+v"(cf[2]), [cf3] "+v"(cf[3]), [cf4] "+v"(cf[4]),
+        [cl] "+v"(cl)
+      : [kf] "{a[128:159]}"(kf), [vf] "{a[160:191]}"(vf), [c] "s"(p.c), [T] "s"(Tn), [G] "s"(Gn),
+        [tlast] "s"(tlast), [incw] "s"(incw), [inch] "s"(inch), [inclw] "s"(inclw), [inclh] "s"(inclh),
+        [rq] "s"(qrs), [rd] "s"(dors), [rl] "s"(lrs), [lw] "s"(lw), [lwl] "s"(lw),
+        [qe] "v"(qe), [qo] "v"(qo), [ge] "v"(qe + kKvDRegion), [go] "v"(qo + kKvDRegion), [q00] "v"(tq[0]),
+        [q10] "v"(tq[1]), [q01] "v"(tq[2]), [q11] "v"(tq[3]), [d00] "v"(tq[0] + kKvDRegion),
+        [d10] "v"(tq[1] + kKvDRegion), [d01] "v"(tq[2] + kKvDRegion), [d11] "v"(tq[3] + kKvDRegion),
+        [lp0] "v"(lp0), [lp1] "v"(lp1), [w00] "v"(w00), [w01] "v"(w01), [w10] "v"(w10), [w11] "v"(w11),
+        [wl0] "v"(wl0), [wl1] "v"(wl1)
+      : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", "s90", SFA_DKDV128_CLOBBER_V,
+        SFA_DKDV128_CLOBBER_A);
+
+  if (kvalid) {
+    const f32x32 dk2[2] = {dka, dkb}, dv2[2] = {dva, dvb};
+    const size_t krow = (size_t(base_row + vk * pstride) * p.hkv + kvh) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 kv, vv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          kv[r] = (__bf16)(dk2[db >> 1][(db & 1) * 16 + 4 * g + r] * p.scale);
+          vv[r] = (__bf16)dv2[db >> 1][(db & 1) * 16 + 4 * g + r];
+        }
+        *reinterpret_cast<bf16x4*>(p.dk + krow + db * 32 + 8 * g + 4 * hh) = kv;
+        *reinterpret_cast<bf16x4*>(p.dv + krow + db * 32 + 8 * g + 4 * hh) = vv;
+      }
+  }
+  // the DMA of the steps past the last is still in flight: wait before the
+  // work group ends and its LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // dQ at d = 128, intra and cross_full: one wave per SIMD with 64 queries (two
 // blocks of 32) of one query head, so that every K / V row read from LDS
 // feeds twice as many MFMAs as in bwd_dq_kernel. The work group's 4 waves
@@ -1876,7 +2091,11 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, pgrid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<64>, pgrid, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(kDkdv[di][kind], kgrid, dim3(kThreads), 0, stream, p);
+  if (di && kind != 2)
+    hipLaunchKernelGGL(kind == 0 ? bwd_dkdv128_stream_kernel<0> : bwd_dkdv128_stream_kernel<1>, kgrid, dim3(kThreads),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL(kDkdv[di][kind], kgrid, dim3(kThreads), 0, stream, p);
   if (dq128)
     hipLaunchKernelGGL(kind == 0 ? bwd_dq128_kernel<0> : bwd_dq128_kernel<1>, qgrid, dim3(kThreads), 0, stream, p);
   else

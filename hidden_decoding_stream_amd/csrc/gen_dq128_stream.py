@@ -44,6 +44,8 @@ DS1 = 96            # dS^T(kb1)
 KT = 64             # K^T operands: [db][jj] at KT + 8 db + 4 jj
 KR = 32             # K row ring: slot s at KR + 4 s
 VRG = 48            # V row ring: slot s at VRG + 4 s
+_spans = [(SX[0], 32), (PX[0], 32), (SY[0], 32), (PY[0], 32), (DS0, 16), (DS1, 16), (KT, 32), (KR, 16), (VRG, 16)]
+assert sorted(x for b, n in _spans for x in range(b, b + n)) == list(range(32, 256)), "fixed VGPRs overlap"
 # AGPRs
 DQ = 0              # dQ^T[j][db] at DQ + 64 j + 16 db
 QA = 128            # Q^T operands [j][kk] at QA + 32 j + 4 kk
@@ -54,7 +56,8 @@ SI, STMP, SINC = 84, 85, 86
 KST = 20480         # bytes per K (or V) stage: 64 rows of 320
 V_REGION = 3 * KST  # the V stages follow the 3 K stages
 NST = 3
-LDS_LAT = 3         # MFMAs between an LDS read and its first consumer (at least)
+LDS_LAT = int(__import__("os").environ.get("DQ_LDS_LAT", "3"))      # MFMAs from an LDS read to its first consumer
+DMA_DEADLINE = int(__import__("os").environ.get("DQ_DMA_DL", "60"))  # the DMA of tile t+2 issues before this MFMA
 
 
 def tr_temps(kb):
@@ -253,7 +256,7 @@ def build_iteration(st, h_split):
         if it.name.startswith("m0_") or it.name == "sinc":
             it.deps = [bar]
         # issued right after the barrier: the next barrier waits for it
-        it.fixed_deadline = 66 if it.name.startswith("inc") else 60
+        it.fixed_deadline = DMA_DEADLINE + (6 if it.name.startswith("inc") else 0)
     for it in kvN:
         it.deps = [bar]
     lds = ktA + kvA + kvC0 + kvC1 + ktC + kvN
