@@ -287,7 +287,7 @@ def build_iteration(stage, h_split):
 
 
 def main():
-    h_split = int(sys.argv[1]) if len(sys.argv) > 1 and sys.argv[1].isdigit() else 4
+    h_split = int(sys.argv[1]) if len(sys.argv) > 1 and sys.argv[1].isdigit() else 0
     allseq, blocks = [], []
     total = 0
     for stage in range(NST):

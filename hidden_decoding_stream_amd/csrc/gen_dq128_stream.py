@@ -277,15 +277,22 @@ def build_iteration(st, h_split):
     return out, t
 
 
-def insert_lgkm_waits(seq):
+LGKM_AHEAD = int(__import__("os").environ.get("LGKM_AHEAD", "4"))   # MFMAs a wait also covers
+
+
+def insert_lgkm_waits(seq, ahead=None):
     """Before each instruction that reads (or overwrites) registers an outstanding
-    LDS read writes, wait until that read has completed. The sequence is one
-    iteration; it runs after a copy of itself, so reads issued late in the
-    previous iteration are outstanding at the start."""
+    LDS read writes, wait until that read has completed; the wait also covers
+    the reads already issued that the instructions up to `ahead` MFMAs further
+    need (fewer waits, each a little earlier). The sequence is one iteration;
+    it runs after a copy of itself, so reads issued late in the previous
+    iteration are outstanding at the start."""
+    ahead = LGKM_AHEAD if ahead is None else ahead
+
     def run(prefix_outstanding, body, emit):
         outstanding = list(prefix_outstanding)    # in issue order: sets of written registers
         out = []
-        for it in body:
+        for pos, it in enumerate(body):
             if it.kind in ("label",):
                 out.append(it)
                 continue
@@ -294,6 +301,16 @@ def insert_lgkm_waits(seq):
             for i, w in enumerate(outstanding):
                 if w & regs:
                     need = i
+            if need >= 0 and it.kind != "lds" and ahead > 0:
+                nm = 0
+                for nxt in body[pos + 1:]:
+                    if nxt.kind == "mfma":
+                        nm += 1
+                        if nm > ahead:
+                            break
+                    for i, w in enumerate(outstanding):
+                        if w & (nxt.rd | nxt.wr):
+                            need = max(need, i)
             if need >= 0 and it.kind != "lds":
                 keep = len(outstanding) - need - 1
                 out.append(Ins(f"s_waitcnt lgkmcnt({min(keep, 15)})", "sync", name="lgkm"))
