@@ -1636,7 +1636,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
 // 16 queries' pairs, into a KiB of its own), and the masks are per-lane words
 // formed once (the first two query tiles hold the diagonal, a ragged last
 // tile masks the queries past the end; the step after the last, which
-// closes the stream, is masked whole). Rows past the end of a sequence load
+// closes the stream, is masked whole). The query tiles are walked from the
+// last down, so that the work groups of an XCD, which start together, read
+// the same Q and dO tiles at about the same time (from L2). Rows past the end of a sequence load
 // the next rows of the buffer (or zeros past its end), which those masks
 // exclude.
 // ---------------------------------------------------------------------------
@@ -1711,11 +1713,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdPara
     cf[x] = u >= 16 ? kOobOffset : uint32_t(row * pstride) * q_pos_bytes + (u ^ row_swizzle128(row >> 2)) * 16;
   }
   auto step_base = [&](int s) {
-    const int qt = qt_begin + s / G, h = kvh * G + s % G;
+    const int qt = qt_end - 1 - s / G, h = kvh * G + s % G;
     return uint32_t(base_row + qt * BT * pstride) * q_pos_bytes + uint32_t(h) * D * 2;
   };
   auto pair_off = [&](int s) {
-    const int qt = qt_begin + s / G, h = kvh * G + s % G;
+    const int qt = qt_end - 1 - s / G, h = kvh * G + s % G;
     return lane < 8 && s < T ? ((lbase_seq + h) * uint32_t(p.Lv) + uint32_t(qt * BT + 16 * wave + 2 * lane)) * 8
                              : kOobOffset;
   };
@@ -1785,13 +1787,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdPara
   const uint32_t w00 = word(qt_begin, 0), w01 = word(qt_begin, 1);
   const uint32_t w10 = word(qt_begin + 1, 0), w11 = word(qt_begin + 1, 1);
   const uint32_t wl0 = word(qt_end - 1, 0), wl1 = word(qt_end - 1, 1);
-  const uint32_t tlast = p.Lv % BT ? uint32_t(qt_end - 1 - qt_begin) : 0xffffffffu;
+  // the query tiles go from the last down: qt_begin + 1 and qt_begin come after
+  // tb1 and tb0 tiles, a ragged last tile first
+  const uint32_t tb0 = __builtin_amdgcn_readfirstlane(uint32_t(qt_end - 1 - qt_begin));
+  const uint32_t tb1 = __builtin_amdgcn_readfirstlane(uint32_t(qt_end - 2 - qt_begin));
+  const uint32_t tlast = __builtin_amdgcn_readfirstlane(p.Lv % BT ? 0u : 0xffffffffu);
 
   const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(wave) * 1024);
   const uint32_t Tn = __builtin_amdgcn_readfirstlane(uint32_t(T));
   const uint32_t Gn = uint32_t(G);
-  const uint32_t inch = D * 2, incw = uint32_t(BT * pstride) * q_pos_bytes - uint32_t(G - 1) * D * 2;
-  const uint32_t inclh = uint32_t(p.Lv) * 8, inclw = uint32_t(BT) * 8 - uint32_t(G - 1) * uint32_t(p.Lv) * 8;
+  // offset steps (mod 2^32): next head, or the tile below and the first head
+  const uint32_t incw = 0u - uint32_t(BT * pstride) * q_pos_bytes - uint32_t(G - 1) * D * 2;
+  const uint32_t inclh = uint32_t(p.Lv) * 8, inclw = 0u - uint32_t(BT) * 8 - uint32_t(G - 1) * uint32_t(p.Lv) * 8;
 
   // step 0 and the zeros landed for every wave (step 1 may still be in flight)
   asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
@@ -1808,8 +1815,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdPara
         [cf0] "+v"(cf[0]), [cf1] "+v"(cf[1]), [cf2] "+v"(cf[2]), [cf3] "+v"(cf[3]), [cf4] "+v"(cf[4]),
         [cl] "+v"(cl)
       : [kf] "{a[128:159]}"(kf), [vf] "{a[160:191]}"(vf), [c] "s"(p.c), [T] "s"(Tn), [G] "s"(Gn),
-        [tlast] "s"(tlast), [incw] "s"(incw), [inch] "s"(inch), [inclw] "s"(inclw), [inclh] "s"(inclh),
-        [rq] "s"(qrs), [rd] "s"(dors), [rl] "s"(lrs), [lw] "s"(lw), [lwl] "s"(lw),
+        [tlast] "s"(tlast), [tb0] "s"(tb0), [tb1] "s"(tb1), [incw] "s"(incw), [inclw] "s"(inclw), [inclh] "s"(inclh),
+        [rq] "s"(qrs), [rd] "s"(dors), [rl] "s"(lrs), [lw] "s"(lw),
         [qe] "v"(qe), [qo] "v"(qo), [ge] "v"(qe + kKvDRegion), [go] "v"(qo + kKvDRegion), [q00] "v"(tq[0]),
         [q10] "v"(tq[1]), [q01] "v"(tq[2]), [q11] "v"(tq[3]), [d00] "v"(tq[0] + kKvDRegion),
         [d10] "v"(tq[1] + kKvDRegion), [d01] "v"(tq[2] + kKvDRegion), [d11] "v"(tq[3] + kKvDRegion),

@@ -8,7 +8,8 @@ Scheduling, wait states, LDS waits and checks as in gen_dq128_stream.py.
 
 Per wave: 32 keys (K^T and V^T operands in AGPRs), accumulating dK^T and dV^T
 over the steps of its work group: one step is one 64-query tile of one query
-head (two blocks qb0, qb1 of 32 queries). Per step t, 64 MFMAs:
+head (two blocks qb0, qb1 of 32 queries), the tiles from the last down, so
+that the work groups of one XCD read the same tiles at about the same time. Per step t, 64 MFMAs:
   M0-15  G1: S(t, qb0) = Q K^T, dP(t, qb0) = dO V^T          (set A)
   M16-31 G2: dV^T += dO^T P, dK^T += Q^T dS  of (t-1, qb1)   (set B)
   M32-47 G3: S(t, qb1), dP(t, qb1)                           (set B)
@@ -115,17 +116,17 @@ def pdsa(st, pairs):
 
 def mask_block(st, lab):
     """Out of line: the step past the last masks every score of the block; the
-    first two query tiles and a ragged last one take the lane's mask word
+    first two query tiles (done last) and a ragged last one (done first) take the lane's mask word
     (bit r set when register r's query sees the lane's key and is valid)."""
     s = SETS[st]
     t0, t1, t2 = s["DS"], s["DS"] + 1, s["DS"] + 2      # free until this block's dS
     b = [Ins(f"{lab}:", "label"),
          Ins(f"s_cmp_ge_u32 s{SI}, %[T]\n\ts_cbranch_scc1 {lab}_all", "salu"),
          Ins(f"v_mov_b32 v{t0}, %[wl{st}]", rd={f"%[wl{st}]"}, wr={f"v{t0}"}),
-         Ins(f"s_cmp_eq_u32 s{STI}, 0\n\ts_cbranch_scc0 {lab}_1", "salu"),
+         Ins(f"s_cmp_eq_u32 s{STI}, %[tb0]\n\ts_cbranch_scc0 {lab}_1", "salu"),
          Ins(f"v_mov_b32 v{t0}, %[w0{st}]", rd={f"%[w0{st}]"}, wr={f"v{t0}"}),
          Ins(f"{lab}_1:", "label"),
-         Ins(f"s_cmp_eq_u32 s{STI}, 1\n\ts_cbranch_scc0 {lab}_2", "salu"),
+         Ins(f"s_cmp_eq_u32 s{STI}, %[tb1]\n\ts_cbranch_scc0 {lab}_2", "salu"),
          Ins(f"v_mov_b32 v{t0}, %[w1{st}]", rd={f"%[w1{st}]"}, wr={f"v{t0}"}),
          Ins(f"{lab}_2:", "label"),
          Ins(f"v_mov_b32 v{t2}, {NEG_INF}", wr={f"v{t2}"})]
@@ -143,9 +144,11 @@ def mask_block(st, lab):
 
 
 def mask_check(st, lab):
-    """Full blocks (a middle query tile, or a last one that is whole) fall through."""
+    """Full blocks fall through: the query tiles are walked from the last down
+    (STI counts the tiles done), so the two holding the diagonal come last
+    (STI >= tb1) and a ragged last tile first (STI == tlast, 0 or never)."""
     s = SETS[st]
-    br = Ins(f"s_cmp_lt_u32 s{STI}, 2\n\ts_cbranch_scc1 {lab}\n\ts_cmp_eq_u32 s{STI}, %[tlast]\n\t"
+    br = Ins(f"s_cmp_ge_i32 s{STI}, %[tb1]\n\ts_cbranch_scc1 {lab}\n\ts_cmp_eq_u32 s{STI}, %[tlast]\n\t"
              f"s_cbranch_scc1 {lab}\n\ts_cmp_ge_u32 s{SI}, %[T]\n\ts_cbranch_scc1 {lab}\n{lab}_r:", "br",
              rd=vset(s["S"], 16), wr=vset(s["S"], 16) | {"vcc"} | vset(s["DS"], 3), slots=6, name=f"mchk{st}")
     br.block = fix_block(mask_block(st, lab))
@@ -210,7 +213,7 @@ def dma(dst):
     then the offsets advance to step t+3 (next head, or next tile after the
     last head; past the last step out of range)."""
     items = [Ins(f"s_add_u32 s{SG2}, s{SG2}, 1\n\ts_cmp_eq_u32 s{SG2}, %[G]\n\t"
-                 f"s_cselect_b32 s{SINC}, %[incw], %[inch]\n\ts_cselect_b32 s{SINCL}, %[inclw], %[inclh]\n\t"
+                 f"s_cselect_b32 s{SINC}, %[incw], 256\n\ts_cselect_b32 s{SINCL}, %[inclw], %[inclh]\n\t"
                  f"s_cselect_b32 s{SG2}, 0, s{SG2}\n\ts_add_u32 s{STMP}, s{SI}, 3\n\ts_cmp_eq_u32 s{STMP}, %[T]\n\t"
                  f"s_cselect_b32 s{STMP}, 0x80000000, 0\n\ts_add_u32 s{SINC}, s{SINC}, s{STMP}\n\t"
                  f"s_add_u32 s{SINCL}, s{SINCL}, s{STMP}", "salu", slots=10, name="sinc")]
@@ -220,7 +223,7 @@ def dma(dst):
             items.append(Ins(f"s_add_u32 m0, %[lw], {off}", "salu", wr={"m0"}, name=f"m0_{x}{int(dout)}"))
             items.append(Ins(f"buffer_load_dwordx4 %[cf{x}], %[{'rd' if dout else 'rq'}], 0 offen lds", "vmem",
                              rd={"m0", f"%[cf{x}]"}, name=f"dma{x}{int(dout)}"))
-    items.append(Ins(f"s_add_u32 m0, %[lwl], {L_REGION + dst * LST}", "salu", wr={"m0"}, name="m0_l"))
+    items.append(Ins(f"s_add_u32 m0, %[lw], {L_REGION + dst * LST}", "salu", wr={"m0"}, name="m0_l"))
     items.append(Ins("buffer_load_dwordx4 %[cl], %[rl], 0 offen lds", "vmem", rd={"m0", "%[cl]"}, name="dmal"))
     for x in range(5):
         items.append(Ins(f"v_add_u32 %[cf{x}], s{SINC}, %[cf{x}]", rd={f"%[cf{x}]"}, wr={f"%[cf{x}]"},
