@@ -14,29 +14,32 @@
 // * bwd_prep_kernel: D and lse*log2(e) per query row, into a workspace laid
 //   out by virtual sequence ([B][nseq][hq][Lv][2]) so that a run of queries of
 //   one virtual sequence is contiguous.
-// * bwd_dq_kernel: query-stationary, shaped like the forward. Per 64-key tile
+// * dK, dV (key-stationary): a wave owns 32 keys (K and V as B operands); the
+//   Q and dO tiles of 64 queries stream through LDS, for each of the G query
+//   heads in turn. S = Q K^T and dP = dO V^T (lane = key column), P and dS
+//   with each register's own query lse / D, then dV^T += dO^T P and
+//   dK^T += Q^T dS (dO^T, Q^T by transposed reads). At d = 128, intra and
+//   cross_full run bwd_dkdv128_stream_kernel, whose whole step loop is one asm
+//   stream (attn_dkdv128_stream.h); the windowed mode runs bwd_dkdv128_kernel
+//   (one scheduled asm block per 32-query block, dkdv_block128) and d = 64
+//   bwd_dkdv_kernel (three asm phases per block, DkdvAsm).
+// * dQ (query-stationary, shaped like the forward): per 64-key tile
 //   S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS as A operands, Q^T
 //   and dO^T in registers), then P^T = exp2(S^T c - lse2) with the lane's own
 //   lse, dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T, with dS^T taken straight
 //   from the accumulators as the B operand (rows read in the sigma order) and
-//   K^T gathered by transposed LDS reads. intra and cross_full run two
-//   groups per CU (253 VGPRs, no spills: the per-lane DMA offsets are
-//   recomputed per tile, and the transposed reads share two base registers);
-//   the windowed mode runs one and its loop in asm phases (DqAsm).
-// * bwd_dkdv128_kernel (d = 128) and bwd_dkdv_kernel (d = 64): key-stationary.
-//   A wave owns 32 keys (K and V as B operands); the Q and dO tiles of 64
-//   queries stream through LDS, for each of the G query heads in turn.
-//   S = Q K^T and dP = dO V^T (lane = key column), P and dS with each
-//   register's own query lse / D, then dV^T += dO^T P and dK^T += Q^T dS
-//   (dO^T, Q^T by transposed reads). At d = 128 each 32-query block is one
-//   scheduled asm stream (dkdv_block128) over tiles laid out free of LDS
-//   bank conflicts (row_swizzle128, common.h); at d = 64 the block runs in
-//   three asm phases (DkdvAsm).
-// Tiles go by buffer->LDS DMA through a ring (2 stages for dQ, 3 for dK/dV)
-// with one bare barrier per tile; dQ and the d = 64 dK/dV use K-style rows
-// padded to D+16 elements. LDS reads are asm blocks that wait for their own
+//   K^T by transposed LDS reads. At d = 128, intra and cross_full run
+//   bwd_dq128_kernel (one wave per SIMD with 64 queries, the loop one asm
+//   stream, attn_dq128_stream.h); otherwise bwd_dq_kernel (two groups per CU
+//   for intra and cross_full, the windowed mode one group with its loop in
+//   asm phases, DqAsm).
+// The d = 128 kernels keep K, V, Q and dO tiles in rows of 320 bytes whose
+// 16-byte chunks are swizzled by row quad (row_swizzle128, common.h): row and
+// transposed reads are then free of LDS bank conflicts. The others use rows
+// padded to D+16 elements. Tiles go by buffer->LDS DMA through a ring with
+// one bare barrier per tile. LDS reads are asm blocks that wait for their own
 // results (see common.h), and the one-wave-per-SIMD loops run their MFMAs
-// inside those blocks (dkdv_block128, DkdvAsm, DqAsm).
+// inside those blocks.
 #include <math.h>
 
 #include "attn_dkdv128_stream.h"
