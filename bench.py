@@ -178,6 +178,22 @@ def main():
                     raise RuntimeError("sfp_read launch failed")
         torch.cuda.synchronize()
         print(json.dumps({"profile_read": nbytes, "blocks": 256, "launches": 24}), flush=True)
+        # the same bytes in the decode's pattern (8 heads x 32 key ranges, each head's 256-byte slice of
+        # every K and V row): 16-byte loads into registers, then buffer->LDS DMA through rings of 2, 4
+        # and 8 stages per wave; 8 cache pairs (1 GiB) rotated, 3 rounds each
+        rows = 4 * 8192
+        pairs = [(bufs[i], bufs[i + 4]) for i in range(4)] + [(bufs[i + 4], bufs[i]) for i in range(4)]
+        sink = torch.empty(8 * 32, dtype=torch.int32, device=dev)
+        for ring in (0, 2, 4, 8):
+            for _ in range(3):
+                for kb, vb in pairs:
+                    rc = (P.lib().sfp_read_slices(kb.data_ptr(), vb.data_ptr(), rows, 8, 32, sink.data_ptr(), st)
+                          if ring == 0 else
+                          P.lib().sfp_read_slices_lds(kb.data_ptr(), vb.data_ptr(), rows, 8, 32, ring, st))
+                    if rc != 0:
+                        raise RuntimeError("sfp_read_slices launch failed")
+            torch.cuda.synchronize()
+            print(json.dumps({"profile_read_slices": ring or "registers", "launches": 24}), flush=True)
         return
 
     if args.trace_prefill:

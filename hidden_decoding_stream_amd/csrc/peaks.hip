@@ -5,6 +5,12 @@
 //              per lane) and folds it into one word per work group; the
 //              bandwidth a read-only kernel such as decode can reach.
 //   sfp_copy   copies a buffer (read + write), the pattern of the interleave.
+//   sfp_read_slices, sfp_read_slices_lds
+//              read what one decode call reads, in its pattern: for each kv
+//              head (work group x) and key range (work group y), the head's
+//              256-byte slice of every K and V row (rows of heads * 256 bytes),
+//              by 16-byte loads into registers, or by buffer->LDS DMA through
+//              a ring of stages per wave, the decode kernel's way.
 //   sfp_mfma   back-to-back v_mfma_f32_32x32x16_bf16 on register operands,
 //              several independent accumulators per wave; the dense bf16
 //              matrix-core rate at the clock the chip holds under load.
@@ -86,6 +92,70 @@ __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int 
   out[size_t(blockIdx.x) * 256 + threadIdx.x] = s;
 }
 
+
+// One work group per (head, key range); 16 lanes cover one 256-byte slice, 16
+// rows per pass, kUnroll / 2 passes of K and V in flight per lane.
+__global__ __launch_bounds__(256) void slices_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                                     int rows_per_group, int heads, uint32_t* __restrict__ sink) {
+  const int u = blockIdx.x, s = blockIdx.y;
+  const int c16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;
+  const size_t row16 = size_t(heads) * 16;                 // 16-byte units per row
+  u32x4 acc = {0, 0, 0, 0};
+  for (int r = 0; r < rows_per_group; r += 16 * (kUnroll / 2)) {
+    u32x4 x[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll / 2; ++j) {
+      const size_t i = (size_t(s) * rows_per_group + r + j * 16 + rsub) * row16 + size_t(u) * 16 + c16;
+      x[2 * j] = __builtin_nontemporal_load(k + i);
+      x[2 * j + 1] = __builtin_nontemporal_load(v + i);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) acc ^= x[j];
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) sink[blockIdx.y * gridDim.x + blockIdx.x] = 1;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The same bytes by DMA: wave w takes every 4th step of R rows of K and of V
+// (NS stages of R * 512 bytes per wave), waits for a stage and reissues it at
+// once (no work on the data: the stream alone).
+template <int NS, int R>
+__global__ __launch_bounds__(256) void slices_lds_kernel(const void* k, const void* v, uint32_t bytes,
+                                                         int rows_per_group, int heads) {
+  constexpr int SB = R * 512, NI = R / 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * NS * SB];
+  const int u = blockIdx.x, s = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6), lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(k), (short)0, int(bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(v), (short)0, int(bytes), 0x00020000);
+  const uint32_t row_bytes = uint32_t(heads) * 256;
+  const int nsteps = rows_per_group / R / 4;
+  const uint32_t lane_off = uint32_t(lane / 16) * row_bytes + uint32_t(u) * 256 + uint32_t(lane % 16) * 16;
+  uint8_t* ring = lds + wave * NS * SB;
+  auto issue = [&](int st, int step) {
+    const uint32_t row0 = uint32_t(s * rows_per_group + (step * 4 + wave) * R);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ring + st * SB + i * 1024), 16,
+                                               (row0 + 4 * i) * row_bytes + lane_off, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ring + st * SB + SB / 2 + i * 1024), 16,
+                                               (row0 + 4 * i) * row_bytes + lane_off, 0, 0, 0);
+  };
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    if (st < nsteps) issue(st, st);
+  for (int step = 0; step < nsteps; ++step) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * 2 * NI) : "memory");
+    if (step + NS < nsteps) issue(step % NS, step + NS);
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 }  // namespace
 
 extern "C" {
@@ -103,6 +173,37 @@ int sfp_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStrea
 int sfp_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t stream) {
   hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
                      static_cast<u32x4*>(dst), bytes / 16);
+  return int(hipGetLastError());
+}
+
+// The decode's read pattern: k and v hold `rows` rows of `heads` * 256 bytes
+// each (one bf16 d = 128 row per head); work group (u, s) reads head u's
+// slice of rows [s * rows / splits, (s + 1) * rows / splits) of both.
+// rows / splits must be a multiple of 64. sink: heads * splits words.
+int sfp_read_slices(const void* k, const void* v, int rows, int heads, int splits, uint32_t* sink,
+                    hipStream_t stream) {
+  if (rows % splits || (rows / splits) % 64) return int(hipErrorInvalidValue);
+  hipLaunchKernelGGL(slices_kernel, dim3(heads, splits), dim3(256), 0, stream, static_cast<const u32x4*>(k),
+                     static_cast<const u32x4*>(v), rows / splits, heads, sink);
+  return int(hipGetLastError());
+}
+
+// The same by buffer->LDS DMA, ring = 2, 4 or 8 stages per wave (of 32, 16 or
+// 8 rows: 128 KiB of LDS per group either way). rows * heads * 256 < 2^31.
+int sfp_read_slices_lds(const void* k, const void* v, int rows, int heads, int splits, int ring,
+                        hipStream_t stream) {
+  const int rpg = rows / splits;
+  if (rows % splits || rpg % 128 || size_t(rows) * heads * 256 >= (size_t(1) << 31)) return int(hipErrorInvalidValue);
+  const uint32_t bytes = uint32_t(size_t(rows) * heads * 256);
+  const dim3 grid(heads, splits);
+  if (ring == 2)
+    hipLaunchKernelGGL((slices_lds_kernel<2, 32>), grid, dim3(256), 0, stream, k, v, bytes, rpg, heads);
+  else if (ring == 4)
+    hipLaunchKernelGGL((slices_lds_kernel<4, 16>), grid, dim3(256), 0, stream, k, v, bytes, rpg, heads);
+  else if (ring == 8)
+    hipLaunchKernelGGL((slices_lds_kernel<8, 8>), grid, dim3(256), 0, stream, k, v, bytes, rpg, heads);
+  else
+    return int(hipErrorInvalidValue);
   return int(hipGetLastError());
 }
 

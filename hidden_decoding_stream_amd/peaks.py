@@ -22,7 +22,9 @@ def lib() -> ctypes.CDLL:
         L.sfp_read.argtypes = [c.c_void_p, c.c_size_t, c.c_void_p, c.c_int, c.c_void_p]
         L.sfp_copy.argtypes = [c.c_void_p, c.c_void_p, c.c_size_t, c.c_int, c.c_void_p]
         L.sfp_mfma.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_int, c.c_void_p]
-        for f in (L.sfp_read, L.sfp_copy, L.sfp_mfma):
+        L.sfp_read_slices.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int, c.c_int, c.c_void_p, c.c_void_p]
+        L.sfp_read_slices_lds.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int, c.c_int, c.c_int, c.c_void_p]
+        for f in (L.sfp_read, L.sfp_copy, L.sfp_mfma, L.sfp_read_slices, L.sfp_read_slices_lds):
             f.restype = c.c_int
         _lib = L
     return _lib

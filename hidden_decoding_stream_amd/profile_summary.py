@@ -165,7 +165,9 @@ def decode(d) -> str:
         for r in csv.DictReader(open(f)):
             name = r["Kernel_Name"]
             short = ("split" if "decode_split_kernel" in name else "combine" if "decode_combine_kernel" in name
-                     else "read" if "read_kernel" in name else None)
+                     else "read" if "read_kernel" in name else "slices" if "slices_kernel" in name
+                     else "ring" + re.search(r"slices_lds_kernel<(\d+)", name).group(1)
+                     if "slices_lds_kernel" in name else None)
             if short:
                 rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short, name,
                              r.get("Grid_Size") or r.get("Grid_Size_X") or ""))
@@ -191,6 +193,12 @@ def decode(d) -> str:
     if reads:
         out.append(f"plain read of the same bytes, 256 groups: mean {sum(reads) / len(reads):.2f} us, "
                    f"min {min(reads):.2f} us over {len(reads)} launches")
+    for short, what in (("slices", "16-byte loads into registers"), ("ring2", "DMA, ring of 2 stages of 32 rows"),
+                        ("ring4", "DMA, ring of 4 stages of 16 rows"), ("ring8", "DMA, ring of 8 stages of 8 rows")):
+        ts = [(en - st) / 1e3 for st, en, s, _, _ in rows if s == short]
+        if ts:
+            out.append(f"the same bytes in the decode's pattern, {what}: mean {sum(ts) / len(ts):.2f} us, "
+                       f"min {min(ts):.2f} us over {len(ts)} launches")
     return "\n".join(out)
 
 
