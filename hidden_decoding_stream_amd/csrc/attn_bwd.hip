@@ -18,21 +18,20 @@
 //   Q and dO tiles of 64 queries stream through LDS, for each of the G query
 //   heads in turn. S = Q K^T and dP = dO V^T (lane = key column), P and dS
 //   with each register's own query lse / D, then dV^T += dO^T P and
-//   dK^T += Q^T dS (dO^T, Q^T by transposed reads). At d = 128, intra and
-//   cross_full run bwd_dkdv128_stream_kernel, whose whole step loop is one asm
-//   stream (attn_dkdv128_stream.h); the windowed mode runs bwd_dkdv128_kernel
-//   (one scheduled asm block per 32-query block, dkdv_block128) and d = 64
-//   bwd_dkdv_kernel (three asm phases per block, DkdvAsm).
+//   dK^T += Q^T dS (dO^T, Q^T by transposed reads). At d = 128 every mode runs
+//   bwd_dkdv128_stream_kernel, whose whole step loop is one asm stream
+//   (attn_dkdv128_stream.h); d = 64 runs bwd_dkdv_kernel (three asm phases
+//   per 32-query block, DkdvAsm).
 // * dQ (query-stationary, shaped like the forward): per 64-key tile
 //   S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS as A operands, Q^T
 //   and dO^T in registers), then P^T = exp2(S^T c - lse2) with the lane's own
 //   lse, dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T, with dS^T taken straight
 //   from the accumulators as the B operand (rows read in the sigma order) and
-//   K^T by transposed LDS reads. At d = 128, intra and cross_full run
-//   bwd_dq128_kernel (one wave per SIMD with 64 queries, the loop one asm
-//   stream, attn_dq128_stream.h); otherwise bwd_dq_kernel (two groups per CU
-//   for intra and cross_full, the windowed mode one group with its loop in
-//   asm phases, DqAsm).
+//   K^T by transposed LDS reads. At d = 128 every mode runs bwd_dq128_kernel
+//   (one wave per SIMD with 64 queries, the loop one asm stream,
+//   attn_dq128_stream.h); d = 64 runs bwd_dq_kernel (two groups per CU for
+//   intra and cross_full, the windowed mode one group with its loop in asm
+//   phases, DqAsm).
 // The d = 128 kernels keep K, V, Q and dO tiles in rows of 320 bytes whose
 // 16-byte chunks are swizzled by row quad (row_swizzle128, common.h): row and
 // transposed reads are then free of LDS bank conflicts. The others use rows
@@ -99,31 +98,6 @@ template <int D> struct BTile {
 // waits for its results (a builtin read would wait for every buffer->LDS load
 // in flight).
 template <int D> __device__ __forceinline__ void gather16(u32x2 (&x)[D / 8], uint32_t ae, uint32_t ao);
-template <> __device__ __forceinline__ void gather16<128>(u32x2 (&x)[16], uint32_t ae, uint32_t ao) {
-  // row offsets (8t + 4j2) * 144 elements * 2 bytes: t0j0 0, t1j0 2304, t0j1 1152, t1j1 3456
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
-      "ds_read_b64_tr_b16 %1, %16 offset:2304\n\t"
-      "ds_read_b64_tr_b16 %2, %17 offset:1152\n\t"
-      "ds_read_b64_tr_b16 %3, %17 offset:3456\n\t"
-      "ds_read_b64_tr_b16 %4, %16 offset:64\n\t"
-      "ds_read_b64_tr_b16 %5, %16 offset:2368\n\t"
-      "ds_read_b64_tr_b16 %6, %17 offset:1216\n\t"
-      "ds_read_b64_tr_b16 %7, %17 offset:3520\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
-      "ds_read_b64_tr_b16 %9, %16 offset:2432\n\t"
-      "ds_read_b64_tr_b16 %10, %17 offset:1280\n\t"
-      "ds_read_b64_tr_b16 %11, %17 offset:3584\n\t"
-      "ds_read_b64_tr_b16 %12, %16 offset:192\n\t"
-      "ds_read_b64_tr_b16 %13, %16 offset:2496\n\t"
-      "ds_read_b64_tr_b16 %14, %17 offset:1344\n\t"
-      "ds_read_b64_tr_b16 %15, %17 offset:3648\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
-        "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
-      : "v"(ae), "v"(ao)
-      : "memory");
-}
 template <> __device__ __forceinline__ void gather16<64>(u32x2 (&x)[8], uint32_t ae, uint32_t ao) {
   // row offsets (8t + 4j2) * 80 elements * 2 bytes: t0j0 0, t1j0 1280, t0j1 640, t1j1 1920
   asm volatile(
@@ -167,36 +141,6 @@ __device__ __forceinline__ void lds_pair2(bf16x8 (&a)[2], bf16x8 (&b)[2], uint32
 // the buffer->LDS loads in flight.
 template <int D> __device__ __forceinline__ void lds_rows2(bf16x8 (&a)[D / 16], bf16x8 (&b)[D / 16], uint32_t pa,
                                                            uint32_t pb);
-template <> __device__ __forceinline__ void lds_rows2<128>(bf16x8 (&a)[8], bf16x8 (&b)[8], uint32_t pa,
-                                                             uint32_t pb) {
-  u32x4 x[16];
-  asm volatile(
-      "ds_read_b128 %0, %16 offset:0\n\t"
-      "ds_read_b128 %1, %16 offset:32\n\t"
-      "ds_read_b128 %2, %16 offset:64\n\t"
-      "ds_read_b128 %3, %16 offset:96\n\t"
-      "ds_read_b128 %4, %16 offset:128\n\t"
-      "ds_read_b128 %5, %16 offset:160\n\t"
-      "ds_read_b128 %6, %16 offset:192\n\t"
-      "ds_read_b128 %7, %16 offset:224\n\t"
-      "ds_read_b128 %8, %17 offset:0\n\t"
-      "ds_read_b128 %9, %17 offset:32\n\t"
-      "ds_read_b128 %10, %17 offset:64\n\t"
-      "ds_read_b128 %11, %17 offset:96\n\t"
-      "ds_read_b128 %12, %17 offset:128\n\t"
-      "ds_read_b128 %13, %17 offset:160\n\t"
-      "ds_read_b128 %14, %17 offset:192\n\t"
-      "ds_read_b128 %15, %17 offset:224\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
-      : "v"(pa), "v"(pb)
-      : "memory");
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_memcpy(&a[i], &x[i], 16);
-    __builtin_memcpy(&b[i], &x[8 + i], 16);
-  }
-}
 template <> __device__ __forceinline__ void lds_rows2<64>(bf16x8 (&a)[4], bf16x8 (&b)[4], uint32_t pa,
                                                              uint32_t pb) {
   u32x4 x[8];
@@ -326,110 +270,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 //   x2: the second half; gathers K^T (transposed)
 //   y:  dQ^T += K^T dS^T; reads the first half of the next block's rows
 template <int D> struct DqAsm;
-template <> struct DqAsm<128> {
-  static __device__ __forceinline__ void x1(f32x16& s, f32x16& p, const bf16x8 (&ka)[8], const bf16x8 (&va)[8],
-                                            const bf16x8 (&qf)[8], const bf16x8 (&dof)[8], uint32_t pa, uint32_t pb,
-                                            u32x4 (&y)[8]) {
-  asm volatile(
-      "s_nop 2\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka0], %[qf0], 0\n\t"
-      "ds_read_b128 %[y0], %[pa] offset:128\n\t"
-      "ds_read_b128 %[y1], %[pa] offset:160\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va0], %[dof0], 0\n\t"
-      "ds_read_b128 %[y2], %[pa] offset:192\n\t"
-      "ds_read_b128 %[y3], %[pa] offset:224\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka1], %[qf1], %[s]\n\t"
-      "ds_read_b128 %[y4], %[pb] offset:128\n\t"
-      "ds_read_b128 %[y5], %[pb] offset:160\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va1], %[dof1], %[p]\n\t"
-      "ds_read_b128 %[y6], %[pb] offset:192\n\t"
-      "ds_read_b128 %[y7], %[pb] offset:224\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka2], %[qf2], %[s]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va2], %[dof2], %[p]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka3], %[qf3], %[s]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va3], %[dof3], %[p]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      : [s] "=&v"(s), [p] "=&v"(p), [y0] "=&v"(y[0]), [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3]),
-        [y4] "=&v"(y[4]), [y5] "=&v"(y[5]), [y6] "=&v"(y[6]), [y7] "=&v"(y[7])
-      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [va0] "v"(va[0]),
-        [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [qf0] "v"(qf[0]), [qf1] "v"(qf[1]),
-        [qf2] "v"(qf[2]), [qf3] "v"(qf[3]), [dof0] "v"(dof[0]), [dof1] "v"(dof[1]), [dof2] "v"(dof[2]),
-        [dof3] "v"(dof[3]), [pa] "v"(pa), [pb] "v"(pb)
-      : "memory");
-  }
-  static __device__ __forceinline__ void x2(f32x16& s, f32x16& p, const bf16x8 (&ka)[8], const bf16x8 (&va)[8],
-                                            const bf16x8 (&qf)[8], const bf16x8 (&dof)[8], uint32_t ae, uint32_t ao,
-                                            u32x2 (&x)[16]) {
-  asm volatile(
-      "s_nop 2\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka0], %[qf0], %[s]\n\t"
-      "ds_read_b64_tr_b16 %[x0], %[ae] offset:0\n\t"
-      "ds_read_b64_tr_b16 %[x1], %[ae] offset:2304\n\t"
-      "ds_read_b64_tr_b16 %[x2], %[ao] offset:1152\n\t"
-      "ds_read_b64_tr_b16 %[x3], %[ao] offset:3456\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va0], %[dof0], %[p]\n\t"
-      "ds_read_b64_tr_b16 %[x4], %[ae] offset:64\n\t"
-      "ds_read_b64_tr_b16 %[x5], %[ae] offset:2368\n\t"
-      "ds_read_b64_tr_b16 %[x6], %[ao] offset:1216\n\t"
-      "ds_read_b64_tr_b16 %[x7], %[ao] offset:3520\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka1], %[qf1], %[s]\n\t"
-      "ds_read_b64_tr_b16 %[x8], %[ae] offset:128\n\t"
-      "ds_read_b64_tr_b16 %[x9], %[ae] offset:2432\n\t"
-      "ds_read_b64_tr_b16 %[x10], %[ao] offset:1280\n\t"
-      "ds_read_b64_tr_b16 %[x11], %[ao] offset:3584\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va1], %[dof1], %[p]\n\t"
-      "ds_read_b64_tr_b16 %[x12], %[ae] offset:192\n\t"
-      "ds_read_b64_tr_b16 %[x13], %[ae] offset:2496\n\t"
-      "ds_read_b64_tr_b16 %[x14], %[ao] offset:1344\n\t"
-      "ds_read_b64_tr_b16 %[x15], %[ao] offset:3648\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka2], %[qf2], %[s]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va2], %[dof2], %[p]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[ka3], %[qf3], %[s]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[p], %[va3], %[dof3], %[p]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7\n\t"
-      "s_nop 3\n\t"
-      : [s] "+v"(s), [p] "+v"(p), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]), [x3] "=&v"(x[3]),
-        [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]), [x7] "=&v"(x[7]), [x8] "=&v"(x[8]),
-        [x9] "=&v"(x[9]), [x10] "=&v"(x[10]), [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]),
-        [x14] "=&v"(x[14]), [x15] "=&v"(x[15])
-      : [ka0] "v"(ka[4]), [ka1] "v"(ka[5]), [ka2] "v"(ka[6]), [ka3] "v"(ka[7]), [va0] "v"(va[4]),
-        [va1] "v"(va[5]), [va2] "v"(va[6]), [va3] "v"(va[7]), [qf0] "v"(qf[4]), [qf1] "v"(qf[5]),
-        [qf2] "v"(qf[6]), [qf3] "v"(qf[7]), [dof0] "v"(dof[4]), [dof1] "v"(dof[5]), [dof2] "v"(dof[6]),
-        [dof3] "v"(dof[7]), [ae] "v"(ae), [ao] "v"(ao)
-      : "memory");
-  }
-  static __device__ __forceinline__ void y(f32x16 (&acc)[4], const bf16x8 (&kT)[4][2], const bf16x8 (&dsf)[2],
-                                           uint32_t pa, uint32_t pb, u32x4 (&y)[8]) {
-  asm volatile(
-      "s_nop 2\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v0], %[t00], %[ds0], %[v0]\n\t"
-      "ds_read_b128 %[y0], %[pa] offset:0\n\t"
-      "ds_read_b128 %[y1], %[pa] offset:32\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v1], %[t10], %[ds0], %[v1]\n\t"
-      "ds_read_b128 %[y2], %[pa] offset:64\n\t"
-      "ds_read_b128 %[y3], %[pa] offset:96\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v2], %[t20], %[ds0], %[v2]\n\t"
-      "ds_read_b128 %[y4], %[pb] offset:0\n\t"
-      "ds_read_b128 %[y5], %[pb] offset:32\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v3], %[t30], %[ds0], %[v3]\n\t"
-      "ds_read_b128 %[y6], %[pb] offset:64\n\t"
-      "ds_read_b128 %[y7], %[pb] offset:96\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v0], %[t01], %[ds1], %[v0]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v1], %[t11], %[ds1], %[v1]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v2], %[t21], %[ds1], %[v2]\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[v3], %[t31], %[ds1], %[v3]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      : [v0] "+a"(acc[0]), [v1] "+a"(acc[1]), [v2] "+a"(acc[2]), [v3] "+a"(acc[3]), [y0] "=&v"(y[0]),
-        [y1] "=&v"(y[1]), [y2] "=&v"(y[2]), [y3] "=&v"(y[3]), [y4] "=&v"(y[4]), [y5] "=&v"(y[5]),
-        [y6] "=&v"(y[6]), [y7] "=&v"(y[7])
-      : [t00] "v"(kT[0][0]), [t01] "v"(kT[0][1]), [t10] "v"(kT[1][0]), [t11] "v"(kT[1][1]), [t20] "v"(kT[2][0]),
-        [t21] "v"(kT[2][1]), [t30] "v"(kT[3][0]), [t31] "v"(kT[3][1]), [ds0] "v"(dsf[0]), [ds1] "v"(dsf[1]),
-        [pa] "v"(pa), [pb] "v"(pb)
-      : "memory");
-  }
-};
 template <> struct DqAsm<64> {
   static __device__ __forceinline__ void x1(f32x16& s, f32x16& p, const bf16x8 (&ka)[4], const bf16x8 (&va)[4],
                                             const bf16x8 (&qf)[4], const bf16x8 (&dof)[4], uint32_t pa, uint32_t pb,
@@ -870,8 +710,8 @@ template <> struct DkdvAsm<64> {
 };
 
 // ---------------------------------------------------------------------------
-// dK, dV at d = 128: the tile layout and one 32-query block as a single
-// scheduled instruction stream
+// The d = 128 tile layout (Q / dO tiles of the dK/dV kernel, K / V tiles of
+// the dQ kernel)
 // ---------------------------------------------------------------------------
 // gfx950 LDS has 64 banks of 4 bytes. A 16-byte read (ds_read_b128) is served
 // in four passes of 16 lanes: within each half-wave, the lanes whose quad
@@ -881,7 +721,7 @@ template <> struct DkdvAsm<64> {
 // cycle. With rows padded to D+16 elements every row read and every
 // transposed read of these tiles met two lanes per bank; this layout meets
 // none:
-// * row r (a query) holds its 128 bf16 as 16 chunks of 16 bytes at r * 320
+// * row r holds its 128 bf16 as 16 chunks of 16 bytes at r * 320
 //   bytes, chunk c in slot c ^ s(r) with s(r) = (q & 3) ^ ((q >> 2) & 1) for
 //   the row quad q = r / 4; slots 16-19 stay unused (the DMA moves zeros).
 // * transposed reads: a pass reads 64 contiguous bytes (chunks 4 db .. 4 db
@@ -897,323 +737,6 @@ template <> struct DkdvAsm<64> {
 // row reads at 64 j from one base for the even and one for the odd k-steps.
 constexpr int kRowBytes128 = 320;
 constexpr int kTileBytes128 = 64 * kRowBytes128;
-
-// The block as four groups of eight MFMAs. With one wave per SIMD the matrix
-// core only stays busy if the same wave's vector work and LDS reads issue
-// between its MFMAs; each instruction takes at least one issue slot of four
-// cycles (a transcendental two), so the work is spread to fill the eight
-// slots of 32 cycles that each group's MFMAs leave:
-//   S:  S = Q K^T              reads the (lse2, D) pairs, dO^T and Q^T
-//   dP: dP = dO V^T            P = exp2(S c - lse2) in place of S, two
-//                              elements per slot
-//   dV: dV^T += dO^T P         dS = P (dP - D) in place of dP, two elements
-//                              per slot; reads the next block's Q rows
-//   dK: dK^T += Q^T dS         reads the next block's dO rows
-// Each half-wave needs the same 16 (lse2, D) pairs: 8 broadcast 16-byte reads
-// per lane (all lanes of a half on one address cost no bank conflict).
-// Products, accumulation order and rounding are those of the d = 64 phases
-// (fma(S, c, -lse2), exp2, round to bf16; dP - D, times P).
-// Fixed registers, listed as clobbers: S/P v240-v255, dP/dS v224-v239,
-// P packed v216-v223 (k = 0-7 in v220-v223, 8-15 in v216-v219), dS packed
-// v208-v215 (0-7 in v212-v215), pair k (lse2, D) in v176+2k, v177+2k,
-// mask temporaries v174-v175, dO^T a128-a159 and Q^T a160-a191 (operand
-// [db][j] at 8 db + 4 j). Hazards the compiler cannot see in asm are
-// covered explicitly: at least 12 wait states (instructions, or s_nop
-// counts) between the last MFMA writing S or dP and the first vector read of
-// it, as the compiler itself requires for this MFMA on gfx950; an instruction
-// between a transcendental and the first read of its result; two wait states
-// before an MFMA reads vector-written packs.
-#define SFA_MF "v_mfma_f32_32x32x16_bf16 "
-// transposed read of (db, j, t) into AGPR pair dst: base a<t><j>, offset 64 db
-// (+ 20480 for the dO tile). SFA_BLOCK_ASM below is generated from the slot
-// plan above: after each MFMA, the reads and vector work of its slot.
-#define SFA_TR(dst, base, off) "ds_read_b64_tr_b16 " dst ", %[" base "] offset:" #off "\n\t"
-// Masked blocks: S = -inf (held in v175) where bit k of the lane's mask word
-// is clear; skipped when every lane's word is 0xffff.
-#define SFA_M1(k, sk)                                 \
-  "v_bfe_u32 v174, %[mword], " #k ", 1\n\t"           \
-  "v_cmp_ne_u32 vcc, 0, v174\n\t"                     \
-  "v_cndmask_b32 v" #sk ", v175, v" #sk ", vcc\n\t"
-#define SFA_MASK                                                                                        \
-  "v_cmp_ne_u32 vcc, 0xffff, %[mword]\n\t"                                                             \
-  "s_nop 1\n\t"                                                                                         \
-  "s_cbranch_vccz 5f\n\t"                                                                              \
-  "v_mov_b32 v175, 0xff800000\n\t"                                                                    \
-  SFA_M1(0, 240) SFA_M1(1, 241) SFA_M1(2, 242) SFA_M1(3, 243) SFA_M1(4, 244) SFA_M1(5, 245)            \
-  SFA_M1(6, 246) SFA_M1(7, 247) SFA_M1(8, 248) SFA_M1(9, 249) SFA_M1(10, 250) SFA_M1(11, 251)          \
-  SFA_M1(12, 252) SFA_M1(13, 253) SFA_M1(14, 254) SFA_M1(15, 255)                                      \
-  "5:\n\t"
-// sync 0: no hand-over; 1, 2, 3: wait for every LDS read of this stage and
-// until at most 0, vm1 or vm2 buffer->LDS loads of this wave are in flight,
-// then meet the other waves
-#define SFA_SYNC                     \
-  "s_cmp_eq_u32 %[sync], 0\n\t"      \
-  "s_cbranch_scc1 3f\n\t"            \
-  "s_waitcnt lgkmcnt(0)\n\t"         \
-  "s_cmp_eq_u32 %[sync], 1\n\t"      \
-  "s_cbranch_scc0 1f\n\t"            \
-  "s_waitcnt vmcnt(0)\n\t"           \
-  "s_branch 2f\n\t"                  \
-  "1:\n\t"                           \
-  "s_cmp_eq_u32 %[sync], 2\n\t"      \
-  "s_cbranch_scc0 4f\n\t"            \
-  "s_waitcnt vmcnt(%[vm1])\n\t"      \
-  "s_branch 2f\n\t"                  \
-  "4:\n\t"                           \
-  "s_waitcnt vmcnt(%[vm2])\n\t"      \
-  "2:\n\t"                           \
-  "s_barrier\n\t"                    \
-  "3:\n\t"                           \
-  "s_waitcnt lgkmcnt(15)\n\t"
-#define SFA_BLOCK_ASM \
-  "s_nop 2\n\t" \
-  SFA_MF "v[240:255], %[qa0], %[kf0], 0\n\t" \
-  "ds_read_b128 v[176:179], %[l0] offset:0\n\t" \
-  "ds_read_b128 v[180:183], %[l0] offset:16\n\t" \
-  "ds_read_b128 v[184:187], %[l0] offset:64\n\t" \
-  "ds_read_b128 v[188:191], %[l0] offset:80\n\t" \
-  "ds_read_b128 v[192:195], %[l1] offset:0\n\t" \
-  SFA_MF "v[240:255], %[qa1], %[kf1], v[240:255]\n\t" \
-  "ds_read_b128 v[196:199], %[l1] offset:16\n\t" \
-  "ds_read_b128 v[200:203], %[l1] offset:64\n\t" \
-  "ds_read_b128 v[204:207], %[l1] offset:80\n\t" \
-  SFA_TR("a[128:129]", "a00", 20480) \
-  SFA_TR("a[130:131]", "a10", 20480) \
-  SFA_MF "v[240:255], %[qa2], %[kf2], v[240:255]\n\t" \
-  SFA_TR("a[132:133]", "a01", 20480) \
-  SFA_TR("a[134:135]", "a11", 20480) \
-  SFA_TR("a[136:137]", "a00", 20544) \
-  SFA_TR("a[138:139]", "a10", 20544) \
-  SFA_TR("a[140:141]", "a01", 20544) \
-  SFA_MF "v[240:255], %[qa3], %[kf3], v[240:255]\n\t" \
-  SFA_TR("a[142:143]", "a11", 20544) \
-  SFA_TR("a[144:145]", "a00", 20608) \
-  SFA_TR("a[146:147]", "a10", 20608) \
-  SFA_TR("a[148:149]", "a01", 20608) \
-  SFA_TR("a[150:151]", "a11", 20608) \
-  SFA_MF "v[240:255], %[qa4], %[kf4], v[240:255]\n\t" \
-  SFA_TR("a[152:153]", "a00", 20672) \
-  SFA_TR("a[154:155]", "a10", 20672) \
-  SFA_TR("a[156:157]", "a01", 20672) \
-  SFA_TR("a[158:159]", "a11", 20672) \
-  SFA_TR("a[160:161]", "a00", 0) \
-  SFA_MF "v[240:255], %[qa5], %[kf5], v[240:255]\n\t" \
-  SFA_TR("a[162:163]", "a10", 0) \
-  SFA_TR("a[164:165]", "a01", 0) \
-  SFA_TR("a[166:167]", "a11", 0) \
-  SFA_TR("a[168:169]", "a00", 64) \
-  SFA_TR("a[170:171]", "a10", 64) \
-  SFA_MF "v[240:255], %[qa6], %[kf6], v[240:255]\n\t" \
-  SFA_TR("a[172:173]", "a01", 64) \
-  SFA_TR("a[174:175]", "a11", 64) \
-  SFA_TR("a[176:177]", "a00", 128) \
-  SFA_TR("a[178:179]", "a10", 128) \
-  SFA_TR("a[180:181]", "a01", 128) \
-  SFA_MF "v[240:255], %[qa7], %[kf7], v[240:255]\n\t" \
-  SFA_TR("a[182:183]", "a11", 128) \
-  SFA_TR("a[184:185]", "a00", 192) \
-  SFA_TR("a[186:187]", "a10", 192) \
-  SFA_TR("a[188:189]", "a01", 192) \
-  SFA_TR("a[190:191]", "a11", 192) \
-  SFA_MF "v[224:239], %[da0], %[vf0], 0\n\t" \
-  "s_nop 6\n\t" \
-  "s_waitcnt lgkmcnt(15)\n\t" \
-  SFA_MASK \
-  "v_fma_f32 v240, v240, %[c], -v176\n\t" \
-  "v_fma_f32 v241, v241, %[c], -v178\n\t" \
-  "v_exp_f32 v240, v240\n\t" \
-  "v_exp_f32 v241, v241\n\t" \
-  SFA_MF "v[224:239], %[da1], %[vf1], v[224:239]\n\t" \
-  "v_cvt_pk_bf16_f32 v220, v240, v241\n\t" \
-  "v_fma_f32 v242, v242, %[c], -v180\n\t" \
-  "v_fma_f32 v243, v243, %[c], -v182\n\t" \
-  "v_exp_f32 v242, v242\n\t" \
-  "v_exp_f32 v243, v243\n\t" \
-  SFA_MF "v[224:239], %[da2], %[vf2], v[224:239]\n\t" \
-  "v_cvt_pk_bf16_f32 v221, v242, v243\n\t" \
-  "v_fma_f32 v244, v244, %[c], -v184\n\t" \
-  "v_fma_f32 v245, v245, %[c], -v186\n\t" \
-  "v_exp_f32 v244, v244\n\t" \
-  "v_exp_f32 v245, v245\n\t" \
-  SFA_MF "v[224:239], %[da3], %[vf3], v[224:239]\n\t" \
-  "v_cvt_pk_bf16_f32 v222, v244, v245\n\t" \
-  "v_fma_f32 v246, v246, %[c], -v188\n\t" \
-  "v_fma_f32 v247, v247, %[c], -v190\n\t" \
-  "v_exp_f32 v246, v246\n\t" \
-  "v_exp_f32 v247, v247\n\t" \
-  SFA_MF "v[224:239], %[da4], %[vf4], v[224:239]\n\t" \
-  "v_cvt_pk_bf16_f32 v223, v246, v247\n\t" \
-  "v_fma_f32 v248, v248, %[c], -v192\n\t" \
-  "v_fma_f32 v249, v249, %[c], -v194\n\t" \
-  "v_exp_f32 v248, v248\n\t" \
-  "v_exp_f32 v249, v249\n\t" \
-  SFA_MF "v[224:239], %[da5], %[vf5], v[224:239]\n\t" \
-  "v_cvt_pk_bf16_f32 v216, v248, v249\n\t" \
-  "v_fma_f32 v250, v250, %[c], -v196\n\t" \
-  "v_fma_f32 v251, v251, %[c], -v198\n\t" \
-  "v_exp_f32 v250, v250\n\t" \
-  "v_exp_f32 v251, v251\n\t" \
-  SFA_MF "v[224:239], %[da6], %[vf6], v[224:239]\n\t" \
-  "v_cvt_pk_bf16_f32 v217, v250, v251\n\t" \
-  "v_fma_f32 v252, v252, %[c], -v200\n\t" \
-  "v_fma_f32 v253, v253, %[c], -v202\n\t" \
-  "v_exp_f32 v252, v252\n\t" \
-  "v_exp_f32 v253, v253\n\t" \
-  SFA_MF "v[224:239], %[da7], %[vf7], v[224:239]\n\t" \
-  "v_cvt_pk_bf16_f32 v218, v252, v253\n\t" \
-  "v_fma_f32 v254, v254, %[c], -v204\n\t" \
-  "v_fma_f32 v255, v255, %[c], -v206\n\t" \
-  "v_exp_f32 v254, v254\n\t" \
-  "v_exp_f32 v255, v255\n\t" \
-  SFA_SYNC \
-  "v_cvt_pk_bf16_f32 v219, v254, v255\n\t" \
-  "s_nop 1\n\t" \
-  SFA_MF "%[dv0], a[128:131], v[220:223], %[dv0]\n\t" \
-  "ds_read_b128 %[qa0], %[re] offset:0\n\t" \
-  "s_nop 1\n\t" \
-  "v_sub_f32 v224, v224, v177\n\t" \
-  "v_sub_f32 v225, v225, v179\n\t" \
-  "v_mul_f32 v224, v240, v224\n\t" \
-  "v_mul_f32 v225, v241, v225\n\t" \
-  "v_cvt_pk_bf16_f32 v212, v224, v225\n\t" \
-  SFA_MF "%[dv1], a[136:139], v[220:223], %[dv1]\n\t" \
-  "ds_read_b128 %[qa1], %[ro] offset:0\n\t" \
-  "v_sub_f32 v226, v226, v181\n\t" \
-  "v_sub_f32 v227, v227, v183\n\t" \
-  "v_mul_f32 v226, v242, v226\n\t" \
-  "v_mul_f32 v227, v243, v227\n\t" \
-  "v_cvt_pk_bf16_f32 v213, v226, v227\n\t" \
-  SFA_MF "%[dv2], a[144:147], v[220:223], %[dv2]\n\t" \
-  "ds_read_b128 %[qa2], %[re] offset:64\n\t" \
-  "v_sub_f32 v228, v228, v185\n\t" \
-  "v_sub_f32 v229, v229, v187\n\t" \
-  "v_mul_f32 v228, v244, v228\n\t" \
-  "v_mul_f32 v229, v245, v229\n\t" \
-  "v_cvt_pk_bf16_f32 v214, v228, v229\n\t" \
-  SFA_MF "%[dv3], a[152:155], v[220:223], %[dv3]\n\t" \
-  "ds_read_b128 %[qa3], %[ro] offset:64\n\t" \
-  "v_sub_f32 v230, v230, v189\n\t" \
-  "v_sub_f32 v231, v231, v191\n\t" \
-  "v_mul_f32 v230, v246, v230\n\t" \
-  "v_mul_f32 v231, v247, v231\n\t" \
-  "v_cvt_pk_bf16_f32 v215, v230, v231\n\t" \
-  SFA_MF "%[dv0], a[132:135], v[216:219], %[dv0]\n\t" \
-  "ds_read_b128 %[qa4], %[re] offset:128\n\t" \
-  "v_sub_f32 v232, v232, v193\n\t" \
-  "v_sub_f32 v233, v233, v195\n\t" \
-  "v_mul_f32 v232, v248, v232\n\t" \
-  "v_mul_f32 v233, v249, v233\n\t" \
-  "v_cvt_pk_bf16_f32 v208, v232, v233\n\t" \
-  SFA_MF "%[dv1], a[140:143], v[216:219], %[dv1]\n\t" \
-  "ds_read_b128 %[qa5], %[ro] offset:128\n\t" \
-  "v_sub_f32 v234, v234, v197\n\t" \
-  "v_sub_f32 v235, v235, v199\n\t" \
-  "v_mul_f32 v234, v250, v234\n\t" \
-  "v_mul_f32 v235, v251, v235\n\t" \
-  "v_cvt_pk_bf16_f32 v209, v234, v235\n\t" \
-  SFA_MF "%[dv2], a[148:151], v[216:219], %[dv2]\n\t" \
-  "ds_read_b128 %[qa6], %[re] offset:192\n\t" \
-  "v_sub_f32 v236, v236, v201\n\t" \
-  "v_sub_f32 v237, v237, v203\n\t" \
-  "v_mul_f32 v236, v252, v236\n\t" \
-  "v_mul_f32 v237, v253, v237\n\t" \
-  "v_cvt_pk_bf16_f32 v210, v236, v237\n\t" \
-  SFA_MF "%[dv3], a[156:159], v[216:219], %[dv3]\n\t" \
-  "ds_read_b128 %[qa7], %[ro] offset:192\n\t" \
-  "v_sub_f32 v238, v238, v205\n\t" \
-  "v_sub_f32 v239, v239, v207\n\t" \
-  "v_mul_f32 v238, v254, v238\n\t" \
-  "v_mul_f32 v239, v255, v239\n\t" \
-  "v_cvt_pk_bf16_f32 v211, v238, v239\n\t" \
-  "s_waitcnt lgkmcnt(8)\n\t" \
-  "s_nop 1\n\t" \
-  SFA_MF "%[dk0], a[160:163], v[212:215], %[dk0]\n\t" \
-  "ds_read_b128 %[da0], %[re] offset:20480\n\t" \
-  "ds_read_b128 %[da1], %[ro] offset:20480\n\t" \
-  SFA_MF "%[dk1], a[168:171], v[212:215], %[dk1]\n\t" \
-  "ds_read_b128 %[da2], %[re] offset:20544\n\t" \
-  "ds_read_b128 %[da3], %[ro] offset:20544\n\t" \
-  SFA_MF "%[dk2], a[176:179], v[212:215], %[dk2]\n\t" \
-  "ds_read_b128 %[da4], %[re] offset:20608\n\t" \
-  "ds_read_b128 %[da5], %[ro] offset:20608\n\t" \
-  SFA_MF "%[dk3], a[184:187], v[212:215], %[dk3]\n\t" \
-  "ds_read_b128 %[da6], %[re] offset:20672\n\t" \
-  "ds_read_b128 %[da7], %[ro] offset:20672\n\t" \
-  SFA_MF "%[dk0], a[164:167], v[208:211], %[dk0]\n\t" \
-  SFA_MF "%[dk1], a[172:175], v[208:211], %[dk1]\n\t" \
-  SFA_MF "%[dk2], a[180:183], v[208:211], %[dk2]\n\t" \
-  SFA_MF "%[dk3], a[188:191], v[208:211], %[dk3]\n\t" \
-  "s_waitcnt lgkmcnt(0)\n\t" \
-  "s_nop 3\n\t"
-#define SFA_BLOCK_OPERANDS                                                                              \
-  : [qa0] "+v"(qa[0]), [qa1] "+v"(qa[1]), [qa2] "+v"(qa[2]), [qa3] "+v"(qa[3]), [qa4] "+v"(qa[4]),        \
-    [qa5] "+v"(qa[5]), [qa6] "+v"(qa[6]), [qa7] "+v"(qa[7]), [da0] "+v"(da[0]), [da1] "+v"(da[1]),        \
-    [da2] "+v"(da[2]), [da3] "+v"(da[3]), [da4] "+v"(da[4]), [da5] "+v"(da[5]), [da6] "+v"(da[6]),        \
-    [da7] "+v"(da[7]), [dk0] "+a"(dk[0]), [dk1] "+a"(dk[1]), [dk2] "+a"(dk[2]), [dk3] "+a"(dk[3]),        \
-    [dv0] "+a"(dv[0]), [dv1] "+a"(dv[1]), [dv2] "+a"(dv[2]), [dv3] "+a"(dv[3])                            \
-  : [kf0] "a"(kf[0]), [kf1] "a"(kf[1]), [kf2] "a"(kf[2]), [kf3] "a"(kf[3]), [kf4] "a"(kf[4]),            \
-    [kf5] "a"(kf[5]), [kf6] "a"(kf[6]), [kf7] "a"(kf[7]), [vf0] "a"(vf[0]), [vf1] "a"(vf[1]),             \
-    [vf2] "a"(vf[2]), [vf3] "a"(vf[3]), [vf4] "a"(vf[4]), [vf5] "a"(vf[5]), [vf6] "a"(vf[6]),             \
-    [vf7] "a"(vf[7]), [a00] "v"(tr[0]), [a10] "v"(tr[1]), [a01] "v"(tr[2]), [a11] "v"(tr[3]),              \
-    [l0] "v"(lp[0]), [l1] "v"(lp[1]), [re] "v"(re), [ro] "v"(ro), [c] "s"(c), [mword] "v"(mword),           \
-    [sync] "s"(sync),                                                                                   \
-    [vm1] "n"(VM1), [vm2] "n"(VM1 + 1)                                                                  \
-  : "memory", "vcc", "scc", SFA_CLOBBER_V, SFA_CLOBBER_A
-#define SFA_CLOBBER_V "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
-#define SFA_CLOBBER_A                                                                                   \
-  "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", \
-      "a141", "a142", "a143", "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152",      \
-      "a153", "a154", "a155", "a156", "a157", "a158", "a159", "a160", "a161", "a162", "a163", "a164",      \
-      "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175", "a176",      \
-      "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188",      \
-      "a189", "a190", "a191"
-
-// qa, da: this block's Q and dO rows in, the next block's out (read at re /
-// ro plus 64 j, the dO tile 20480 bytes above the Q tile); tr: bases of this
-// block's transposed reads for (t, j) = (0,0), (1,0), (0,1), (1,1) in the Q
-// tile; lp: bases of the (lse2, D) pair reads (registers 0-7 at lp[0] + 0,
-// 16, 64, 80, registers 8-15 at lp[1] + the same); mword: the lane's mask
-// word. sync != 0
-// marks the block that hands the ring to the next step (see SFA_SYNC; VM1 is
-// a wave's buffer->LDS load count per step).
-template <int VM1>
-__device__ __forceinline__ void dkdv_block128(bf16x8 (&qa)[8], bf16x8 (&da)[8], f32x16 (&dk)[4], f32x16 (&dv)[4],
-                                              const bf16x8 (&kf)[8], const bf16x8 (&vf)[8], const uint32_t (&tr)[4],
-                                              const uint32_t (&lp)[2], uint32_t re, uint32_t ro, float c,
-                                              uint32_t mword, int sync) {
-  asm volatile(SFA_BLOCK_ASM SFA_BLOCK_OPERANDS);
-}
-#undef SFA_MF
-#undef SFA_TR
-#undef SFA_BLOCK_ASM
-#undef SFA_M1
-#undef SFA_MASK
-#undef SFA_SYNC
-#undef SFA_BLOCK_OPERANDS
-#undef SFA_CLOBBER_V
-#undef SFA_CLOBBER_A
-
-// The first block's Q and dO rows (re / ro as in dkdv_block128), in one asm
-// block that waits for its results.
-__device__ __forceinline__ void rows128(bf16x8 (&qa)[8], bf16x8 (&da)[8], uint32_t re, uint32_t ro) {
-  asm volatile(
-      "ds_read_b128 %[q0], %[re] offset:0\n\tds_read_b128 %[q1], %[ro] offset:0\n\t"
-      "ds_read_b128 %[q2], %[re] offset:64\n\tds_read_b128 %[q3], %[ro] offset:64\n\t"
-      "ds_read_b128 %[q4], %[re] offset:128\n\tds_read_b128 %[q5], %[ro] offset:128\n\t"
-      "ds_read_b128 %[q6], %[re] offset:192\n\tds_read_b128 %[q7], %[ro] offset:192\n\t"
-      "ds_read_b128 %[d0], %[re] offset:20480\n\tds_read_b128 %[d1], %[ro] offset:20480\n\t"
-      "ds_read_b128 %[d2], %[re] offset:20544\n\tds_read_b128 %[d3], %[ro] offset:20544\n\t"
-      "ds_read_b128 %[d4], %[re] offset:20608\n\tds_read_b128 %[d5], %[ro] offset:20608\n\t"
-      "ds_read_b128 %[d6], %[re] offset:20672\n\tds_read_b128 %[d7], %[ro] offset:20672\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : [q0] "=&v"(qa[0]), [q1] "=&v"(qa[1]), [q2] "=&v"(qa[2]), [q3] "=&v"(qa[3]), [q4] "=&v"(qa[4]),
-        [q5] "=&v"(qa[5]), [q6] "=&v"(qa[6]), [q7] "=&v"(qa[7]), [d0] "=&v"(da[0]), [d1] "=&v"(da[1]),
-        [d2] "=&v"(da[2]), [d3] "=&v"(da[3]), [d4] "=&v"(da[4]), [d5] "=&v"(da[5]), [d6] "=&v"(da[6]),
-        [d7] "=&v"(da[7])
-      : [re] "v"(re), [ro] "v"(ro)
-      : "memory");
-}
-
 
 // ---------------------------------------------------------------------------
 // dK, dV: key-stationary
@@ -1439,21 +962,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
-// dK, dV at d = 128: the kernel above with the tile layout and the block
-// stream of dkdv_block128 (same work items, ring, masks and epilogue).
+// ---------------------------------------------------------------------------
+// dK, dV at d = 128: the work items and products of bwd_dkdv_kernel in the
+// 320-byte tile layout, with the whole step loop as one asm stream
+// (attn_dkdv128_stream.h, written by gen_dkdv128_stream.py), so that no
+// compiled code runs between blocks: the DMA offsets advance by per-step
+// increments, and the (lse2, D) pairs of a step come by DMA too (each wave
+// moves 16 queries' pairs, into a KiB of its own). Masks: the query tiles
+// whose every query sees every key of the wave form one range per wave,
+// tested with two scalar instructions; the other steps (the diagonal, the
+// window's end, a ragged last tile, and the step after the last, which
+// closes the stream) test each score against its query and the lane's key.
+// The query tiles are walked from the last down, so that the work groups of
+// an XCD, which start together, read the same Q and dO tiles at about the
+// same time (from L2). Rows past the end of a sequence load the next rows of
+// the buffer (or zeros past its end), which the masks exclude.
+// ---------------------------------------------------------------------------
+constexpr int kKvTile = 20480;                 // bytes of a Q (or dO) tile
+constexpr int kKvDRegion = 3 * kKvTile;        // the 3 dO tiles follow the 3 Q tiles
+constexpr int kKvLRegion = 6 * kKvTile;        // then the pairs, 4 KiB per stage
+constexpr int kKvLStage = 4096;
+
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
-  constexpr int D = 128, KD = D / 16, DB = D / 32;
-  constexpr int RBU = kRowBytes128 / 16;               // 16-byte slots per row
-  constexpr int CH = BT * RBU / 64;                    // 1 KiB DMA chunks per tile
-  constexpr int NCW = 2 * CH / kWaves;                 // chunks per wave (wave 0 also moves lse2/D)
-  static_assert(2 * CH % kWaves == 0 && CH % kWaves == 0, "chunks must split evenly over the waves");
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdParams p) {
+  constexpr int D = 128;
   constexpr int KB = kWaves * 32;                      // keys per work group
-  constexpr int SK = 3;                                // LDS stages: step s + 2 loads while s runs
-  // per stage: the Q tile, then the dO tile kTileBytes128 above it
-  __shared__ __attribute__((aligned(16))) u16 tl[SK][2][kTileBytes128 / 2];
-  __shared__ __attribute__((aligned(16))) float ls[SK][2 * 64 * 2];   // [query][lse2, D], 1 KiB per stage
-  static_assert(kTileBytes128 == 20480, "the block stream's immediate offsets assume 20480-byte tiles");
+  static_assert(kKvTile == kTileBytes128, "the stream's offsets assume 20480-byte tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kKvLRegion + 3 * kKvLStage];
 
   const int pstride = MODE == 0 ? p.pstride : 1;
   const int window = MODE == 2 ? p.window : 0;
@@ -1475,209 +1010,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_kernel(BwdParams p) {
   const int k0 = wg_k0 + wave * 32;
   const int vk = k0 + l32;
   const bool kvalid = vk < p.Lv;
-  const int wg_klast = min(wg_k0 + KB, p.Lv) - 1;
   const int qt_begin = wg_k0 / BT;
-  const int qlast = window > 0 ? min(p.Lv - 1, wg_klast + window - 1) : p.Lv - 1;
-  const int qt_end = qlast / BT + 1;
-  const int nsteps = (qt_end - qt_begin) * p.G;
-
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
-  const __amdgpu_buffer_rsrc_t dors = make_rsrc(p.dout, p.q_bytes);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k, p.kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v, p.kv_bytes);
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lsed, p.lsed_bytes);
-  const uint32_t q_pos_bytes = uint32_t(p.hq) * D * 2;
-  const uint32_t lbase_seq = uint32_t(b * p.nseq + sq) * p.hq;
-
-  bf16x8 kf[KD], vf[KD];
-  {
-    const uint32_t koff = (uint32_t(base_row + vk * pstride) * p.hkv + kvh) * D * 2;
-    load_rows<D>(kf, krs, koff, kvalid, hh);
-    load_rows<D>(vf, vrs, koff, kvalid, hh);
-  }
-
-  // step s: query tile qt_begin + s / G, query head kvh*G + s % G. Chunk c of
-  // a tile (c < CH: Q, else dO) covers slots 64 (c mod CH) + lane; slot sl is
-  // 16-byte slot u = sl mod RBU of row sl / RBU and holds chunk u ^ s(row)
-  // (slots 16-19 read zeros); wave w moves chunks w, w + 4, ...; wave 0 also
-  // moves the 64 queries' (lse2, D) pairs, 16 bytes per lane.
-  auto issue = [&](int st, int qt, int h) {
-    const uint32_t tbase = uint32_t(base_row + qt * BT * pstride) * q_pos_bytes + uint32_t(h) * D * 2;
-#pragma unroll
-    for (int j = 0; j < NCW; ++j) {
-      const int c = wave + j * kWaves;
-      const int cc = j < NCW / 2 ? c : c - CH;          // waves 0-3 cover Q chunks for j < NCW / 2
-      const int sl = cc * 64 + lane;
-      const int row = sl / RBU, u = sl % RBU;
-      const bool ok = u < 16 && qt * BT + row < p.Lv;
-      const uint32_t off =
-          ok ? tbase + uint32_t(row * pstride) * q_pos_bytes + uint32_t(u ^ row_swizzle128(row >> 2)) * 16 : kOobOffset;
-      dma16(j < NCW / 2 ? qrs : dors, &tl[st][j < NCW / 2 ? 0 : 1][cc * 512], off);
-    }
-    if (wave == 0) {
-      const int iq = qt * BT + 2 * lane;
-      const uint32_t off = lane < 32 && iq < p.Lv ? ((lbase_seq + h) * p.Lv + iq) * 8 : kOobOffset;
-      dma16(lrs, &ls[st][0], off);
-    }
-  };
-  auto wait_prev = [&](bool keep) {
-    if (!keep) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCW + 1) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCW) : "memory");
-  };
-
-  const uint32_t lim = MODE == 2 ? uint32_t(window) : 0x80000000u;
-  // lane constants of the layout: row reads of a 32-row block (sigma order,
-  // chunks 2 j + hh: base re for even j, ro for odd j, each plus 64 (j / 2))
-  uint32_t rofe, rofo;
-  {
-    const int r = sigma(l32), sw = row_swizzle128(r >> 2);
-    const uint32_t rb = uint32_t(r * kRowBytes128 + 16 * (hh ^ (sw & 1)));
-    rofe = rb + 32 * (sw >> 1);
-    rofo = rb + 32 - 32 * (sw >> 1);
-  }
-  // transposed reads of a 32-row block for (t, j): rows e + row offset
-  // (j = 0: 20 vh + 8 t; j = 1: 12 vh + 4 + 8 t), bytes 32 (grp & 1) + 8 (gi & 3)
-  uint32_t trof[4];
-  {
-    const int grp = lane >> 4, gi = lane & 15, vh = grp >> 1, e = gi >> 2;
-    const int c0 = 2 * (grp & 1) + ((gi & 3) >> 1), half = gi & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = i & 1, jj = i >> 1;
-      const int ro = jj ? 12 * vh + 4 + 8 * tt : 20 * vh + 8 * tt;
-      trof[i] = uint32_t((e + ro) * kRowBytes128 + 16 * (c0 ^ row_swizzle128(ro >> 2)) + 8 * half);
-    }
-  }
-  // (lse2, D) pairs: registers 4 g .. 4 g + 3 hold queries reg_key_offset(g, hh) + 0..3,
-  // 8 bytes each; g = 0, 1 lie 64 bytes apart, as do g = 2, 3
-  const uint32_t lpo0 = 8 * reg_key_offset(0, hh), lpo1 = 8 * reg_key_offset(2, hh);
-
-  f32x16 dkacc[DB], dvacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
-
-  // steps s and s + 2 as (stage, query tile, head offset g = s mod G), advanced
-  // by counters rather than divisions
-  int st = 0, qt = qt_begin, g = 0;
-  int st2 = 2, qt2 = qt_begin + 2 / p.G, g2 = 2 % p.G;
-  if (nsteps > 0) {
-    issue(0, qt_begin, kvh * p.G);
-    if (nsteps > 1) issue(1, qt_begin + 1 / p.G, kvh * p.G + 1 % p.G);
-    wait_prev(nsteps > 1);
-    asm volatile("s_barrier" ::: "memory");
-  }
-  constexpr uint32_t kStageBytes = 2 * kTileBytes128, kLsBytes = 2 * 64 * 2 * 4;
-  const uint32_t t0 = lds_addr(&tl[0][0][0]), ls0 = lds_addr(&ls[0][0]);
-  bf16x8 qa[KD], da[KD];
-  if (nsteps > 0) rows128(qa, da, t0 + rofe, t0 + rofo);
-  for (int s = 0; s < nsteps; ++s) {
-    // stage (s + 2) % 3 held step s - 1, which every wave has finished
-    if (s + 2 < nsteps) issue(st2, qt2, kvh * p.G + g2);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qf0 = qt * BT + qb * 32;        // first query of the block
-      // the block is full when every query sees every key of the wave and all queries are valid
-      const bool full = qf0 + 31 < p.Lv && k0 + 31 <= qf0 && (window == 0 || qf0 + 31 - k0 < window);
-      // masked blocks: bit r of the lane's word set when register r's query sees its key
-      uint32_t mword = 0xffff;
-      if (!full) {
-        mword = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int iq = qf0 + reg_key_offset(r >> 2, hh) + (r & 3);
-          mword |= uint32_t(iq < p.Lv && uint32_t(iq - vk) < lim) << r;
-        }
-      }
-      const uint32_t blk = t0 + st * kStageBytes + uint32_t(qb * 32 * kRowBytes128);
-      const uint32_t tr[4] = {blk + trof[0], blk + trof[1], blk + trof[2], blk + trof[3]};
-      const uint32_t lsb = ls0 + st * kLsBytes + 8 * qb * 32;
-      const uint32_t lp[2] = {lsb + lpo0, lsb + lpo1};
-      // the next block's rows: (s, 1) from this stage, or (s + 1, 0) from the
-      // next one, published by this block's hand-over (on the last step a
-      // harmless read of a stage no DMA writes)
-      const uint32_t nblk = qb == 0 ? t0 + st * kStageBytes + uint32_t(32 * kRowBytes128)
-                                    : t0 + (st == SK - 1 ? 0 : st + 1) * kStageBytes;
-      const int sync = qb == 0 || s + 1 >= nsteps ? 0 : s + 2 >= nsteps ? 1 : wave == 0 ? 3 : 2;
-      dkdv_block128<NCW>(qa, da, dkacc, dvacc, kf, vf, tr, lp, nblk + rofe, nblk + rofo, p.c, mword, sync);
-    }
-    st = st == SK - 1 ? 0 : st + 1;
-    if (++g == p.G) g = 0, ++qt;
-    st2 = st2 == SK - 1 ? 0 : st2 + 1;
-    if (++g2 == p.G) g2 = 0, ++qt2;
-  }
-  // accumulators written by MFMAs are read by the epilogue below
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
-
-  if (!kvalid) return;
-  const size_t krow = (size_t(base_row + vk * pstride) * p.hkv + kvh) * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 kv, vv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        kv[r] = (__bf16)(dkacc[db][4 * g + r] * p.scale);
-        vv[r] = (__bf16)dvacc[db][4 * g + r];
-      }
-      *reinterpret_cast<bf16x4*>(p.dk + krow + db * 32 + 8 * g + 4 * hh) = kv;
-      *reinterpret_cast<bf16x4*>(p.dv + krow + db * 32 + 8 * g + 4 * hh) = vv;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dK, dV at d = 128, intra and cross_full: the work items, tile layout and
-// products of bwd_dkdv128_kernel, with the whole step loop as one asm stream
-// (attn_dkdv128_stream.h, written by gen_dkdv128_stream.py), so that no
-// compiled code runs between blocks: the DMA offsets advance by per-step
-// increments, the (lse2, D) pairs of a step come by DMA too (each wave moves
-// 16 queries' pairs, into a KiB of its own), and the masks are per-lane words
-// formed once (the first two query tiles hold the diagonal, a ragged last
-// tile masks the queries past the end; the step after the last, which
-// closes the stream, is masked whole). The query tiles are walked from the
-// last down, so that the work groups of an XCD, which start together, read
-// the same Q and dO tiles at about the same time (from L2). Rows past the end of a sequence load
-// the next rows of the buffer (or zeros past its end), which those masks
-// exclude.
-// ---------------------------------------------------------------------------
-constexpr int kKvTile = 20480;                 // bytes of a Q (or dO) tile
-constexpr int kKvDRegion = 3 * kKvTile;        // the 3 dO tiles follow the 3 Q tiles
-constexpr int kKvLRegion = 6 * kKvTile;        // then the pairs, 4 KiB per stage
-constexpr int kKvLStage = 4096;
-
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdParams p) {
-  constexpr int D = 128;
-  constexpr int KB = kWaves * 32;                      // keys per work group
-  static_assert(kKvTile == kTileBytes128, "the stream's offsets assume 20480-byte tiles");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kKvLRegion + 3 * kKvLStage];
-
-  const int pstride = MODE == 0 ? p.pstride : 1;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-
-  // work item: (batch, virtual sequence, kv head, key block), heaviest first
-  const int t = (blockIdx.x & 7) * p.per_xcd_k + (blockIdx.x >> 3);
-  if (t >= p.total_k) return;
-  const int unit = t / p.nkb;
-  const int kbk = t - unit * p.nkb;
-  const int kvh = unit % p.hkv;
-  const int bs = unit / p.hkv;
-  const int sq = bs % p.nseq;
-  const int b = bs / p.nseq;
-  const int base_row = b * p.S + sq;
-  const int wg_k0 = kbk * KB;
-  const int k0 = wg_k0 + wave * 32;
-  const int vk = k0 + l32;
-  const bool kvalid = vk < p.Lv;
-  const int qt_begin = wg_k0 / BT;
-  const int qt_end = (p.Lv - 1) / BT + 1;
+  const int64_t W = window > 0 ? window : 0x7fffffff;
+  const int qt_end = int(min<int64_t>(p.Lv - 1, int64_t(min(wg_k0 + KB, p.Lv) - 1) + W - 1) / BT) + 1;
   const int G = p.G;
   const int T = (qt_end - qt_begin) * G;               // steps: (query tile, head of the group)
 
@@ -1776,25 +1111,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdPara
   const uint32_t lp0 = lpb + 8 * uint32_t(reg_key_offset(0, hh) - 16 * hh);
   const uint32_t lp1 = lpb + 8 * uint32_t(reg_key_offset(2, hh) - 16 * hh);
 
-  // mask words: bit r set when register r's query (query tile qt, block qb)
-  // is valid and sees the lane's key
-  auto word = [&](int qt, int qb) {
-    uint32_t w = 0;
+  // masks: the query tiles whose every query (valid, and within the window)
+  // sees every key of the wave (qt*64 >= k0 + 31, qt*64 + 63 - k0 < W,
+  // qt*64 + 63 < Lv), as processed indices fd .. fd + fc - 1; the other steps
+  // test each score (lane key vk, query offsets by register group in off)
+  auto fdiv64 = [](int64_t x) { return x >= 0 ? x / BT : -((-x + BT - 1) / BT); };   // floor(x / 64)
+  const int64_t fa = max<int64_t>(qt_begin, (int64_t(k0) + 31 + BT - 1) / BT);
+  const int64_t fb = min<int64_t>(qt_end - 1, min(fdiv64(int64_t(k0) + W - BT), fdiv64(int64_t(p.Lv) - BT)));
+  const uint32_t fd = __builtin_amdgcn_readfirstlane(uint32_t(qt_end - 1 - fb));
+  const uint32_t fc = __builtin_amdgcn_readfirstlane(uint32_t(max<int64_t>(0, fb - fa + 1)));
+  const uint32_t qtop = __builtin_amdgcn_readfirstlane(uint32_t((qt_end - 1) * BT));
+  const uint32_t Wn = uint32_t(W), Lvn = uint32_t(p.Lv);
+  uint32_t off = 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int iq = qt * BT + qb * 32 + reg_key_offset(r >> 2, hh) + (r & 3);
-      w |= uint32_t(iq < p.Lv && iq >= vk) << r;
-    }
-    return w;
-  };
-  const uint32_t w00 = word(qt_begin, 0), w01 = word(qt_begin, 1);
-  const uint32_t w10 = word(qt_begin + 1, 0), w11 = word(qt_begin + 1, 1);
-  const uint32_t wl0 = word(qt_end - 1, 0), wl1 = word(qt_end - 1, 1);
-  // the query tiles go from the last down: qt_begin + 1 and qt_begin come after
-  // tb1 and tb0 tiles, a ragged last tile first
-  const uint32_t tb0 = __builtin_amdgcn_readfirstlane(uint32_t(qt_end - 1 - qt_begin));
-  const uint32_t tb1 = __builtin_amdgcn_readfirstlane(uint32_t(qt_end - 2 - qt_begin));
-  const uint32_t tlast = __builtin_amdgcn_readfirstlane(p.Lv % BT ? 0u : 0xffffffffu);
+  for (int g = 0; g < 4; ++g) off |= uint32_t(reg_key_offset(g, hh)) << (8 * g);
 
   const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(wave) * 1024);
   const uint32_t Tn = __builtin_amdgcn_readfirstlane(uint32_t(T));
@@ -1818,14 +1148,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdPara
         [cf0] "+v"(cf[0]), [cf1] "+v"(cf[1]), [cf2] "+v"(cf[2]), [cf3] "+v"(cf[3]), [cf4] "+v"(cf[4]),
         [cl] "+v"(cl)
       : [kf] "{a[128:159]}"(kf), [vf] "{a[160:191]}"(vf), [c] "s"(p.c), [T] "s"(Tn), [G] "s"(Gn),
-        [tlast] "s"(tlast), [tb0] "s"(tb0), [tb1] "s"(tb1), [incw] "s"(incw), [inclw] "s"(inclw), [inclh] "s"(inclh),
+        [fd] "s"(fd), [fc] "s"(fc), [qtop] "s"(qtop), [W] "s"(Wn), [Lv] "s"(Lvn), [incw] "s"(incw), [inclw] "s"(inclw), [inclh] "s"(inclh),
         [rq] "s"(qrs), [rd] "s"(dors), [rl] "s"(lrs), [lw] "s"(lw),
         [qe] "v"(qe), [qo] "v"(qo), [ge] "v"(qe + kKvDRegion), [go] "v"(qo + kKvDRegion), [q00] "v"(tq[0]),
         [q10] "v"(tq[1]), [q01] "v"(tq[2]), [q11] "v"(tq[3]), [d00] "v"(tq[0] + kKvDRegion),
         [d10] "v"(tq[1] + kKvDRegion), [d01] "v"(tq[2] + kKvDRegion), [d11] "v"(tq[3] + kKvDRegion),
-        [lp0] "v"(lp0), [lp1] "v"(lp1), [w00] "v"(w00), [w01] "v"(w01), [w10] "v"(w10), [w11] "v"(w11),
-        [wl0] "v"(wl0), [wl1] "v"(wl1)
-      : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", "s90", SFA_DKDV128_CLOBBER_V,
+        [lp0] "v"(lp0), [lp1] "v"(lp1), [vk] "v"(uint32_t(vk)), [off] "v"(off)
+      : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91", "s92", "s93",
+        SFA_DKDV128_CLOBBER_V,
         SFA_DKDV128_CLOBBER_A);
 
   if (kvalid) {
@@ -1852,7 +1182,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdPara
 }
 
 // ---------------------------------------------------------------------------
-// dQ at d = 128, intra and cross_full: one wave per SIMD with 64 queries (two
+// dQ at d = 128: one wave per SIMD with 64 queries (two
 // blocks of 32) of one query head, so that every K / V row read from LDS
 // feeds twice as many MFMAs as in bwd_dq_kernel. The work group's 4 waves
 // share the key tiles: HG query heads of one key/value head times 4 / HG
@@ -1863,10 +1193,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv128_stream_kernel(BwdPara
 // Products, their accumulation order and the rounding of dS are those of
 // bwd_dq_kernel. K and V tiles go by DMA through 3 stages (tile t + 2 while
 // t runs), in the rows of 320 bytes of the d = 128 dK/dV tiles (row reads
-// and transposed reads free of bank conflicts). Tiles up to the diagonal of
-// the wave's queries are full; the diagonal one takes the lanes' mask words,
-// later ones (other waves' queries, and the extra tile that closes the
-// stream) are masked whole.
+// and transposed reads free of bank conflicts). The key tiles whose every key
+// every query of the wave admits form one range per wave, tested with two
+// scalar instructions; the others (the diagonal, the window's start, tiles
+// past the wave's queries, and the extra tile that closes the stream) test
+// each score against the lane's query.
 // ---------------------------------------------------------------------------
 constexpr int kDqStage = 20480;                // bytes per K (or V) stage
 constexpr int kDqVRegion = 3 * kDqStage;       // V stages after the 3 K stages
@@ -1878,6 +1209,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq128_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[6 * kDqStage];
 
   const int pstride = MODE == 0 ? p.pstride : 1;
+  const int window = MODE == 2 ? p.window : 0;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -1899,7 +1231,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq128_kernel(BwdParams p) {
   const int wg_q0 = qb * PS;
   const int q0 = wg_q0 + (wave / p.HG) * 64;
   const int wg_qlast = min(wg_q0 + PS, p.Lv) - 1;
-  const int T = wg_qlast / BT + 1;
+  const int kt_begin = window > 0 ? max(0, wg_q0 - window + 1) / BT : 0;
+  const int T = wg_qlast / BT + 1 - kt_begin;           // key tiles of the work group
   const int base_row = b * p.S + sq;
 
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q, p.q_bytes);
@@ -1949,9 +1282,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq128_kernel(BwdParams p) {
   auto tile_base = [&](int kt) { return uint32_t(base_row + kt * BT * pstride) * kv_pos_bytes; };
   // tile 0 into stage 0, zeros into the K tile of stage 2 (the first iteration
   // reads its K^T as that of a tile -1, whose dS are 0), tile 1 into stage 1
+  // (tile i of the loop is key tile kt_begin + i)
 #pragma unroll
   for (int x = 0; x < 5; ++x) {
-    const uint32_t o0 = cf[x] < kOobOffset ? cf[x] + tile_base(0) : kOobOffset;
+    const uint32_t o0 = cf[x] < kOobOffset ? cf[x] + tile_base(kt_begin) : kOobOffset;
     dma16(krs, &lds[(wave + 4 * x) * 1024], o0);
     dma16(vrs, &lds[kDqVRegion + (wave + 4 * x) * 1024], o0);
   }
@@ -1959,13 +1293,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq128_kernel(BwdParams p) {
   for (int x = 0; x < 5; ++x) dma16(krs, &lds[2 * kDqStage + (wave + 4 * x) * 1024], kOobOffset);
 #pragma unroll
   for (int x = 0; x < 5; ++x) {
-    const uint32_t o1 = (1 < T && cf[x] < kOobOffset) ? cf[x] + tile_base(1) : kOobOffset;
+    const uint32_t o1 = (1 < T && cf[x] < kOobOffset) ? cf[x] + tile_base(kt_begin + 1) : kOobOffset;
     dma16(krs, &lds[kDqStage + (wave + 4 * x) * 1024], o1);
     dma16(vrs, &lds[kDqVRegion + kDqStage + (wave + 4 * x) * 1024], o1);
   }
   // the loop's first DMA is tile 2
 #pragma unroll
-  for (int x = 0; x < 5; ++x) cf[x] = (2 < T && cf[x] < kOobOffset) ? cf[x] + tile_base(2) : kOobOffset;
+  for (int x = 0; x < 5; ++x) cf[x] = (2 < T && cf[x] < kOobOffset) ? cf[x] + tile_base(kt_begin + 2) : kOobOffset;
 
   // LDS read bases: rows of a 32-row block in the sigma order (chunks 2 kk + hh:
   // even kk from ke, odd from ko, plus 64 (kk / 2)); transposed reads for
@@ -1988,9 +1322,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq128_kernel(BwdParams p) {
   }
   const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + uint32_t(wave) * 1024);
   const uint32_t Tn = __builtin_amdgcn_readfirstlane(uint32_t(T));
-  // the wave's diagonal tile and the lanes' admitted keys in it
-  const uint32_t dtl = __builtin_amdgcn_readfirstlane(uint32_t(q0 / BT));
-  const uint32_t mk0 = tile_mask_word(0, l32, hh), mk1 = tile_mask_word(0, 32 + l32, hh);
+  // masks: the key tiles whose every key every query of the wave admits (key
+  // <= q0 and q0 + 63 - key < W), as loop indices fd .. fd + fc - 1; the others
+  // test each score (lane query vq0 / vq1, key offsets by register group in off)
+  const int64_t W = window > 0 ? window : 0x7fffffff;
+  auto cdiv = [](int64_t x) { return x >= 0 ? (x + BT - 1) / BT : -((-x) / BT); };   // ceil(x / 64)
+  const int64_t fa = max<int64_t>(kt_begin, cdiv(int64_t(q0) + 64 - W));
+  const int64_t fb = int64_t(q0) / BT - 1;
+  const uint32_t fd = __builtin_amdgcn_readfirstlane(uint32_t(fa - kt_begin));
+  const uint32_t fc = __builtin_amdgcn_readfirstlane(uint32_t(max<int64_t>(0, fb - fa + 1)));
+  const uint32_t kb0 = __builtin_amdgcn_readfirstlane(uint32_t(kt_begin * BT));
+  const uint32_t Wn = uint32_t(W);
+  const uint32_t vq0 = uint32_t(q0 + l32), vq1 = uint32_t(q0 + 32 + l32);
+  uint32_t off = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) off |= uint32_t(reg_key_offset(g, hh)) << (8 * g);
 
   // tile 0 and the zeros landed for every wave (tile 1 may still be in flight)
   asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
@@ -2007,8 +1353,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq128_kernel(BwdParams p) {
         [cf0] "+v"(cf[0]), [cf1] "+v"(cf[1]), [cf2] "+v"(cf[2]), [cf3] "+v"(cf[3]), [cf4] "+v"(cf[4])
       : [q0] "{a[128:159]}"(qv[0]), [q1] "{a[160:191]}"(qv[1]), [o0] "{a[192:223]}"(dv[0]),
         [o1] "{a[224:255]}"(dv[1]), [c] "s"(p.c), [T] "s"(Tn), [tstride] "s"(tstride), [rk] "s"(krs),
-        [rv] "s"(vrs), [lw] "s"(lw), [dtl] "s"(dtl), [l0] "v"(lse2[0]), [l1] "v"(lse2[1]), [d0] "v"(dd[0]),
-        [d1] "v"(dd[1]), [mk0] "v"(mk0), [mk1] "v"(mk1), [ke] "v"(ke), [ko] "v"(ko), [ve] "v"(ve), [vo] "v"(vo),
+        [rv] "s"(vrs), [lw] "s"(lw), [fd] "s"(fd), [fc] "s"(fc), [kb0] "s"(kb0), [W] "s"(Wn), [l0] "v"(lse2[0]),
+        [l1] "v"(lse2[1]), [d0] "v"(dd[0]), [d1] "v"(dd[1]), [vq0] "v"(vq0), [vq1] "v"(vq1), [off] "v"(off), [ke] "v"(ke), [ko] "v"(ko), [ve] "v"(ve), [vo] "v"(vo),
         [t00] "v"(tr[0]), [t10] "v"(tr[1]), [t01] "v"(tr[2]), [t11] "v"(tr[3])
       : "memory", "vcc", "scc", "m0", "s84", "s85", "s86", SFA_DQ128_CLOBBER_V);
 
@@ -2072,8 +1418,8 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
   p.window = (a.mode == 2 && a.window < S) ? int32_t(a.window) : 0;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
-  // dQ at d = 128 without a window: 64 queries per wave (bwd_dq128_kernel), else 32
-  const bool dq128 = a.d == 128 && !(a.mode == 2 && p.window > 0);
+  // dQ at d = 128: 64 queries per wave (bwd_dq128_kernel), else 32
+  const bool dq128 = a.d == 128;
   const int PS = (kWaves / p.HG) * (dq128 ? 64 : 32);
   p.nqb = (p.Lv + PS - 1) / PS;
   p.nkb = (p.Lv + kWaves * 32 - 1) / (kWaves * 32);
@@ -2089,27 +1435,25 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
   const dim3 pgrid(uint32_t(a.batch * a.hq * ((S + kPrepRows - 1) / kPrepRows)));
   const dim3 qgrid(uint32_t(p.per_xcd_q) * 8u), kgrid(uint32_t(p.per_xcd_k) * 8u);
   using Kernel = void (*)(BwdParams);
-  static constexpr Kernel kDq[2][3] = {
-      {bwd_dq_kernel<64, 0>, bwd_dq_kernel<64, 1>, bwd_dq_kernel<64, 2>},
-      {bwd_dq_kernel<128, 0>, bwd_dq_kernel<128, 1>, bwd_dq_kernel<128, 2>}};
-  static constexpr Kernel kDkdv[2][3] = {
-      {bwd_dkdv_kernel<64, 0>, bwd_dkdv_kernel<64, 1>, bwd_dkdv_kernel<64, 2>},
-      {bwd_dkdv128_kernel<0>, bwd_dkdv128_kernel<1>, bwd_dkdv128_kernel<2>}};
+  static constexpr Kernel kDq64[3] = {bwd_dq_kernel<64, 0>, bwd_dq_kernel<64, 1>, bwd_dq_kernel<64, 2>};
+  static constexpr Kernel kDkdv64[3] = {bwd_dkdv_kernel<64, 0>, bwd_dkdv_kernel<64, 1>, bwd_dkdv_kernel<64, 2>};
   const int kind = intra ? 0 : (p.window > 0 ? 2 : 1);
   const int di = a.d == 128;
   if (di)
     hipLaunchKernelGGL(bwd_prep_kernel<128>, pgrid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<64>, pgrid, dim3(256), 0, stream, p);
-  if (di && kind != 2)
-    hipLaunchKernelGGL(kind == 0 ? bwd_dkdv128_stream_kernel<0> : bwd_dkdv128_stream_kernel<1>, kgrid, dim3(kThreads),
-                       0, stream, p);
+  static constexpr Kernel kDkdv128[3] = {bwd_dkdv128_stream_kernel<0>, bwd_dkdv128_stream_kernel<1>,
+                                         bwd_dkdv128_stream_kernel<2>};
+  static constexpr Kernel kDq128[3] = {bwd_dq128_kernel<0>, bwd_dq128_kernel<1>, bwd_dq128_kernel<2>};
+  if (di)
+    hipLaunchKernelGGL(kDkdv128[kind], kgrid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(kDkdv[di][kind], kgrid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kDkdv64[kind], kgrid, dim3(kThreads), 0, stream, p);
   if (dq128)
-    hipLaunchKernelGGL(kind == 0 ? bwd_dq128_kernel<0> : bwd_dq128_kernel<1>, qgrid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kDq128[kind], qgrid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(kDq[di][kind], qgrid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kDq64[kind], qgrid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ _SIZES = dict(L=32, S=16, P=16, PP=8, DS=8)
 _spans = [(QR, 16), (DR, 16)] + [(st[k], n) for st in SETS for k, n in _SIZES.items()]
 assert sorted(x for b, n in _spans for x in range(b, b + n)) == list(range(64, 256)), "fixed VGPRs overlap"
 # SGPRs
-SI, SG, STI, SG2, STMP, SINC, SINCL = 84, 85, 86, 87, 88, 89, 90
+SI, SG, STI, SG2, STMP, SINC, SINCL, SLIM, SCMP = 84, 85, 86, 87, 88, 89, 90, 91, 92   # SCMP: s[92:93]
 
 TILE = 20480             # bytes of a Q (or dO) tile: 64 rows of 320
 D_REGION = 3 * TILE      # the dO tiles follow the 3 Q tiles
@@ -115,42 +115,46 @@ def pdsa(st, pairs):
 
 
 def mask_block(st, lab):
-    """Out of line: the step past the last masks every score of the block; the
-    first two query tiles (done last) and a ragged last one (done first) take the lane's mask word
-    (bit r set when register r's query sees the lane's key and is valid)."""
+    """Out of line: a block that is not full for every key of the wave. Score
+    register r of lane (key vk, half hh) holds query q0b + e(r), e(r) =
+    reg_key_offset(r / 4, hh) + r % 4 (the byte r / 4 of %[off] holds the first
+    term), q0b = 64 qt + 32 qb for the step's query tile qt = (qtop - 64 STI) / 64;
+    it stays when 0 <= q - vk < W (unsigned compare, W = 2^31 - 1 without a
+    window) and q < Lv, else it becomes -inf. The step past the last (tile
+    qt_begin - 1) has every query below every key."""
     s = SETS[st]
-    t0, t1, t2 = s["DS"], s["DS"] + 1, s["DS"] + 2      # free until this block's dS
+    t0, t1, t2, t3, t4 = (s["DS"] + x for x in range(5))     # free until this block's dS
     b = [Ins(f"{lab}:", "label"),
-         Ins(f"s_cmp_ge_u32 s{SI}, %[T]\n\ts_cbranch_scc1 {lab}_all", "salu"),
-         Ins(f"v_mov_b32 v{t0}, %[wl{st}]", rd={f"%[wl{st}]"}, wr={f"v{t0}"}),
-         Ins(f"s_cmp_eq_u32 s{STI}, %[tb0]\n\ts_cbranch_scc0 {lab}_1", "salu"),
-         Ins(f"v_mov_b32 v{t0}, %[w0{st}]", rd={f"%[w0{st}]"}, wr={f"v{t0}"}),
-         Ins(f"{lab}_1:", "label"),
-         Ins(f"s_cmp_eq_u32 s{STI}, %[tb1]\n\ts_cbranch_scc0 {lab}_2", "salu"),
-         Ins(f"v_mov_b32 v{t0}, %[w1{st}]", rd={f"%[w1{st}]"}, wr={f"v{t0}"}),
-         Ins(f"{lab}_2:", "label"),
-         Ins(f"v_mov_b32 v{t2}, {NEG_INF}", wr={f"v{t2}"})]
-    for r in range(16):
-        e = s["S"] + r
-        b.append(Ins(f"v_bfe_u32 v{t1}, v{t0}, {r}, 1", rd={f"v{t0}"}, wr={f"v{t1}"}))
-        b.append(Ins(f"v_cmp_ne_u32 vcc, 0, v{t1}", rd={f"v{t1}"}, wr={"vcc"}))
-        b.append(Ins(f"v_cndmask_b32 v{e}, v{t2}, v{e}, vcc", rd={f"v{t2}", f"v{e}", "vcc"}, wr={f"v{e}"}))
-    b.append(Ins(f"s_branch {lab}_r", "salu"))
-    b.append(Ins(f"{lab}_all:", "label"))
-    for r in range(16):
-        b.append(Ins(f"v_mov_b32 v{s['S'] + r}, {NEG_INF}", wr={f"v{s['S'] + r}"}))
+         Ins(f"s_lshl_b32 s{STMP}, s{STI}, 6\n\ts_sub_u32 s{STMP}, %[qtop], s{STMP}" +
+             (f"\n\ts_add_u32 s{STMP}, s{STMP}, 32" if st else "") +
+             f"\n\ts_sub_u32 s{SLIM}, %[Lv], s{STMP}", "salu"),
+         Ins(f"v_sub_u32 v{t0}, s{STMP}, %[vk]", rd={"%[vk]"}, wr={f"v{t0}"}),
+         Ins(f"v_mov_b32 v{t3}, {NEG_INF}", wr={f"v{t3}"})]
+    for g in range(4):
+        b.append(Ins(f"v_bfe_u32 v{t1}, %[off], {8 * g}, 8", rd={"%[off]"}, wr={f"v{t1}"}))
+        for i in range(4):
+            e = s["S"] + 4 * g + i
+            q = t1
+            if i:
+                b.append(Ins(f"v_add_u32 v{t2}, {i}, v{t1}", rd={f"v{t1}"}, wr={f"v{t2}"}))
+                q = t2
+            b.append(Ins(f"v_add_u32 v{t4}, v{q}, v{t0}", rd={f"v{q}", f"v{t0}"}, wr={f"v{t4}"}))
+            b.append(Ins(f"v_cmp_gt_u32 vcc, %[W], v{t4}", rd={f"v{t4}"}, wr={"vcc"}))
+            b.append(Ins(f"v_cmp_gt_i32_e64 s[{SCMP}:{SCMP + 1}], s{SLIM}, v{q}\n\t"
+                         f"s_and_b64 vcc, vcc, s[{SCMP}:{SCMP + 1}]", rd={f"v{q}", "vcc"}, wr={"vcc"}))
+            b.append(Ins(f"v_cndmask_b32 v{e}, v{t3}, v{e}, vcc", rd={f"v{t3}", f"v{e}", "vcc"}, wr={f"v{e}"}))
     b.append(Ins(f"s_branch {lab}_r", "salu"))
     return b
 
 
 def mask_check(st, lab):
-    """Full blocks fall through: the query tiles are walked from the last down
-    (STI counts the tiles done), so the two holding the diagonal come last
-    (STI >= tb1) and a ragged last tile first (STI == tlast, 0 or never)."""
+    """Steps whose query tile is full for every key of the wave (processed
+    indices fd .. fd + fc - 1) fall through; the rest, the step that closes the
+    stream included, go out of line."""
     s = SETS[st]
-    br = Ins(f"s_cmp_ge_i32 s{STI}, %[tb1]\n\ts_cbranch_scc1 {lab}\n\ts_cmp_eq_u32 s{STI}, %[tlast]\n\t"
-             f"s_cbranch_scc1 {lab}\n\ts_cmp_ge_u32 s{SI}, %[T]\n\ts_cbranch_scc1 {lab}\n{lab}_r:", "br",
-             rd=vset(s["S"], 16), wr=vset(s["S"], 16) | {"vcc"} | vset(s["DS"], 3), slots=6, name=f"mchk{st}")
+    br = Ins(f"s_sub_u32 s{STMP}, s{STI}, %[fd]\n\ts_cmp_lt_u32 s{STMP}, %[fc]\n\ts_cbranch_scc0 {lab}\n{lab}_r:",
+             "br", rd=vset(s["S"], 16), wr=vset(s["S"], 16) | {"vcc"} | vset(s["DS"], 5), slots=3,
+             name=f"mchk{st}")
     br.block = fix_block(mask_block(st, lab))
     return br
 

@@ -63,7 +63,7 @@ DMA_DEADLINE = int(__import__("os").environ.get("DQ_DMA_DL", "60"))  # the DMA o
 def tr_temps(kb):
     """Mask temporaries: the dS registers of that key block are free while its mask applies."""
     b = DS0 if kb == 0 else DS1
-    return b, b + 1, b + 2
+    return b, b + 1, b + 2, b + 3
 
 
 # ---------------------------------------------------------------- MFMAs
@@ -136,34 +136,42 @@ def ds_pairs(kb, pairs):
 
 
 def mask_block(kb, lab):
-    """Out of line: this tile is the wave's diagonal (apply the lanes' mask words,
-    bits 16 kb .. 16 kb + 15) or lies past it (every score of the key block -inf)."""
+    """Out of line: a tile that is not full for every query of the wave. Score
+    register r of lane (query vq, half hh) holds key key0 + o(r), o(r) =
+    reg_key_offset(r / 4, hh) + r % 4 (the byte r / 4 of %[off] holds the first
+    term); it stays when vq - key < W (unsigned: 0 <= vq - key < W, W = 2^31 - 1
+    without a window), else it becomes -inf."""
     S = SX if kb == 0 else SY
-    t0, t1, t2 = tr_temps(kb)
+    t0, t1, t2, t3 = tr_temps(kb)
     b = [Ins(f"{lab}:", "label"),
-         Ins(f"s_cmp_eq_u32 s{SI}, %[dtl]\n\ts_cbranch_scc0 {lab}_all", "salu"),
-         Ins(f"v_mov_b32 v{t2}, {NEG_INF}", wr={f"v{t2}"})]
+         Ins(f"s_lshl_b32 s{STMP}, s{SI}, 6\n\ts_add_u32 s{STMP}, s{STMP}, %[kb0]" +
+             (f"\n\ts_add_u32 s{STMP}, s{STMP}, 32" if kb else ""), "salu"),
+         Ins(f"v_mov_b32 v{t3}, {NEG_INF}", wr={f"v{t3}"})]
     for j in range(2):
-        for r in range(16):
-            e = S[j] + r
-            b.append(Ins(f"v_bfe_u32 v{t1}, %[mk{j}], {16 * kb + r}, 1", rd={f"%[mk{j}]"}, wr={f"v{t1}"}))
-            b.append(Ins(f"v_cmp_ne_u32 vcc, 0, v{t1}", rd={f"v{t1}"}, wr={"vcc"}))
-            b.append(Ins(f"v_cndmask_b32 v{e}, v{t2}, v{e}, vcc", rd={f"v{t2}", f"v{e}", "vcc"}, wr={f"v{e}"}))
-    b.append(Ins(f"s_branch {lab}_r", "salu"))
-    b.append(Ins(f"{lab}_all:", "label"))
-    for j in range(2):
-        for r in range(16):
-            b.append(Ins(f"v_mov_b32 v{S[j] + r}, {NEG_INF}", wr={f"v{S[j] + r}"}))
+        b.append(Ins(f"v_subrev_u32 v{t0}, s{STMP}, %[vq{j}]", rd={f"%[vq{j}]"}, wr={f"v{t0}"}))
+        for g in range(4):
+            b.append(Ins(f"v_bfe_u32 v{t1}, %[off], {8 * g}, 8", rd={"%[off]"}, wr={f"v{t1}"}))
+            b.append(Ins(f"v_sub_u32 v{t1}, v{t0}, v{t1}", rd={f"v{t0}", f"v{t1}"}, wr={f"v{t1}"}))
+            for i in range(4):
+                e = S[j] + 4 * g + i
+                d = t1
+                if i:
+                    b.append(Ins(f"v_sub_u32_e64 v{t2}, v{t1}, {i}", rd={f"v{t1}"}, wr={f"v{t2}"}))
+                    d = t2
+                b.append(Ins(f"v_cmp_gt_u32 vcc, %[W], v{d}", rd={f"v{d}"}, wr={"vcc"}))
+                b.append(Ins(f"v_cndmask_b32 v{e}, v{t3}, v{e}, vcc", rd={f"v{t3}", f"v{e}", "vcc"}, wr={f"v{e}"}))
     b.append(Ins(f"s_branch {lab}_r", "salu"))
     return b
 
 
 def mask_check(kb, lab):
-    """Full tiles (before the wave's diagonal) fall through; the rest go out of line."""
+    """Tiles in the wave's full range (every key of the tile admitted for every
+    query of the wave: relative tile index fd .. fd + fc - 1) fall through; the
+    rest, the extra tile that closes the stream included, go out of line."""
     S = SX if kb == 0 else SY
-    br = Ins(f"s_cmp_lt_u32 s{SI}, %[dtl]\n\ts_cbranch_scc0 {lab}\n{lab}_r:", "br",
-             rd=vset(S[0], 16) | vset(S[1], 16), wr=vset(S[0], 16) | vset(S[1], 16) | {"vcc"}
-             | set(f"v{x}" for x in tr_temps(kb)), slots=2, name=f"mchk{kb}")
+    br = Ins(f"s_sub_u32 s{STMP}, s{SI}, %[fd]\n\ts_cmp_lt_u32 s{STMP}, %[fc]\n\ts_cbranch_scc0 {lab}\n{lab}_r:",
+             "br", rd=vset(S[0], 16) | vset(S[1], 16), wr=vset(S[0], 16) | vset(S[1], 16) | {"vcc"}
+             | set(f"v{x}" for x in tr_temps(kb)), slots=3, name=f"mchk{kb}")
     br.block = fix_block(mask_block(kb, lab))
     return br
 
