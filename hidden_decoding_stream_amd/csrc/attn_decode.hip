@@ -570,27 +570,53 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int64_
     ns = max(1, min(p.splits, (keys + p.chunk - 1) / p.chunk));
   }
   const float* ml = p.ws_ml + orow * p.splits * 2;
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float lt = 0.f;
-  for (int s = lane; s < ns; s += 64) {
-    const float ms = ml[2 * s];
-    lt += ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[2 * s + 1];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off);
-
   const int d4 = lane % LPR, cls = lane / LPR;
   const float* po = p.ws_o + orow * p.splits * D + 4 * d4;
+  float M = -INFINITY, lt = 0.f;
   f32x4 acc = f32x4{};
+  constexpr int PF = 16;                  // splits per lane loaded up front
+  if (ns <= 64 && ns <= PF * C) {
+    // every load first, so that the row costs one trip to memory: split
+    // `lane`'s (m, l), and the m and partial O of this lane's splits. Same
+    // reductions in the same order as the loops below.
+    const float mv = lane < ns ? ml[2 * lane] : -INFINITY;
+    const float lv = lane < ns ? ml[2 * lane + 1] : 0.f;
+    float msl[PF];
+    f32x4 xs[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int s = cls + i * C;
+      msl[i] = s < ns ? ml[2 * s] : -INFINITY;
+      xs[i] = s < ns ? *reinterpret_cast<const f32x4*>(po + (size_t)s * D) : f32x4{};
+    }
+    M = mv;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    lt = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M) * lv;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const float f = msl[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(msl[i] - M);
+      acc += f * xs[i];
+    }
+  } else {
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int s = lane; s < ns; s += 64) {
+      const float ms = ml[2 * s];
+      lt += ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[2 * s + 1];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off);
 #pragma unroll 8
-  for (int s = cls; s < ns; s += C) {
-    const float ms = ml[2 * s];
-    const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(po + (size_t)s * D);
-    acc += f * x;
+    for (int s = cls; s < ns; s += C) {
+      const float ms = ml[2 * s];
+      const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(po + (size_t)s * D);
+      acc += f * x;
+    }
   }
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1)
