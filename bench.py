@@ -47,6 +47,10 @@ FWD_SOURCES = (ROOT / "hidden_decoding_stream_amd" / "csrc" / "attn_fwd.hip",
 # launches per workload in --profile-prefill (counter runs read them in this order)
 PROFILE_PREFILL_ORDER = ("intra_16k", "cross_window_16k", "cross_full_32k", "intra_32k")
 PROFILE_PREFILL_REPS = 3
+# --prefill-data: the cross_full 32k launch on the workload's N(0,1) inputs and on the same inputs with
+# operands zeroed (one warm-up launch, then this many per data set, in this order)
+PREFILL_DATA_ORDER = ("randn", "v_zero", "q_zero", "all_zero")
+PREFILL_DATA_REPS = 5
 
 
 def parse_args():
@@ -73,6 +77,10 @@ def parse_args():
                     help="only run the four full-size prefill workloads for counter runs "
                          f"({', '.join(PROFILE_PREFILL_ORDER)}; {PROFILE_PREFILL_REPS} launches each, "
                          "in that order), then exit")
+    ap.add_argument("--prefill-data", action="store_true",
+                    help="only run the cross_full 32k prefill on its N(0,1) inputs and with operands zeroed "
+                         f"({', '.join(PREFILL_DATA_ORDER)}; one warm-up launch, then {PREFILL_DATA_REPS} "
+                         "launches each, timed with HIP events), then exit")
     return ap.parse_args()
 
 
@@ -223,6 +231,35 @@ def main():
             print(json.dumps({"profile_prefill": name, "launches": PROFILE_PREFILL_REPS}), flush=True)
             del q, k, v, o
             torch.cuda.empty_cache()
+        return
+
+    if args.prefill_data:
+        # Same kernel, same shapes and masks, different operand values: the matrix core's switching
+        # activity depends on the data, and with it the clock the chip holds under this load.
+        wp = I.CROSS_32K
+        q, k, v = I.workload_qkv(wp, device=dev)
+        o = torch.empty_like(q)
+        data = {"randn": (q, k, v), "v_zero": (q, k, torch.zeros_like(v)),
+                "q_zero": (torch.zeros_like(q), k, v),
+                "all_zero": (torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v))}
+        st = torch.cuda.current_stream()
+        useful = C.prefill_flops(wp.mode, wp.n, wp.L, wp.batch, wp.hq, wp.d, wp.window)
+        sfa.sf_attn_fwd(q, k, v, wp.mode, wp.n, scale=wp.scale, out=o)
+        for name in PREFILL_DATA_ORDER:
+            qq, kk, vv = data[name]
+            ev = []
+            for _ in range(PREFILL_DATA_REPS):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                sfa.sf_attn_fwd(qq, kk, vv, wp.mode, wp.n, scale=wp.scale, out=o)
+                e1.record(st)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ev)
+            med = ms[len(ms) // 2]
+            print(json.dumps({"prefill_data": name, "workload": wp.name, "launches": PREFILL_DATA_REPS,
+                              "ms_median": round(med, 4), "ms_min": round(ms[0], 4),
+                              "useful_tflops": round(useful / med / 1e9, 1)}), flush=True)
         return
 
     w = I.CROSS_32K

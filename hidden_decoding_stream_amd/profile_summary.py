@@ -3,6 +3,7 @@ tooling; not used by the library itself).
 
     python -m hidden_decoding_stream_amd.profile_summary prefill DIR [DIR ...]
     python -m hidden_decoding_stream_amd.profile_summary decode DIR
+    python -m hidden_decoding_stream_amd.profile_summary data DIR [DIR ...]
     python -m hidden_decoding_stream_amd.profile_summary kernels PATTERN DIR [DIR ...]
 
 Each DIR holds the CSV output of one `rocprofv3 --pmc ... --kernel-trace
@@ -258,9 +259,46 @@ def kernels(pattern: str, dirs) -> str:
     return "\n".join(out)
 
 
+DATA_ORDER = ("randn", "v_zero", "q_zero", "all_zero")
+DATA_REPS = 5
+
+
+def data(dirs) -> str:
+    """Counter runs of `bench.py --prefill-data`: the cross_full 32k prefill
+    launched DATA_REPS times on each data set of DATA_ORDER after one warm-up
+    launch. Per data set: duration, effective clock, MFMA busy and CU busy,
+    averaged over its launches (the warm-up launch is left out)."""
+    w = I.CROSS_32K
+    useful = C.prefill_flops(w.mode, w.n, w.L, w.batch, w.hq, w.d, w.window)
+    per = {name: {} for name in DATA_ORDER}
+    for d in dirs:
+        rows = _read_dir(pathlib.Path(d))
+        fwd = [rows[k] for k in sorted(rows) if re.search(r"attn_fwd128_kernel<", rows[k]["name"])]
+        if len(fwd) != 1 + len(DATA_ORDER) * DATA_REPS:
+            raise SystemExit(f"{d}: expected {1 + len(DATA_ORDER) * DATA_REPS} prefill dispatches, found {len(fwd)}")
+        for i, name in enumerate(DATA_ORDER):
+            for rec in fwd[1 + i * DATA_REPS:1 + (i + 1) * DATA_REPS]:
+                for key, val in rec.items():
+                    if key != "name":
+                        per[name].setdefault(key, []).append(val)
+    out = [f"{'data':9s} {'us':>8s} {'TFLOP/s':>8s} {'clock_GHz':>9s} {'mfma_busy_%':>11s} {'cu_busy_%':>9s}"]
+    for name in DATA_ORDER:
+        avg = {k: sum(v) / len(v) for k, v in per[name].items()}
+        ns = avg.get("ns", float("nan"))
+        gx = avg.get("GRBM_GUI_ACTIVE", float("nan")) / XCDS
+        busy = 100.0 * avg.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (gx * SIMDS)
+        cu = 100.0 * avg.get("SQ_BUSY_CU_CYCLES", float("nan")) / (gx * CUS)
+        out.append(f"{name:9s} {ns / 1e3:8.1f} {useful / ns / 1e3:8.1f} {gx / ns:9.3f} {busy:11.2f} {cu:9.2f}")
+    out.append("")
+    out.append("kernel_source_sha256_16: " + _sha16([PKG / "csrc" / "attn_fwd.hip", PKG / "csrc" / "attn_fwd128_stream.h"]))
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "prefill":
         print(prefill(argv[1:]))
+    elif len(argv) >= 2 and argv[0] == "data":
+        print(data(argv[1:]))
     elif len(argv) == 2 and argv[0] == "decode":
         print(decode(argv[1]))
     elif len(argv) >= 3 and argv[0] == "kernels":

@@ -66,6 +66,10 @@ CASES = [
     (4, 33, 1, 16, 2, 64, "cross_full", 0),         # G = 8
     (3, 50, 1, 6, 2, 128, "intra", 0),              # G = 3
     (2, 65, 1, 12, 2, 128, "cross_window", 50),     # G = 6
+    # d = 128 window edges inside and across tiles, ragged lengths (the streams' per-score masks)
+    (3, 45, 1, 8, 2, 128, "cross_window", 37),
+    (2, 97, 2, 4, 4, 128, "cross_window", 130),      # G = 1, W spans tiles
+    (4, 65, 1, 8, 2, 128, "cross_window", 190),
 ]
 
 
