@@ -14,6 +14,13 @@
 //   sfp_mfma   back-to-back v_mfma_f32_32x32x16_bf16 on register operands,
 //              several independent accumulators per wave; the dense bf16
 //              matrix-core rate at the clock the chip holds under load.
+//              Every MFMA multiplies the same two operands, so the matrix
+//              core's inputs hardly switch between instructions.
+//   sfp_mfma_random
+//              the same, rotating over four pairs of operands filled with
+//              hashed random bf16 values, so consecutive MFMAs multiply
+//              unrelated data, as attention on random inputs does: the rate
+//              at the clock the chip holds when the operands switch.
 // Not part of the attention library: a separate shared object with its own
 // C entry points, each enqueued on `stream`; the caller times them.
 #include <hip/hip_runtime.h>
@@ -92,6 +99,43 @@ __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int 
   out[size_t(blockIdx.x) * 256 + threadIdx.x] = s;
 }
 
+
+// lowbias32 (C. Wellons' integer hash): a well-mixed 32-bit value per input.
+__device__ inline uint32_t hash32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// As mfma_kernel<8>, with four operand pairs of random values in [-2, 2):
+// MFMA j of an iteration multiplies A set j mod 4 by B set (j + 1) mod 4.
+__global__ __launch_bounds__(256) void mfma_random_kernel(float* __restrict__ out, int iters, uint32_t seed) {
+  constexpr int CH = 8;
+  bf16x8 a[4], b[4];
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ha = hash32(seed ^ hash32(t * 64u + s * 16u + i));
+      const uint32_t hb = hash32(seed ^ hash32(t * 64u + s * 16u + 8u + i));
+      a[s][i] = (__bf16)(float(ha >> 8) * 0x1p-22f - 2.f);
+      b[s][i] = (__bf16)(float(hb >> 8) * 0x1p-22f - 2.f);
+    }
+  f32x16 c[CH] = {};
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < CH; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 3], b[(j + 1) & 3], c[j], 0, 0, 0);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += c[j][i];
+  out[size_t(blockIdx.x) * 256 + threadIdx.x] = sum;
+}
 
 // One work group per (head, key range); 16 lanes cover one 256-byte slice, 16
 // rows per pass, kUnroll / 2 passes of K and V in flight per lane.
@@ -215,6 +259,13 @@ int sfp_mfma(float* out, int blocks, int iters, int chains, hipStream_t stream) 
     hipLaunchKernelGGL(mfma_kernel<8>, dim3(blocks), dim3(256), 0, stream, out, iters, 1e-3f);
   else
     hipLaunchKernelGGL(mfma_kernel<4>, dim3(blocks), dim3(256), 0, stream, out, iters, 1e-3f);
+  return int(hipGetLastError());
+}
+
+// blocks x 4 waves, each running 8 * iters MFMAs of 32x32x16 on random
+// operands (8 independent accumulators); `out` holds blocks * 256 floats.
+int sfp_mfma_random(float* out, int blocks, int iters, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_random_kernel, dim3(blocks), dim3(256), 0, stream, out, iters, 0x5eedu);
   return int(hipGetLastError());
 }
 

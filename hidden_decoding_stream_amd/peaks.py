@@ -22,9 +22,10 @@ def lib() -> ctypes.CDLL:
         L.sfp_read.argtypes = [c.c_void_p, c.c_size_t, c.c_void_p, c.c_int, c.c_void_p]
         L.sfp_copy.argtypes = [c.c_void_p, c.c_void_p, c.c_size_t, c.c_int, c.c_void_p]
         L.sfp_mfma.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_int, c.c_void_p]
+        L.sfp_mfma_random.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_void_p]
         L.sfp_read_slices.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int, c.c_int, c.c_void_p, c.c_void_p]
         L.sfp_read_slices_lds.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int, c.c_int, c.c_int, c.c_void_p]
-        for f in (L.sfp_read, L.sfp_copy, L.sfp_mfma, L.sfp_read_slices, L.sfp_read_slices_lds):
+        for f in (L.sfp_read, L.sfp_copy, L.sfp_mfma, L.sfp_mfma_random, L.sfp_read_slices, L.sfp_read_slices_lds):
             f.restype = c.c_int
         _lib = L
     return _lib
@@ -72,10 +73,23 @@ def copy_bandwidth(nbytes: int = 1 << 30, blocks: int = 256 * 8, reps: int = 10)
     return 2 * nbytes / t
 
 
-def mfma_bf16_flops(blocks: int = 256, iters: int = 4096, chains: int = 8, reps: int = 5) -> float:
+def mfma_bf16_flops(blocks: int = 256, iters: int = 32768, chains: int = 8, reps: int = 5) -> float:
     """Dense bf16 flop/s of back-to-back 32x32x16 MFMAs, one wave per SIMD
-    with `chains` independent accumulators."""
+    with `chains` independent accumulators. The default launch runs about
+    4 ms, as long as the 32k prefill: the clock under this load settles over
+    a few milliseconds, and launches of under a millisecond read 10-15%
+    high or low."""
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
     t = _time(lambda: _check(lib().sfp_mfma(out.data_ptr(), blocks, iters, chains, st), "sfp_mfma"), reps)
     return blocks * 4 * chains * iters * 32768 / t
+
+
+def mfma_bf16_random_flops(blocks: int = 256, iters: int = 32768, reps: int = 5) -> float:
+    """As mfma_bf16_flops with 8 chains, the operands rotating over four
+    pairs of random bf16 values (the matrix core's inputs switch as on
+    random data)."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    t = _time(lambda: _check(lib().sfp_mfma_random(out.data_ptr(), blocks, iters, st), "sfp_mfma_random"), reps)
+    return blocks * 4 * 8 * iters * 32768 / t
