@@ -340,9 +340,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     // the step base goes into the per-lane offset: only that offset is
     // range-checked, which is what turns rows t >= T into zeros
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(krs, kt + i * 512, koff[i] + sbase);
+    for (int i = 0; i < NI; ++i) dma16_nt(krs, kt + i * 512, koff[i] + sbase);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(vrs, vt + i * 512, voff[i] + sbase);
+    for (int i = 0; i < NI; ++i) dma16_nt(vrs, vt + i * 512, voff[i] + sbase);
   };
 
   float m[RB], lsum[RB];

@@ -55,6 +55,14 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
 }
+// The same with the nontemporal cache policy (`nt`), for data read once and
+// not again by this launch (the decode's cache rows): on MI355X it streams a
+// strided read of every row's 256-byte head slice about 10% faster at 1 GiB
+// and 20% faster at 128 MiB than the default policy. Tiles that other work
+// groups re-read from L2 (prefill, backward) keep the default.
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 2);
+}
 
 // ---- transposed LDS reads (gfx950) ----
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

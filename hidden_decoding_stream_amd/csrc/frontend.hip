@@ -15,7 +15,10 @@
 // expand_embed moves rows as opaque VB-byte vectors (VB = 16..1, the widest
 // the row size and pointers allow), like the interleave: each block takes
 // 4*256 consecutive output vectors, so both the loads of a table row and the
-// stores of the expanded row are coalesced. rope forms each angle in fp64
+// stores of the expanded row are coalesced; the output is written with the
+// nontemporal cache policy (table rows keep the default: repeated ids re-read
+// them). rope, which rewrites its rows in place, keeps the default policy
+// (nontemporal there was 25% slower), and forms each angle in fp64
 // (position x frequency, reduced modulo 2*pi) and only then takes sin/cos in
 // fp32, so large positions keep their accuracy; each thread rotates 4 pairs
 // (8-byte loads and stores of bf16).
@@ -31,8 +34,8 @@ constexpr int kThreads = 256;
 constexpr int kIlp = 4;
 
 template <int VB> struct Vec;
-template <> struct Vec<16> { using T = uint4; };
-template <> struct Vec<8> { using T = uint2; };
+template <> struct Vec<16> { using T = u32x4; };
+template <> struct Vec<8> { using T = u32x2; };
 template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 template <> struct Vec<1> { using T = uint8_t; };
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void expand_embed_kernel(EmbedParams p) {
 #pragma unroll
   for (int j = 0; j < kIlp; ++j) {
     const uint32_t e = base + j * kThreads;
-    if (e < p.total) out[e] = val[j];
+    if (e < p.total) __builtin_nontemporal_store(val[j], out + e);
   }
 }
 

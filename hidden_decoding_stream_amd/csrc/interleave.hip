@@ -13,7 +13,9 @@
 // e = base + t + j*256, so each wave touches 64 consecutive vectors per step
 // (coalesced on the expanded side, and on the per-stream side whenever a row
 // spans at least a wave's worth of bytes). All loads of a thread are issued
-// before its stores. Index math is 32-bit with invariant-divisor division.
+// before its stores, both with the nontemporal cache policy (every byte is
+// read once and written once). Index math is 32-bit with invariant-divisor
+// division.
 // One launch can move up to kMaxTensors tensors of the same (n, L, batch),
 // each with its own row size (Q with hq heads, K and V with hkv): every block
 // belongs to one tensor, so small tensors no longer pay a launch and a ramp
@@ -29,8 +31,8 @@ constexpr int kThreads = 256;
 constexpr int kIlp = 4;
 
 template <int VB> struct Vec;
-template <> struct Vec<16> { using T = uint4; };
-template <> struct Vec<8> { using T = uint2; };
+template <> struct Vec<16> { using T = u32x4; };
+template <> struct Vec<8> { using T = u32x2; };
 template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 template <> struct Vec<1> { using T = uint8_t; };
@@ -91,11 +93,11 @@ __global__ __launch_bounds__(kThreads) void interleave_kernel(InterleaveParams p
     const uint32_t x_idx = e;                           // expanded layout index
     const uint32_t in_idx = p.inverse ? x_idx : s_idx;
     out_idx[j] = p.inverse ? s_idx : x_idx;
-    buf[j] = src[in_idx];
+    buf[j] = __builtin_nontemporal_load(src + in_idx);
   }
 #pragma unroll
   for (int j = 0; j < kIlp; ++j) {
-    if (live[j]) dst[out_idx[j]] = buf[j];
+    if (live[j]) __builtin_nontemporal_store(buf[j], dst + out_idx[j]);
   }
 }
 

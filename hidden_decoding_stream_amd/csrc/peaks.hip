@@ -10,7 +10,8 @@
 //              head (work group x) and key range (work group y), the head's
 //              256-byte slice of every K and V row (rows of heads * 256 bytes),
 //              by 16-byte loads into registers, or by buffer->LDS DMA through
-//              a ring of stages per wave, the decode kernel's way.
+//              a ring of stages per wave, the decode kernel's way; both with
+//              the nontemporal cache policy, as the decode kernel reads.
 //   sfp_mfma   back-to-back v_mfma_f32_32x32x16_bf16 on register operands,
 //              several independent accumulators per wave; the dense bf16
 //              matrix-core rate at the clock the chip holds under load.
@@ -163,7 +164,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // The same bytes by DMA: wave w takes every 4th step of R rows of K and of V
 // (NS stages of R * 512 bytes per wave), waits for a stage and reissues it at
-// once (no work on the data: the stream alone).
+// once (no work on the data: the stream alone). Nontemporal policy (aux 2).
 template <int NS, int R>
 __global__ __launch_bounds__(256) void slices_lds_kernel(const void* k, const void* v, uint32_t bytes,
                                                          int rows_per_group, int heads) {
@@ -184,11 +185,11 @@ __global__ __launch_bounds__(256) void slices_lds_kernel(const void* k, const vo
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ring + st * SB + i * 1024), 16,
-                                               (row0 + 4 * i) * row_bytes + lane_off, 0, 0, 0);
+                                               (row0 + 4 * i) * row_bytes + lane_off, 0, 0, 2);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ring + st * SB + SB / 2 + i * 1024), 16,
-                                               (row0 + 4 * i) * row_bytes + lane_off, 0, 0, 0);
+                                               (row0 + 4 * i) * row_bytes + lane_off, 0, 0, 2);
   };
 #pragma unroll
   for (int st = 0; st < NS; ++st)
