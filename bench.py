@@ -202,6 +202,20 @@ def main():
                         raise RuntimeError("sfp_read_slices launch failed")
             torch.cuda.synchronize()
             print(json.dumps({"profile_read_slices": ring or "registers", "launches": 24}), flush=True)
+        # the batch-1 call's structure with no arithmetic: the same stream, decode-sized partials and
+        # their merge, by a second kernel (two launches per call) or in one launch; 24 calls each
+        part = torch.empty(8 * 16 * 32 * 130, dtype=torch.float32, device=dev)
+        ticket = torch.zeros(8, dtype=torch.int32, device=dev)
+        outb = torch.empty(8 * 16 * 128, dtype=torch.bfloat16, device=dev)
+        for fused in (0, 1):
+            for _ in range(3):
+                for kb, vb in pairs:
+                    if P.lib().sfp_decode_chain(kb.data_ptr(), vb.data_ptr(), rows, 8, 32, part.data_ptr(),
+                                                ticket.data_ptr(), outb.data_ptr(), fused, st) != 0:
+                        raise RuntimeError("sfp_decode_chain launch failed")
+            torch.cuda.synchronize()
+            print(json.dumps({"profile_decode_chain": "one launch" if fused else "split + combine",
+                              "calls": 24}), flush=True)
         return
 
     if args.trace_prefill:
@@ -532,6 +546,12 @@ def attainable_peaks(line):
            "prefill_cross_full_frac_random": round(line["roofline"]["achieved"] / mfma_rnd, 4)}
     for key, rec in (line.get("decode") or {}).items():
         out[f"decode_{key}_frac"] = round(rec["GBps"] / read, 4)
+    # the floor of the batch-1 decode call: its bytes in its pattern with no arithmetic, read alone,
+    # then with the split + combine hand-over (two launches) and with a one-launch merge
+    fl = P.decode_structure_floor()
+    out["decode_b1_floor"] = fl
+    print(f"[bench] batch-1 decode floor: read {fl['read_us']} us, split+combine chain {fl['chain_us']} us, "
+          f"one-launch chain {fl['fused_us']} us", file=sys.stderr, flush=True)
     print(f"[bench] attainable: {mfma:.0f} TFLOP/s bf16 (random operands {mfma_rnd:.0f}), {read:.0f} GB/s read",
           file=sys.stderr, flush=True)
     return out

@@ -12,6 +12,16 @@
 //              by 16-byte loads into registers, or by buffer->LDS DMA through
 //              a ring of stages per wave, the decode kernel's way; both with
 //              the nontemporal cache policy, as the decode kernel reads.
+//   sfp_decode_chain
+//              the batch-1 decode call's structure with no arithmetic: the
+//              pattern read by DMA ring as above, each work group then writing
+//              a partial of the decode's size (16 rows x (128 + 2) floats),
+//              and the partials merged per output row with the decode
+//              combine's loads, either by a second kernel (the library's
+//              split + combine) or inside the same launch by the last work
+//              group of each kv head to finish (a device-scope release fence
+//              and an atomic ticket per kv head, then an acquire fence). The
+//              floor each structure puts under the decode's call time.
 //   sfp_mfma   back-to-back v_mfma_f32_32x32x16_bf16 on register operands,
 //              several independent accumulators per wave; the dense bf16
 //              matrix-core rate at the clock the chip holds under load.
@@ -32,6 +42,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUnroll = 8;   // 16-byte loads in flight per lane
 
@@ -165,11 +176,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // The same bytes by DMA: wave w takes every 4th step of R rows of K and of V
 // (NS stages of R * 512 bytes per wave), waits for a stage and reissues it at
 // once (no work on the data: the stream alone). Nontemporal policy (aux 2).
+// `lds` holds 4 * NS * R * 512 bytes.
 template <int NS, int R>
-__global__ __launch_bounds__(256) void slices_lds_kernel(const void* k, const void* v, uint32_t bytes,
-                                                         int rows_per_group, int heads) {
+__device__ __forceinline__ void stream_slices(uint8_t* lds, const void* k, const void* v, uint32_t bytes,
+                                              int rows_per_group, int heads) {
   constexpr int SB = R * 512, NI = R / 4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * NS * SB];
   const int u = blockIdx.x, s = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6), lane = threadIdx.x & 63;
   const __amdgpu_buffer_rsrc_t kr =
@@ -200,6 +211,96 @@ __global__ __launch_bounds__(256) void slices_lds_kernel(const void* k, const vo
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int NS, int R>
+__global__ __launch_bounds__(256) void slices_lds_kernel(const void* k, const void* v, uint32_t bytes,
+                                                         int rows_per_group, int heads) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * NS * R * 512];
+  stream_slices<NS, R>(lds, k, v, bytes, rows_per_group, heads);
+}
+
+// Decode-shaped partials: output row `row` (16 per kv head) of split s holds
+// 128 floats at part_o[(row * splits + s) * 128] and (max, sum) at
+// part_ml[(row * splits + s) * 2], the decode library's workspace layout.
+constexpr int kChainRows = 16;     // query rows per kv head (n * G at batch 1, cross masks)
+constexpr int kChainSplitsMax = 32;
+
+// One wave merges one output row the way the decode's combine loads it:
+// 32 lanes cover a split's 128 values (4 each), the two halves of the wave
+// take alternate splits, every load first; the values are summed (the
+// probe times the data movement, not the rescaling).
+__device__ __forceinline__ void chain_merge_row(const float* part_o, const float* part_ml, int splits, int row,
+                                                uint16_t* out, int lane) {
+  const int d4 = lane % 32, cls = lane / 32;
+  const float* po = part_o + size_t(row) * splits * 128 + 4 * d4;
+  const float* ml = part_ml + size_t(row) * splits * 2;
+  float w = lane < splits ? ml[2 * lane] + ml[2 * lane + 1] : 0.f;
+  f32x4 xs[kChainSplitsMax / 2];
+#pragma unroll
+  for (int i = 0; i < kChainSplitsMax / 2; ++i) {
+    const int s = cls + 2 * i;
+    xs[i] = s < splits ? *reinterpret_cast<const f32x4*>(po + size_t(s) * 128) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kChainSplitsMax / 2; ++i) acc += xs[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
+  if (cls == 0) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc[i] * w);
+    *reinterpret_cast<bf16x4*>(out + size_t(row) * 128 + 4 * d4) = ov;
+  }
+}
+
+// Work group (kv head u, split s): the decode's stream of its key range
+// (ring of 2 stages of 32 rows per wave), then its partial of 16 rows, stored
+// as the decode's split kernel stores it (one float per thread per pass).
+// FUSED: the last group of kv head u to finish merges its 16 rows.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void chain_split_kernel(const void* k, const void* v, uint32_t bytes,
+                                                          int rows_per_group, int heads, float* part_o,
+                                                          float* part_ml, uint32_t* ticket, uint16_t* out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * 2 * 32 * 512];
+  __shared__ uint32_t last;
+  stream_slices<2, 32>(lds, k, v, bytes, rows_per_group, heads);
+  const int u = blockIdx.x, s = blockIdx.y, splits = gridDim.y;
+  for (int idx = threadIdx.x; idx < kChainRows * 128; idx += 256) {
+    const int row = u * kChainRows + idx / 128, d = idx % 128;
+    part_o[(size_t(row) * splits + s) * 128 + d] = float(d);
+    if (d == 0) {
+      part_ml[(size_t(row) * splits + s) * 2 + 0] = 0.f;
+      part_ml[(size_t(row) * splits + s) * 2 + 1] = 1.f;
+    }
+  }
+  if constexpr (FUSED) {
+    // release this group's partial at device scope, then take a ticket; the
+    // group holding the last ticket resets the counter for the next call
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t t = atomicAdd(&ticket[u], 1u);
+      last = t == uint32_t(splits - 1);
+      if (last) atomicExch(&ticket[u], 0u);
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int r = wave; r < kChainRows; r += 4) chain_merge_row(part_o, part_ml, splits, u * kChainRows + r, out, lane);
+  }
+}
+
+// The library's second kernel: one wave per output row.
+__global__ __launch_bounds__(256) void chain_combine_kernel(const float* part_o, const float* part_ml, int splits,
+                                                            uint16_t* out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  chain_merge_row(part_o, part_ml, splits, row, out, threadIdx.x & 63);
 }
 }  // namespace
 
@@ -249,6 +350,35 @@ int sfp_read_slices_lds(const void* k, const void* v, int rows, int heads, int s
     hipLaunchKernelGGL((slices_lds_kernel<8, 8>), grid, dim3(256), 0, stream, k, v, bytes, rpg, heads);
   else
     return int(hipErrorInvalidValue);
+  return int(hipGetLastError());
+}
+
+// The batch-1 decode call's structure with no arithmetic (see the file
+// header). k, v: `rows` rows of heads * 256 bytes each, as sfp_read_slices_lds
+// (rows / splits a multiple of 128, rows * heads * 256 < 2^31); splits <= 32.
+// part: heads * 16 * splits * 130 floats of scratch. out: heads * 16 * 128
+// bf16 values. ticket: heads words, zero before the first fused call (each
+// fused call leaves them zero). fused = 0: split kernel + combine kernel
+// (two launches); fused = 1: one launch.
+int sfp_decode_chain(const void* k, const void* v, int rows, int heads, int splits, float* part, uint32_t* ticket,
+                     void* out, int fused, hipStream_t stream) {
+  if (splits < 1 || splits > kChainSplitsMax || heads < 1 || rows % splits || (rows / splits) % 128 ||
+      size_t(rows) * heads * 256 >= (size_t(1) << 31))
+    return int(hipErrorInvalidValue);
+  const uint32_t bytes = uint32_t(size_t(rows) * heads * 256);
+  float* part_o = part;
+  float* part_ml = part + size_t(heads) * kChainRows * splits * 128;
+  uint16_t* o = static_cast<uint16_t*>(out);
+  const dim3 grid(heads, splits);
+  if (fused) {
+    hipLaunchKernelGGL(chain_split_kernel<true>, grid, dim3(256), 0, stream, k, v, bytes, rows / splits, heads,
+                       part_o, part_ml, ticket, o);
+  } else {
+    hipLaunchKernelGGL(chain_split_kernel<false>, grid, dim3(256), 0, stream, k, v, bytes, rows / splits, heads,
+                       part_o, part_ml, ticket, o);
+    hipLaunchKernelGGL(chain_combine_kernel, dim3(heads * kChainRows / 4), dim3(256), 0, stream,
+                       static_cast<const float*>(part_o), static_cast<const float*>(part_ml), splits, o);
+  }
   return int(hipGetLastError());
 }
 

@@ -166,6 +166,9 @@ def decode(d) -> str:
         for r in csv.DictReader(open(f)):
             name = r["Kernel_Name"]
             short = ("split" if "decode_split_kernel" in name else "combine" if "decode_combine_kernel" in name
+                     else "cfused" if "chain_split_kernel<true>" in name
+                     else "csplit" if "chain_split_kernel<false>" in name
+                     else "ccomb" if "chain_combine_kernel" in name
                      else "read" if "read_kernel" in name else "slices" if "slices_kernel" in name
                      else "ring" + re.search(r"slices_lds_kernel<(\d+)", name).group(1)
                      if "slices_lds_kernel" in name else None)
@@ -200,6 +203,19 @@ def decode(d) -> str:
         if ts:
             out.append(f"the same bytes in the decode's pattern, {what}: mean {sum(ts) / len(ts):.2f} us, "
                        f"min {min(ts):.2f} us over {len(ts)} launches")
+    chain = [(st, en) for st, en, s, _, _ in rows if s == "csplit"]
+    spans = []
+    for st, en in chain:
+        nxt = [e2 for s2, e2, k2, _, _ in rows if k2 == "ccomb" and s2 >= en]
+        if nxt:
+            spans.append((min(nxt) - st) / 1e3)
+    if spans:
+        out.append(f"the same stream with decode-sized partials and a combine kernel, no arithmetic (split start to "
+                   f"combine end): mean {sum(spans) / len(spans):.2f} us, min {min(spans):.2f} us over {len(spans)} calls")
+    ts = [(en - st) / 1e3 for st, en, s, _, _ in rows if s == "cfused"]
+    if ts:
+        out.append(f"the same in one launch, the last group of each kv head merging: mean {sum(ts) / len(ts):.2f} us, "
+                   f"min {min(ts):.2f} us over {len(ts)} calls")
     return "\n".join(out)
 
 
