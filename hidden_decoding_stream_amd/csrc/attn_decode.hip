@@ -516,18 +516,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
       mrg.l[wave][l16] = lsum[rb];
     }
     __syncthreads();
+    // 16 threads per row, each with EPT consecutive d values: the row's max
+    // and the 4 waves' factors once per thread, every LDS read of the row in
+    // one round trip, vector stores
+    constexpr int EPT = D / 16;
     const int nrows = min(16, p.R - rb * 16);
-    for (int idx = tid; idx < nrows * D; idx += kThreads) {
-      const int row = idx / D, d = idx % D;
+    const int row = tid >> 4, d0 = (tid & 15) * EPT;
+    if (row < nrows) {
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg.m[w][row]);
-      float acc = 0.f, lt = 0.f;
+      float acc[EPT], lt = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const float f = __builtin_amdgcn_exp2f(mrg.m[w][row] - M);
-          acc += f * mrg.o[w][row][d];
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) acc[e] += f * mrg.o[w][row][d0 + e];
           lt += f * mrg.l[w][row];
         }
       }
@@ -538,10 +545,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
       if (p.splits == 1) {
         // every row of a valid sequence admits at least its own key, so lt > 0
         // (an invalid paged length leaves lt = 0: NaN)
-        p.o[orow * D + d] = __builtin_bit_cast(u16, (__bf16)(acc / lt));
+        typedef __bf16 bf16xE __attribute__((ext_vector_type(EPT)));
+        bf16xE ov;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) ov[e] = (__bf16)(acc[e] / lt);
+        *reinterpret_cast<bf16xE*>(p.o + orow * D + d0) = ov;
       } else {
-        p.ws_o[(orow * p.splits + split) * D + d] = acc;
-        if (d == 0) {
+        float* wo = p.ws_o + (orow * p.splits + split) * D + d0;
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) *reinterpret_cast<f32x4*>(wo + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+        if (d0 == 0) {
           p.ws_ml[(orow * p.splits + split) * 2 + 0] = M;
           p.ws_ml[(orow * p.splits + split) * 2 + 1] = lt;
         }
