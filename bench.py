@@ -485,6 +485,21 @@ def trace_prefill(torch, sfa, I, dev, reps=3):
         torch.cuda.empty_cache()
 
 
+def warm_up(torch, call, min_s=0.05):
+    """Untimed launches of `call` until about min_s seconds of it have run.
+    The clock the chip holds under a new load settles over several
+    milliseconds: after a pause (inputs drawn, tensors freed) the first
+    launches of a 1 ms kernel run up to 15% slower than the steady state."""
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    call()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t, 1e-5)
+    for _ in range(max(1, int(min_s / one))):
+        call()
+    torch.cuda.synchronize()
+
+
 def prefill_configs(torch, sfa, C, I, dev, stream, hw, step_ms, reps=10):
     """Every prefill workload on its own: the tiny problem (intra and
     cross_full, attention on the bf16 rounding of its fp32 draws), intra 16k
@@ -505,8 +520,7 @@ def prefill_configs(torch, sfa, C, I, dev, stream, hw, step_ms, reps=10):
             o = torch.empty_like(q)
             call = lambda: sfa.sf_attn_fwd(q, k, v, w.mode, w.n, window=w.window, scale=w.scale,  # noqa: E731
                                            out=o)
-            for _ in range(2):
-                call()
+            warm_up(torch, call)
             pairs = []
             for _ in range(reps):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -564,8 +578,7 @@ def last_stream_timing(torch, sfa, C, Q, K, V, n, L, B, hq, d, scale, stream, re
     o = torch.empty_like(ql)
     out = {}
     for mode in ("cross_full", "intra"):
-        for _ in range(2):
-            sfa.sf_attn_fwd_last_stream(ql, K, V, mode, n, scale=scale, out=o)
+        warm_up(torch, lambda: sfa.sf_attn_fwd_last_stream(ql, K, V, mode, n, scale=scale, out=o))
         pairs = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -635,7 +648,7 @@ def backward_timing(torch, sfa, C, Q, K, V, Oc, n, L, B, hq, hkv, d, scale, dev,
         o, lse = sfa.sf_attn_fwd(Q, K, V, mode, n, scale=scale, lse=True)
         call = lambda: sfa.sf_attn_bwd(Q, K, V, o, dout, lse, mode, n, scale=scale, out=(dq, dk, dv),  # noqa: E731
                                        workspace=ws)
-        call()
+        warm_up(torch, call)
         pairs = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
