@@ -678,10 +678,12 @@ DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t 
   int64_t want = num_splits;
   if (want == 0) {
     // A group holds 128 KiB of LDS, so one runs per CU: aim for one group per
-    // CU (256), with chunks of at least 512 keys.
+    // CU (256), with chunks of at least one step per wave. A unit with few
+    // keys (a window, a short cache) at small batch then still spreads over
+    // every CU instead of leaving most of them idle.
     const int64_t target_groups = 256;
     want = (target_groups + pl.units - 1) / pl.units;
-    want = std::min<int64_t>(want, std::max<int64_t>(1, pl.keys / 512));
+    want = std::min<int64_t>(want, std::max<int64_t>(1, pl.keys / kChunkQuantum));
   }
   want = std::max<int64_t>(1, std::min<int64_t>({want, pl.keys / kStep, int64_t(1024)}));
   pl.chunk = round_up((pl.keys + want - 1) / want, kChunkQuantum);
