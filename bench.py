@@ -67,6 +67,8 @@ def parse_args():
                     help="only run decode calls for trace and counter runs (batch 1 and 8, cross_full and "
                          "intra, 3 calls each on distinct caches; then 24 plain reads of the batch-1 "
                          "cache's bytes on the decode's 256-group grid), then exit")
+    ap.add_argument("--decode-splits", action="store_true",
+                    help="time decode at small batch over explicit split counts (one JSON line per case) and exit")
     ap.add_argument("--trace-prefill", action="store_true",
                     help="only run the four full-size prefill workloads on the trace build of the library "
                          "(libsfattn_trace.so) and print each launch's timeline statistics, then exit")
@@ -218,6 +220,9 @@ def main():
                               "calls": 24}), flush=True)
         return
 
+    if args.decode_splits:
+        decode_split_sweep(torch, sfa, C, dev)
+        return
     if args.trace_prefill:
         trace_prefill(torch, sfa, I, dev)
         return
@@ -723,6 +728,47 @@ def _rotated_time(torch, calls, reps=20):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def decode_split_sweep(torch, sfa, C, dev):
+    """Decode at small batch against the split count: the library's plan (0)
+    and explicit counts 4 ... 128, each the best of 3 rotated timings of 20
+    calls, after ~50 ms of warm-up calls on the case. Cases: cross_window W = 4096 at batch 1 and 8, cross_full and intra
+    at batch 1 (n = 4, T = 8192), cross_full at n = 8, T = 4096, batch 1;
+    32/8 heads, d = 128."""
+    g = torch.Generator(device=dev).manual_seed(1010)
+
+    def bf16(*shape):
+        return torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+
+    hq, hkv, d = 32, 8, 128
+    for tag, n, T, mode, W, batch in (("window4096", 4, 8192, "cross_window", 4096, 1),
+                                      ("window4096", 4, 8192, "cross_window", 4096, 8),
+                                      ("cross_full", 4, 8192, "cross_full", 0, 1),
+                                      ("intra", 4, 8192, "intra", 0, 1),
+                                      ("n8_cross_full", 8, 4096, "cross_full", 0, 1)):
+        nbytes = C.decode_bytes(mode, n, T, batch, hq, hkv, d, window=W)
+        cache_bytes = 2 * batch * n * T * hkv * d * 2
+        copies = max(1, min(math.ceil((1 << 30) / nbytes), (12 << 30) // cache_bytes))
+        q = bf16(batch, n, hq, d)
+        caches = [(bf16(batch, n, T, hkv, d), bf16(batch, n, T, hkv, d)) for _ in range(copies)]
+        o = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(d)
+        res = {}
+        # warm the chip on this case first: the count timed first would otherwise carry the clock's ramp
+        ws0 = torch.empty(sfa.sf_attn_decode_workspace_bytes(batch, n, T, hq, hkv, d, mode, W) + 16,
+                          dtype=torch.uint8, device=dev)
+        warm_up(torch, lambda: [sfa.sf_attn_decode(q, kc, vc, T, mode, window=W, scale=scale, out=o, workspace=ws0)
+                                for kc, vc in caches])
+        for ns in (0, 4, 8, 16, 32, 64, 128):
+            ws = torch.empty(sfa.sf_attn_decode_workspace_bytes(batch, n, T, hq, hkv, d, mode, W, num_splits=ns) + 16,
+                             dtype=torch.uint8, device=dev)
+            calls = [lambda kc=kc, vc=vc: sfa.sf_attn_decode(q, kc, vc, T, mode, window=W, scale=scale, out=o,
+                                                             workspace=ws, num_splits=ns) for kc, vc in caches]
+            res[str(ns)] = round(min(_rotated_time(torch, calls) for _ in range(3)), 2)
+        print(json.dumps({"decode_splits": f"{tag}_b{batch}", "bytes": nbytes, "us_by_splits": res}), flush=True)
+        del caches, q, o
+        torch.cuda.empty_cache()
 
 
 def serving_sweep(torch, sfa, C, I, dev, budget=16 << 30):
