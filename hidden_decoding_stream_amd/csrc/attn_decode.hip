@@ -677,12 +677,13 @@ DecodePlan plan_decode(int64_t batch, int32_t n, int64_t T, int32_t hq, int32_t 
   pl.keys = (intra ? 1 : n) * pl.keys_per_stream;
   int64_t want = num_splits;
   if (want == 0) {
-    // A group holds 128 KiB of LDS, so one runs per CU: aim for one group per
-    // CU (256), with chunks of at least one step per wave. A unit with few
+    // A group holds 128 KiB of LDS, so one runs per CU: at most one group per
+    // CU (256 groups; a second, partial round of groups would add each one's
+    // fixed cost), with chunks of at least one step per wave. A unit with few
     // keys (a window, a short cache) at small batch then still spreads over
     // every CU instead of leaving most of them idle.
     const int64_t target_groups = 256;
-    want = (target_groups + pl.units - 1) / pl.units;
+    want = std::max<int64_t>(1, target_groups / pl.units);
     want = std::min<int64_t>(want, std::max<int64_t>(1, pl.keys / kChunkQuantum));
   }
   want = std::max<int64_t>(1, std::min<int64_t>({want, pl.keys / kStep, int64_t(1024)}));

@@ -346,3 +346,23 @@ def test_bwd_workspace_query():
     assert sfa.lib().sf_attn_bwd_workspace_bytes(2, 4, 100, 8, 2, 128, 1, 0) == -(-2 * 400 * 8 * 8 // 256) * 256
     assert sfa.lib().sf_attn_bwd_workspace_bytes(0, 4, 100, 8, 2, 128, 1, 0) == 0
     assert bwd(batch=0) == B.SF_OK
+
+
+def test_every_default_decode_plan_fits_the_noalloc_scratch():
+    # The plan puts at most one group per CU (256 groups) of at most 64 query
+    # rows, each row's partial (d + 2) floats: at most about 8.5 MB, within
+    # the 16 MiB array sf_attn_decode_noalloc holds. Unit counts that do not
+    # divide 256 are the edge (255 units at two splits each would need 17 MB).
+    limit = int(re.search(r"#define SF_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", HEADER.read_text()).group(1)) << 20
+    worst = 0
+    for mode in ("intra", "cross_full", "cross_window"):
+        for n, hkv, G in ((1, 1, 64), (4, 8, 4), (16, 1, 4), (8, 2, 8), (3, 5, 3), (4, 7, 16), (2, 3, 1)):
+            if mode != "intra" and n * G > 64:
+                continue
+            for batch in (1, 2, 3, 7, 31, 63, 127, 255, 257):
+                for T in (1, 100, 1000, 8192):
+                    for d in (64, 128):
+                        ws = sfa.sf_attn_decode_workspace_bytes(batch, n, T, hkv * G, hkv, d, mode,
+                                                                window=4096 if mode == "cross_window" else 0)
+                        worst = max(worst, ws)
+    assert 0 < worst <= 256 * 64 * (128 + 2) * 4 + 512 <= limit
