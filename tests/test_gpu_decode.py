@@ -94,6 +94,25 @@ def test_full_size(batch, mode):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("batch", [1, 8])
+def test_full_size_window(batch):
+    """Windowed decode at the serving size (8192 tokens x 4 streams, W = 4096
+    positions, 32/8 heads, d = 128) with the library's plan (32 splits of one
+    step per wave at batch 1): every output element against the oracle."""
+    w = I.DecodeWorkload("window4096", 4, 8192, 8192, batch, 32, 8, 128, "cross_window", window=4096, seed=1011)
+    say("decode full size window", batch)
+    q, kc, vc = I.decode_inputs(w, device="cuda")
+    o = sfa.sf_attn_decode(q, kc, vc, w.T, w.mode, window=w.window, scale=_scale(w.d))
+    o2 = sfa.sf_attn_decode(q, kc, vc, w.T, w.mode, window=w.window, scale=_scale(w.d))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2), "decode must be deterministic"
+    ref = pooled(lambda b: orc.decode(np64(q[b:b + 1]), np64(kc[b:b + 1]), np64(vc[b:b + 1]), w.T, w.mode,
+                                      window=w.window, scale=_scale(w.d))[0], list(range(batch)))
+    assert_close(np64(o), np.stack(ref), f"window4096 all {batch} batch elements")
+    del q, kc, vc
+    torch.cuda.empty_cache()
+
+
 def test_workspace_reused_across_calls():
     """One workspace, its contents left over from earlier calls, serves
     consecutive calls of different shapes, split counts and masks; each
