@@ -62,6 +62,7 @@ def test_expand_embed_full_size():
     (300, 2, 64, 10000.0, 1000),
     (17, 3, 256, 500000.0, 32760),
     (50, 1, 8, 10000.0, 7),
+    (40, 2, 24, 10000.0, 3),                # d a multiple of 8 but not of 16
     (2, 32, 128, 10000.0, (1 << 31) - 5),   # positions past 2^31
 ])
 def test_rope_small(S, H, d, base, pos0):
@@ -75,6 +76,21 @@ def test_rope_small(S, H, d, base, pos0):
     assert_close(got, ref, f"rope S={S} d={d} pos0={pos0}")
     # one bf16 rounding of the exact value: half an ulp, plus fp32 arithmetic
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4), "beyond one bf16 rounding"
+
+
+def test_rope_rows_8_byte_aligned():
+    # rows only 8-byte aligned, the least the call accepts; nothing outside the tensor is written
+    S, H, d = 33, 3, 128
+    g = torch.Generator().manual_seed(77)
+    x = I.to_bf16(torch.randn((1, S, H, d), generator=g))
+    buf = torch.zeros(S * H * d + 4, dtype=torch.bfloat16, device="cuda")
+    xv = buf[4:].view(1, S, H, d)
+    xv.copy_(x.cuda())
+    assert xv.data_ptr() % 16 == 8
+    y = sfa.sf_rope(xv, base=10000.0, pos0=5)
+    torch.cuda.synchronize()
+    assert_close(np64(y), orc.rope(np64(x), 10000.0, 5), "rope 8-byte aligned rows")
+    assert torch.equal(buf[:4].cpu(), torch.zeros(4, dtype=torch.bfloat16)), "wrote before the tensor"
 
 
 def test_rope_full_size_q():
